@@ -1,0 +1,295 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) library for one layer of hybrid
+ * compressed attention: CSA (compressed sparse attention) and HCA (heavily
+ * compressed attention), decode and prefill.
+ *
+ * Sources (web pages summarising the DeepSeek-V4 technical report):
+ *   [W1] "DeepSeek-V4: Towards Highly Efficient Million-Token Context
+ *        Intelligence" (awesome-system-papers.pages.dev), "核心方法 / Hybrid
+ *        CSA + HCA Attention", "关键观察" observation 1.
+ *   [W2] "DeepSeek-V4 深读" (ricardokevins.github.io), spec table "模型全貌",
+ *        "CSA：4× 压缩之后再 top-k" with the compression equation and Fig. 2,
+ *        "HCA：128× 压缩后保留 dense 全局视野", the stability-details paragraph,
+ *        "FP4 QAT、可恢复 rollout".
+ *   [W3] "AI深一度 第15期|DeepSeek V4" (yeyulingfeng.com), sections 一 and 二.
+ *   [W4] "DeepSeek-V4 论文解读" (researchpapers.dev), section "注意力栈".
+ *   [W5] "拆解 DeepSeekv4" (daixd5520.github.io), sections CSA, HCA, 细节.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains them.  Strides are in BYTES.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the device or copies to the host.
+ *   - Arguments are validated on the host before any launch; on a validation
+ *     failure nothing is launched and a negative status is returned.
+ *   - Status: CSA_OK (0); CSA_EINVAL (-1) null pointer, misaligned pointer or
+ *     inconsistent shape; CSA_EUNSUPPORTED (-2) a shape or format combination
+ *     this build has no kernel for; CSA_EHIP (-3) a launch error reported by
+ *     the HIP runtime; CSA_EWORKSPACE (-4) workspace missing or too small.
+ *   - Deterministic: for a fixed input and shape the results are bitwise
+ *     reproducible; no kernel uses order-dependent floating-point atomics.
+ *   - Thread-safe: the library keeps no mutable global state.  Calls that
+ *     share a workspace must be ordered on one stream by the caller.
+ *   - Positions are absolute token positions (int64).  Token p of a
+ *     sequence is the p-th token of its context, starting at 0.
+ *
+ * Formats (CSA_FMT_*)
+ *   F32        every element fp32 (the precision-check mode).
+ *   FP8_BF16   main KV entry of d dims: dims [0, d - d_rope) as OCP FP8 E4M3FN
+ *              (round-to-nearest-even, saturating, no scale) in the `nope`
+ *              array, the last d_rope dims as BF16 in the `rope` array [W2
+ *              stability paragraph; W3 section 二].  With d = 512, d_rope = 64
+ *              an entry is 448 + 128 = 576 bytes; a packed cache row places
+ *              `rope` at byte 448 of a 576-byte row (stride 576 for both).
+ *   MXFP4      OCP MX v1.0 FP4: per row, d/2 bytes of E2M1 codes (element 2j
+ *              in the low nibble of byte j) and d/32 E8M0 scale bytes, one per
+ *              block of 32 elements [W2 "FP4 QAT" section: the indexer QK path
+ *              runs in FP4].  Scale = 2^(floor(log2(amax)) - 2); elements
+ *              round-to-nearest-even and clamp to +-6.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+enum {
+  CSA_OK = 0,
+  CSA_EINVAL = -1,
+  CSA_EUNSUPPORTED = -2,
+  CSA_EHIP = -3,
+  CSA_EWORKSPACE = -4
+};
+
+enum { CSA_FMT_F32 = 0, CSA_FMT_FP8_BF16 = 1, CSA_FMT_MXFP4 = 2 };
+enum { CSA_DT_F32 = 0, CSA_DT_BF16 = 1 };
+enum { CSA_OP_COMPRESS = 0, CSA_OP_INDEX_TOPK = 1, CSA_OP_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
+
+/* Attention flags. */
+enum {
+  CSA_ATTEND_NORM_Q = 1,      /* RMS-normalise every query head first (weight 1, eps 1e-6) */
+  CSA_ATTEND_NO_INV_ROPE = 2  /* skip the inverse output rotation (test hook) */
+};
+
+/*
+ * ---------------------------------------------------------------- csa_compress
+ * Softmax-gated, position-biased pooling of every m tokens into one entry
+ * [W2 compression equation; W3 section 一; W4 注意力栈]:
+ *
+ *   C_i[c] = sum_{j=mi}^{mi+m-1} S_j[c] C^a_j[c] + sum_{j=m(i-1)}^{mi-1} S_j[c] C^b_j[c]
+ *
+ * where S is, for every channel c separately, the softmax over all the
+ * candidates of entry i of the logits Z^a_j[c] + B^a[j-mi][c] (a-branch) and
+ * Z^b_j[c] + B^b[j-m(i-1)][c] (b-branch).  The b-branch exists only with
+ * `overlap` (CSA, m = 4) and only for i >= 1; HCA (m = 128) has no overlap
+ * [W2 HCA section].  Then, per entry: optional RMSNorm over the d channels
+ * (weight 1, `rms_eps`) [W2 stability paragraph], optional RoPE of the last
+ * d_rope channels at position m*i (pairs (2u, 2u+1), angle
+ * m*i * theta^(-2u/d_rope)) [W1; W2 spec table], and storage in `out_fmt`.
+ *
+ * Row r of every input holds the token at absolute position pos0 + r for all
+ * B sequences (pos0 a multiple of m).  The call writes exactly the entries
+ * i in [i_first, i_end):
+ *     i_first = pos0/m + (overlap && pos0 > 0 ? 1 : 0),  i_end = (pos0 + n_rows)/m
+ * i.e. every complete block whose candidates are all present; with overlap
+ * and pos0 > 0 the first m rows only feed the b-branch.  Entry i lands at
+ * byte offset (i - out_row0) * out_stride (+ b * out_seq_stride) of each
+ * output array: out_row0 = 0 lets the outputs point at the base of a
+ * caller-owned cache; a window buffer that starts at position p0 passes
+ * out_row0 = p0 (i_first >= out_row0 is required).
+ *
+ * m = 1 with NULL gates and biases is the raw-window store: every row
+ * becomes entry pos0 + r after norm / rotation / storage.
+ *
+ *   in_dtype   CSA_DT_F32 or CSA_DT_BF16 for kv_* and gate_*.
+ *   kv_a/gate_a, kv_b/gate_b  [B][n_rows][d] at in_row_stride / in_seq_stride
+ *              bytes; gate_* NULL means logit 0; kv_b/gate_b must be NULL
+ *              without overlap and kv_b non-NULL with it.
+ *   bias_a, bias_b  fp32 [m][d] contiguous, or NULL (bias 0).
+ *   out_fmt F32:      out0 = fp32 [d] per entry.
+ *   out_fmt FP8_BF16: out0 = E4M3FN bytes [d - d_rope], out1 = BF16 [d_rope].
+ *   out_fmt MXFP4:    out0 = E2M1 codes [d/2], out1 = E8M0 scales [d/32]
+ *                     (d % 32 == 0, d_rope == 0, do_norm == 0 expected).
+ * Constraints: 1 <= m <= 1024, 1 <= d <= 1024, d % 8 == 0, d_rope even and
+ * <= d, n_rows >= 0, B >= 1.  n_rows = 0 or no complete block is a no-op.
+ */
+typedef struct CsaCompressArgs {
+  int32_t B;
+  int32_t n_rows;
+  int64_t pos0;
+  int32_t m;
+  int32_t overlap;
+  int32_t d;
+  int32_t d_rope;
+  int32_t in_dtype;
+  int32_t out_fmt;
+  int32_t do_norm;
+  float rms_eps;
+  double rope_theta;
+  const void* kv_a;
+  const void* gate_a;
+  const void* kv_b;
+  const void* gate_b;
+  int64_t in_row_stride;
+  int64_t in_seq_stride;
+  const float* bias_a;
+  const float* bias_b;
+  void* out0;
+  void* out1;
+  int64_t out_row0;
+  int64_t out0_stride;
+  int64_t out0_seq_stride;
+  int64_t out1_stride;
+  int64_t out1_seq_stride;
+} CsaCompressArgs;
+
+/*
+ * ---------------------------------------------------------------- csa_index_topk
+ * Lightning indexer and top-k selection [W2 CSA section and Fig. 2; W5 CSA
+ * step 2].  For query r of sequence b at position t = q_pos[b][r]:
+ *
+ *   n_vis = min(floor(t / m), n_entries[b])      (a query never selects the
+ *           block that contains it [W1 observation 1; W5 细节])
+ *   I_i   = sum_h w[b][r][h] * ReLU(q_I[b][r][h] . k_I[b][i])   for i < n_vis
+ *
+ * and out_idx[b][r][0 .. top_k) receives the indices of the top_k largest
+ * I_i, ties broken toward the lower index, written in ascending index order;
+ * with n_vis <= top_k every visible index is written and the rest is -1.
+ * Scores are accumulated in fp32 (E2M1 x E2M1 products and 32-element block
+ * sums are exact in fp32).
+ *
+ *   fmt F32:   q0 = fp32 [B][n_q][H_I][d_I]; k0 = fp32 [B][n_cap][d_I].
+ *   fmt MXFP4: q0 = codes [B][n_q][H_I][d_I/2], q1 = scales [B][n_q][H_I][d_I/32];
+ *              k0 = codes [B][n_cap][d_I/2],    k1 = scales [B][n_cap][d_I/32].
+ *   All four arrays are contiguous in the order shown.
+ *   q_pos      device int64 [B][n_q].
+ *   n_entries  device int32 [B] entries present per sequence (NULL = n_cap).
+ *   w          device fp32 [B][n_q][H_I] head weights (any sign).
+ *   out_idx    device int32 [B][n_q][top_k].
+ *   out_score  optional device fp32 [B][n_q][n_cap]: I_i for i < n_vis,
+ *              -inf beyond.
+ * Constraints: d_I % 32 == 0 and d_I <= 256 for MXFP4 (d_I == 128 and
+ * H_I % 16 == 0 take the matrix-core path); 1 <= top_k <= 4096;
+ * n_cap >= 1; m >= 1.
+ * Workspace: csa_workspace_bytes(CSA_OP_INDEX_TOPK, &args) bytes of device
+ * memory, 256-byte aligned, contents undefined on entry and exit.
+ */
+typedef struct CsaIndexArgs {
+  int32_t B;
+  int32_t n_q;
+  int32_t m;
+  int32_t n_cap;
+  int32_t H_I;
+  int32_t d_I;
+  int32_t fmt;
+  int32_t top_k;
+  const int64_t* q_pos;
+  const int32_t* n_entries;
+  const void* q0;
+  const void* q1;
+  const float* w;
+  const void* k0;
+  const void* k1;
+  int32_t* out_idx;
+  float* out_score;
+} CsaIndexArgs;
+
+/*
+ * ---------------------------------------------------------------- csa_attend / hca_attend
+ * Shared-KV multi-query attention with a per-head sink [W2 CSA/HCA intro and
+ * stability paragraph; W5 细节].  Every entry is both key and value.  For
+ * query r of sequence b at t = q_pos[b][r] and head h:
+ *
+ *   q'   = RoPE_t(RMSNorm(q_h))            (RMSNorm only with CSA_ATTEND_NORM_Q)
+ *   KV   = CSA: the compressed entries idx[b][r][*] that are >= 0 and
+ *              < n_vis = min(floor(t/m), n_entries[b])   (csa_attend)
+ *          HCA: every compressed entry i < n_vis         (hca_attend, idx NULL)
+ *          followed by the raw window tokens of positions
+ *          max(0, t-n_win+1) .. t that the window buffer holds [W1 sliding
+ *          window; W2 Fig. 2 caption: top-k entries concatenated with the window]
+ *   s_j  = softmax_scale * q' . kv_j        (softmax_scale 0 => 1/sqrt(d))
+ *   o_h  = sum_j e^{s_j} kv_j / (e^{sink[h]} + sum_j e^{s_j})
+ *   out  = o_h with its last d_rope dims rotated by -t (skipped with
+ *          CSA_ATTEND_NO_INV_ROPE)   [W2: inverse rotation of the output]
+ *   lse  = log sum_j e^{s_j} (the sink excluded; -inf with no KV rows)
+ *
+ *   fmt F32:      q, out fp32; entries / window fp32 rows in kv0 / win0.
+ *   fmt FP8_BF16: q, out BF16; entries / window in storage form (nope bytes
+ *                 in kv0 / win0, BF16 rope dims in kv1 / win1).
+ *   q, out       [B][n_q][H][d] contiguous.
+ *   kv*          row i of sequence b at kv*_base + b*kv_seq_stride + i*kv_stride.
+ *   win*         position p of sequence b at row p - win_pos0[b] of the window
+ *                buffer (rows 0 .. win_len-1, same addressing with win_stride
+ *                and win_seq_stride); positions the buffer does not hold are
+ *                skipped.
+ *   idx          int32 [B][n_q][top_k] (csa_attend); must be NULL for hca_attend.
+ *   sink         fp32 [H].
+ *   out_lse      optional fp32 [B][n_q][H].
+ * Constraints: FP8_BF16 needs d == 512, d_rope == 64 and H % 16 == 0;
+ * F32 needs d <= 512 and H <= 128.  1 <= n_win, win_len >= 0.
+ * Workspace: csa_workspace_bytes(CSA_OP_ATTEND / CSA_OP_HCA_ATTEND, &args).
+ */
+typedef struct CsaAttendArgs {
+  int32_t B;
+  int32_t n_q;
+  int32_t H;
+  int32_t d;
+  int32_t d_rope;
+  int32_t m;
+  int32_t fmt;
+  int32_t flags;
+  double rope_theta;
+  float softmax_scale;
+  int32_t top_k;
+  int32_t n_cap;
+  int32_t n_win;
+  int32_t win_len;
+  int32_t _pad0;
+  const int64_t* q_pos;
+  const void* q;
+  const void* kv0;
+  const void* kv1;
+  int64_t kv_stride;
+  int64_t kv_seq_stride;
+  const int32_t* n_entries;
+  const int32_t* idx;
+  const void* win0;
+  const void* win1;
+  int64_t win_stride;
+  int64_t win_seq_stride;
+  const int64_t* win_pos0;
+  const float* sink;
+  void* out;
+  float* out_lse;
+} CsaAttendArgs;
+
+/* ABI version of the loaded library (CSA_ABI_VERSION). */
+int csa_abi_version(void);
+
+/* Static text for a status code. */
+const char* csa_strerror(int status);
+
+/* sizeof the argument struct of `op` as compiled into the library, so a
+ * binding can check its own mirror of the layout. */
+size_t csa_args_size(int op);
+
+/* Device workspace in bytes that `op` needs for `args` (0 = none).  Returns
+ * (size_t)-1 for invalid arguments. */
+size_t csa_workspace_bytes(int op, const void* args);
+
+int csa_compress(const CsaCompressArgs* args, void* stream);
+int csa_index_topk(const CsaIndexArgs* args, void* workspace, size_t workspace_bytes, void* stream);
+int csa_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
+int hca_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

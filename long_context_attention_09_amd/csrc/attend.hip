@@ -1,0 +1,518 @@
+// Shared-KV multi-query attention with a per-head sink: CSA (gathered top-k
+// entries + raw window) and HCA (every visible entry + raw window).
+//
+// What is computed ("DeepSeek-V4 深读", ricardokevins.github.io, CSA/HCA
+// section and its stability paragraph; "拆解 DeepSeekv4", daixd5520.github.io,
+// section 细节): all query heads read one shared 512-d vector per entry that
+// serves as key and value; the last 64 dims of the query carry RoPE at the
+// query position and the output's last 64 dims are rotated back; exp(sink_h)
+// joins every head's softmax denominator.
+//
+// FP8_BF16 kernel (gfx950 matrix cores).  A workgroup owns one query, 64
+// heads (16 per wavefront) and one contiguous split of the query's KV list.
+// KV rows stream through LDS in tiles of 32 entries: the loader threads fetch
+// the 576-byte rows (448 E4M3FN bytes + 64 BF16 values) with 16-byte loads
+// into registers while the previous tile is being used, then widen FP8 to
+// BF16 (exact) into a row-major LDS tile.  Each wavefront then computes
+//   S^T[32 entries x 16 heads] = K Q^T     (V_MFMA_F32_16X16X32_BF16, 32 per tile)
+// with its query heads held in registers as the B operand, runs the online
+// softmax in the log2 domain, and accumulates
+//   O^T[512 dims x 16 heads] += V^T P^T    (32 MFMAs per tile)
+// where the B operand P^T is the S^T accumulator itself (the summation order
+// over the 32 entries is permuted to match the accumulator layout) and the A
+// operand V^T comes from the LDS tile through ds_read_b64_tr_b16 transposing
+// reads.  The O^T accumulator keeps one head per lane, so rescaling is a
+// per-lane multiply, done only when a running maximum grows.
+//
+// A split that covers the whole list finalises in place (sink, normalisation,
+// inverse RoPE, BF16 store); otherwise (running max, sum, numerator) partials
+// go to the workspace and combine_kernel merges them.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+constexpr int kD = 512;
+constexpr int kDR = 64;
+constexpr int kDN = kD - kDR;         // 448
+constexpr int kTile = 32;             // entries per LDS tile
+constexpr int kRowBytes = kD * 2 + 16;  // bf16 row + 16 B pad (conflict-free 16-byte row reads)
+constexpr int kChunksPerRow = kDN / 16 + (kDR * 2) / 16;  // 28 + 8 = 36 sixteen-byte chunks
+constexpr int kChunksPerTile = kTile * kChunksPerRow;     // 1152
+constexpr int kLoadsPerThread = (kChunksPerTile + 255) / 256;  // 5 (the last one partial)
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+struct ListInfo {
+  int n_comp;     // compressed part of the list (top_k for CSA, n_vis for HCA)
+  int n_vis;      // visible compressed entries
+  int win_lo;     // first window buffer row
+  int n_w;        // window rows present
+  int64_t t;
+};
+
+__device__ __forceinline__ ListInfo list_info(const AttendLaunch& a, int b, int r) {
+  ListInfo L;
+  const int64_t t = a.q_pos[(int64_t)b * a.n_q + r];
+  L.t = t;
+  int64_t nv = t >= 0 ? t / a.m : 0;
+  const int64_t ne = a.n_entries ? (int64_t)a.n_entries[b] : (int64_t)a.n_cap;
+  nv = nv < ne ? nv : ne;
+  nv = nv < a.n_cap ? nv : a.n_cap;
+  L.n_vis = (int)(nv < 0 ? 0 : nv);
+  L.n_comp = a.idx ? a.top_k : L.n_vis;
+  const int64_t wp0 = a.win_pos0[b];
+  int64_t lo = t - a.n_win + 1;
+  lo = lo > 0 ? lo : 0;
+  lo = lo > wp0 ? lo : wp0;
+  int64_t hi = t < wp0 + a.win_len - 1 ? t : wp0 + a.win_len - 1;
+  L.win_lo = (int)(lo - wp0);
+  L.n_w = hi >= lo ? (int)(hi - lo + 1) : 0;
+  return L;
+}
+
+// Resolve list position p to (nope row pointer, rope row pointer); false when masked.
+__device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, const ListInfo& L, int p,
+                                         const uint8_t** pn, const uint8_t** pr) {
+  if (p < L.n_comp) {
+    int e = p;
+    if (a.idx) {
+      e = a.idx[((int64_t)b * a.n_q + r) * a.top_k + p];
+      if (e < 0 || e >= L.n_vis) return false;
+    }
+    const int64_t off = (int64_t)b * a.kv_seq_stride + (int64_t)e * a.kv_stride;
+    *pn = (const uint8_t*)a.kv0 + off;
+    *pr = (const uint8_t*)a.kv1 + off;
+    return true;
+  }
+  const int w = p - L.n_comp;
+  if (w >= L.n_w) return false;
+  const int64_t off = (int64_t)b * a.win_seq_stride + (int64_t)(L.win_lo + w) * a.win_stride;
+  *pn = (const uint8_t*)a.win0 + off;
+  *pr = (const uint8_t*)a.win1 + off;
+  return true;
+}
+
+__device__ __forceinline__ uint32_t pack_hi16(float f0, float f1) {
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+__global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* tile = smem;                                   // [kTile][kRowBytes]
+  int* valid = (int*)(smem + kTile * kRowBytes);          // [kTile]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int split = blockIdx.x, hg = blockIdx.y;
+  const int br = blockIdx.z;
+  const int b = br / a.n_q, r = br % a.n_q;
+  const int head = hg * 64 + wave * 16 + col;
+  const bool head_ok = head < a.H;
+  const ListInfo L = list_info(a, b, r);
+  const int list_len = L.n_comp + L.n_w;
+  const int p0 = split * a.split_len;
+  int p1 = p0 + a.split_len;
+  p1 = p1 < list_len ? p1 : list_len;
+
+  // ---- query operand: head `head`, dims 32kb + 8g + j, RMSNorm, RoPE at t, BF16
+  bf16x8 qv[16];
+  {
+    const int hq = head_ok ? head : 0;
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + hq) * kD;
+    float x[16][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      const i32x4 v = *(const i32x4*)(qrow + 32 * kb + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[kb][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
+        x[kb][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
+        ss += x[kb][2 * j] * x[kb][2 * j] + x[kb][2 * j + 1] * x[kb][2 * j + 1];
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[kb][j] *= rs;
+#pragma unroll
+    for (int kb = 14; kb < 16; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int u = (32 * kb + 8 * g + j - kDN) >> 1;
+        float cs, sn;
+        rope_cos_sin((double)L.t, u, kDR, a.log_theta, &cs, &sn);
+        const float xe = x[kb][j], xo = x[kb][j + 1];
+        x[kb][j] = xe * cs - xo * sn;
+        x[kb][j + 1] = xe * sn + xo * cs;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[kb][j] = u16_as_bf16(f32_to_bf16(x[kb][j]));
+  }
+
+  f32x4 acc_o[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;     // log2 domain, per head (same value in the 4 lanes of a head)
+  float l_part = 0.f;          // this lane's share of the running denominator
+
+  // ---- tile loader: 36 chunks of 16 B per row
+  i32x4 stage[kLoadsPerThread];
+  auto fetch = [&](int tile0) {
+#pragma unroll
+    for (int k = 0; k < kLoadsPerThread; ++k) {
+      const int c = tid + 256 * k;
+      stage[k] = (i32x4){0, 0, 0, 0};
+      if (c < kChunksPerTile) {
+        const int e = c / kChunksPerRow, part = c % kChunksPerRow;
+        const int p = tile0 + e;
+        const uint8_t *pn, *pr;
+        if (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) {
+          const uint8_t* src = part < 28 ? pn + part * 16 : pr + (part - 28) * 16;
+          stage[k] = *(const i32x4*)src;
+        }
+      }
+    }
+  };
+  auto commit = [&](int tile0) {
+#pragma unroll
+    for (int k = 0; k < kLoadsPerThread; ++k) {
+      const int c = tid + 256 * k;
+      if (c < kChunksPerTile) {
+        const int e = c / kChunksPerRow, part = c % kChunksPerRow;
+        uint8_t* row = tile + e * kRowBytes;
+        if (part < 28) {
+          i32x4 lo, hi;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(stage[k][j], false);
+            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(stage[k][j], true);
+            const uint32_t w0 = pack_hi16(f01[0], f01[1]);
+            const uint32_t w1 = pack_hi16(f23[0], f23[1]);
+            if (j < 2) { lo[2 * j] = (int)w0; lo[2 * j + 1] = (int)w1; }
+            else { hi[2 * (j - 2)] = (int)w0; hi[2 * (j - 2) + 1] = (int)w1; }
+          }
+          *(i32x4*)(row + part * 32) = lo;
+          *(i32x4*)(row + part * 32 + 16) = hi;
+        } else {
+          *(i32x4*)(row + kDN * 2 + (part - 28) * 16) = stage[k];
+        }
+      }
+    }
+    if (tid < kTile) {
+      const uint8_t *pn, *pr;
+      const int p = tile0 + tid;
+      valid[tid] = (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) ? 1 : 0;
+    }
+  };
+
+  if (p0 < p1) {
+    fetch(p0);
+    commit(p0);
+  }
+  __syncthreads();
+
+  for (int tile0 = p0; tile0 < p1; tile0 += kTile) {
+    const bool more = tile0 + kTile < p1;
+    if (more) fetch(tile0 + kTile);
+
+    // S^T = K Q^T : two 16-entry blocks
+    f32x4 s[2];
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      s[eb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + 16 * g;
+#pragma unroll
+      for (int kb = 0; kb < 16; ++kb) {
+        const bf16x8 kv = *(const bf16x8*)(krow + 64 * kb);
+        s[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[kb], s[eb], 0, 0, 0);
+      }
+    }
+    // online softmax (log2 domain); lane holds entries eb*16 + 4g + i of head `col`
+    float mx = -INFINITY;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = valid[eb * 16 + 4 * g + i] ? s[eb][i] * a.scale_log2 : -INFINITY;
+        s[eb][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);    // 0 while nothing was seen, 1 if the max holds
+    bf16x8 pv;
+    float psum = 0.f;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(s[eb][i] - m_use);
+        psum += p;
+        pv[eb * 4 + i] = u16_as_bf16(f32_to_bf16(p));
+      }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) acc_o[db] *= alpha;
+    }
+    // O^T += V^T P^T ; lane (g, col) supplies row 4g + col/4 (+16) at dims 16db + 4(col%4)
+    const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + 8 * (col & 3);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * db));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRowBytes + 32 * db));
+      bf16x8 vt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vt[j] = u16_as_bf16((uint16_t)lo[j]);
+        vt[4 + j] = u16_as_bf16((uint16_t)hi[j]);
+      }
+      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[db], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) commit(tile0 + kTile);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  float l_run = l_part + __shfl_xor(l_part, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (!head_ok) return;
+  const int64_t unit = (int64_t)br * gridDim.y + hg;
+  if (a.n_splits == 1) {
+    const float z2 = a.sink[head] * kLog2e;
+    const float top = fmaxf(m_run, z2);
+    const float den = l_run * exp2f(m_run - top) + exp2f(z2 - top);
+    const float inv = exp2f(m_run - top) / den;      // 0 when no row was seen
+    uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc_o[db][i] * inv;
+      if (db >= 28 && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const int u = (16 * db + 4 * g + i - kDN) >> 1;
+          float cs, sn;
+          rope_cos_sin(-(double)L.t, u, kDR, a.log_theta, &cs, &sn);
+          const float xe = o[i], xo = o[i + 1];
+          o[i] = xe * cs - xo * sn;
+          o[i + 1] = xe * sn + xo * cs;
+        }
+      }
+      const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+      *(i32x2*)(orow + 16 * db + 4 * g) = (i32x2){(int)w0, (int)w1};
+    }
+    if (a.out_lse && g == 0)
+      a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
+          l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  } else {
+    const int64_t ps = (unit * a.n_splits + split) * 64 + wave * 16 + col;
+    float* po = a.part_o + ps * kD;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *(f32x4*)(po + 16 * db + 4 * g) = acc_o[db];
+    if (g == 0) {
+      a.part_ml[ps * 2] = m_run;
+      a.part_ml[ps * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Merge the split partials of one (query, 64-head group): 4 threads per head,
+// 128 dims each.
+__global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) {
+  const int unit = blockIdx.x;                 // br * n_hg + hg
+  const int br = unit / n_hg, hg = unit % n_hg;
+  const int b = br / a.n_q, r = br % a.n_q;
+  const int hl = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int head = hg * 64 + hl;
+  if (head >= a.H) return;
+  const int64_t t = a.q_pos[(int64_t)b * a.n_q + r];
+  const int64_t base = (int64_t)unit * a.n_splits * 64 + hl;
+  float top = a.sink[head] * kLog2e;
+  for (int s = 0; s < a.n_splits; ++s) top = fmaxf(top, a.part_ml[(base + s * 64) * 2]);
+  float den = exp2f(a.sink[head] * kLog2e - top);
+  float lsum = 0.f;
+  float o[128];
+#pragma unroll
+  for (int i = 0; i < 128; ++i) o[i] = 0.f;
+  float mmax = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) mmax = fmaxf(mmax, a.part_ml[(base + s * 64) * 2]);
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float ms = a.part_ml[(base + s * 64) * 2];
+    const float ls = a.part_ml[(base + s * 64) * 2 + 1];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - top);
+    den += ls * wgt;
+    lsum += ls * exp2f(ms - mmax);
+    const float* po = a.part_o + (base + s * 64) * kD + part * 128;
+#pragma unroll
+    for (int i = 0; i < 128; i += 4) {
+      const f32x4 v = *(const f32x4*)(po + i);
+      o[i] += v[0] * wgt; o[i + 1] += v[1] * wgt; o[i + 2] += v[2] * wgt; o[i + 3] += v[3] * wgt;
+    }
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int i = 0; i < 128; ++i) o[i] *= inv;
+  if (part == 3 && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
+    // dims 448 .. 511 are o[64 .. 127]
+#pragma unroll
+    for (int i = 64; i < 128; i += 2) {
+      float cs, sn;
+      rope_cos_sin(-(double)t, (i - 64) >> 1, kDR, a.log_theta, &cs, &sn);
+      const float xe = o[i], xo = o[i + 1];
+      o[i] = xe * cs - xo * sn;
+      o[i + 1] = xe * sn + xo * cs;
+    }
+  }
+  uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD + part * 128;
+#pragma unroll
+  for (int i = 0; i < 128; i += 8) {
+    i32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (int)((uint32_t)f32_to_bf16(o[i + 2 * j]) | ((uint32_t)f32_to_bf16(o[i + 2 * j + 1]) << 16));
+    *(i32x4*)(orow + i) = w;
+  }
+  if (a.out_lse && part == 0)
+    a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
+        lsum > 0.f ? (mmax + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
+}
+
+// ------------------------------------------------------------------ fp32 precision mode
+
+// One workgroup per (query, head); rows in chunks of 256 with an online softmax.
+__global__ void __launch_bounds__(256) attend_f32_kernel(AttendLaunch a) {
+  __shared__ float qs[kD];
+  __shared__ float ps[256];
+  __shared__ float red[8];
+  __shared__ const float* rowp[256];
+  const int br = blockIdx.x, head = blockIdx.y;
+  const int b = br / a.n_q, r = br % a.n_q;
+  const int tid = threadIdx.x;
+  const int d = a.d, d0 = a.d - a.d_rope;
+  const ListInfo L = list_info(a, b, r);
+  const float* q = (const float*)a.q + (((int64_t)b * a.n_q + r) * a.H + head) * d;
+  auto block_sum = [&](float v) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+  };
+  auto block_max = [&](float v) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  };
+  float ss = 0.f;
+  for (int c = tid; c < d; c += 256) ss += q[c] * q[c];
+  ss = block_sum(ss);
+  const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)d + 1e-6f) : 1.0f;
+  for (int c = tid; c < d; c += 256) {
+    float v = q[c] * rs;
+    if (c >= d0) {
+      const int pc = c ^ 1;
+      const float w = q[pc] * rs;
+      float cs, sn;
+      rope_cos_sin((double)L.t, (c - d0) >> 1, a.d_rope, a.log_theta, &cs, &sn);
+      v = (c & 1) == 0 ? v * cs - w * sn : w * sn + v * cs;
+    }
+    qs[c] = v;
+  }
+  __syncthreads();
+  const int list_len = L.n_comp + L.n_w;
+  float m_run = -INFINITY, l_run = 0.f;
+  float o0 = 0.f, o1 = 0.f;     // dims tid and tid + 256
+  for (int c0 = 0; c0 < list_len; c0 += 256) {
+    const int p = c0 + tid;
+    float s = -INFINITY;
+    const uint8_t *pn = nullptr, *pr = nullptr;
+    if (p < list_len && list_row(a, b, r, L, p, &pn, &pr)) {
+      const float* row = (const float*)pn;
+      float dot = 0.f;
+      for (int c = 0; c < d; ++c) dot = fmaf(qs[c], row[c], dot);
+      s = dot * a.scale_log2;
+      rowp[tid] = row;
+    } else {
+      rowp[tid] = nullptr;
+    }
+    const float mx = block_max(s);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float p_ = exp2f(s - m_use);
+    ps[tid] = p_;
+    const float psum = block_sum(p_);
+    const float alpha = exp2f(m_run - m_use);
+    l_run = l_run * alpha + psum;
+    o0 *= alpha;
+    o1 *= alpha;
+    m_run = m_new;
+    __syncthreads();
+    const int n = list_len - c0 < 256 ? list_len - c0 : 256;
+    for (int j = 0; j < n; ++j) {
+      const float* row = rowp[j];
+      if (!row) continue;
+      const float pj = ps[j];
+      if (tid < d) o0 = fmaf(pj, row[tid], o0);
+      if (tid + 256 < d) o1 = fmaf(pj, row[tid + 256], o1);
+    }
+    __syncthreads();
+  }
+  const float z2 = a.sink[head] * kLog2e;
+  const float top = fmaxf(m_run, z2);
+  const float den = l_run * exp2f(m_run - top) + exp2f(z2 - top);
+  const float inv = exp2f(m_run - top) / den;
+  __shared__ float os[kD];
+  if (tid < d) os[tid] = o0 * inv;
+  if (tid + 256 < d) os[tid + 256] = o1 * inv;
+  __syncthreads();
+  float* orow = (float*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * d;
+  for (int c = tid; c < d; c += 256) {
+    float v = os[c];
+    if (c >= d0 && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
+      const float w = os[c ^ 1];
+      float cs, sn;
+      rope_cos_sin(-(double)L.t, (c - d0) >> 1, a.d_rope, a.log_theta, &cs, &sn);
+      v = (c & 1) == 0 ? v * cs - w * sn : w * sn + v * cs;
+    }
+    orow[c] = v;
+  }
+  if (a.out_lse && tid == 0)
+    a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
+        l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+}
+
+hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
+  if (a.fmt == CSA_FMT_F32) {
+    dim3 grid(a.B * a.n_q, a.H);
+    attend_f32_kernel<<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  const int n_hg = (a.H + 63) / 64;
+  dim3 grid(a.n_splits, n_hg, a.B * a.n_q);
+  const size_t smem = kTile * kRowBytes + kTile * sizeof(int);
+  attend_fp8_kernel<<<grid, 256, smem, s>>>(a);
+  if (a.n_splits > 1) combine_kernel<<<a.B * a.n_q * n_hg, 256, 0, s>>>(a, n_hg);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,135 @@
+// Device helpers shared by the gfx950 kernels: storage codecs, RoPE angles,
+// wave reductions and MFMA operand types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ BF16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+__device__ __forceinline__ __bf16 u16_as_bf16(uint16_t u) { return __builtin_bit_cast(__bf16, u); }
+
+// ------------------------------------------------------------------ FP8 E4M3FN
+
+// Decode one byte exactly (OCP E4M3FN: bias 7, no inf, S.1111.111 = NaN).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = (c >> 7) & 1u, e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;  // m/8 * 2^-6
+  else if (e == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return s ? -v : v;
+}
+
+// Round-to-nearest-even fp32 -> E4M3FN, saturating at +-448; keeps the sign of
+// values that round to zero.  Scaling by powers of two is exact, so rintf
+// (round-half-even) on the scaled value gives the correctly rounded code.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (a != a) return sign | 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid step 2^-9
+    const uint32_t q = (uint32_t)rintf(a * 512.0f);  // 0 .. 8 (8 = min normal)
+    return sign | q;
+  }
+  int e;
+  const float fr = frexpf(a, &e);            // a = fr * 2^e, fr in [0.5, 1)
+  int E = e - 1;                              // a = (2 fr) * 2^E, 2fr in [1, 2)
+  uint32_t mant = (uint32_t)rintf((2.0f * fr - 1.0f) * 8.0f);
+  if (mant == 8) { mant = 0; ++E; }
+  uint32_t code = ((uint32_t)(E + 7) << 3) | mant;
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
+  const float mags[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  const float v = mags[n & 7u];
+  return (n & 8u) ? -v : v;
+}
+
+// Shared block exponent floor(log2(amax)) - 2 clamped to [-127, 127]; zero -> -127.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e;
+  frexpf(amax, &e);
+  int E = (e - 1) - 2;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// Nearest E2M1 code of |v| with ties to the even code, clamped to 6; the
+// thresholds are the midpoints of the grid {0, .5, 1, 1.5, 2, 3, 4, 6}
+// (a tie goes to the neighbour with an even code).
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float v = fabsf(x);
+  uint32_t c = (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) +
+               (v >= 3.5f) + (v > 5.0f);
+  return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// ------------------------------------------------------------------ RoPE
+
+// cos / sin of pos * theta^(-2u/d_rope), with the angle formed and reduced in
+// fp64: at positions near 2^20 an fp32 angle would be off by ~0.06 rad.
+__device__ __forceinline__ void rope_cos_sin(double pos, int u, int d_rope, double log_theta,
+                                             float* c, float* s) {
+  const double inv_freq = exp(-2.0 * (double)u / (double)d_rope * log_theta);
+  double ang = pos * inv_freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang = ang - two_pi * floor(ang / two_pi);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *c = (float)cd;
+  *s = (float)sd;
+}
+
+// ------------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// fp32 score -> uint32 whose unsigned order is the float order.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t x = __float_as_uint(f);
+  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+}
+
+}  // namespace csa

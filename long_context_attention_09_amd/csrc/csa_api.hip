@@ -1,0 +1,328 @@
+// Host side of the C ABI declared in include/csa.h: argument validation,
+// workspace sizing and kernel launches.  No allocation, no synchronisation,
+// no global mutable state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "csa.h"
+#include "kernels.hpp"
+
+#define CSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kIdxChunk = 4096;       // scores per workgroup in the radix passes
+constexpr int64_t kScoreBudget = int64_t(1) << 28;   // fp32 scores held per query block (1 GiB)
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ------------------------------------------------------------------ compress
+
+int check_compress(const CsaCompressArgs* a) {
+  if (!a) return CSA_EINVAL;
+  if (a->B < 1 || a->n_rows < 0 || a->m < 1 || a->m > 1024 || a->d < 1 || a->d > 1024) return CSA_EINVAL;
+  if (a->d % 8 || a->d_rope < 0 || a->d_rope > a->d || (a->d_rope & 1)) return CSA_EINVAL;
+  if (a->pos0 < 0 || a->pos0 % a->m) return CSA_EINVAL;
+  if (a->in_dtype != CSA_DT_F32 && a->in_dtype != CSA_DT_BF16) return CSA_EINVAL;
+  if (a->out_fmt != CSA_FMT_F32 && a->out_fmt != CSA_FMT_FP8_BF16 && a->out_fmt != CSA_FMT_MXFP4)
+    return CSA_EINVAL;
+  if (a->overlap != 0 && a->overlap != 1) return CSA_EINVAL;
+  if (!a->kv_a || !a->out0) return CSA_EINVAL;
+  if (a->overlap && !a->kv_b) return CSA_EINVAL;
+  if (!a->overlap && (a->kv_b || a->gate_b || a->bias_b)) return CSA_EINVAL;
+  if (a->out_fmt != CSA_FMT_F32 && !a->out1) return CSA_EINVAL;
+  if (!(a->rms_eps >= 0.0f) || (a->d_rope > 0 && !(a->rope_theta > 0.0))) return CSA_EINVAL;
+  const size_t es = a->in_dtype == CSA_DT_F32 ? 4 : 2;
+  if (a->in_row_stride < (int64_t)(a->d * es) || a->in_row_stride % es || a->in_seq_stride < 0 ||
+      a->in_seq_stride % es)
+    return CSA_EINVAL;
+  const void* ins[4] = {a->kv_a, a->gate_a, a->kv_b, a->gate_b};
+  for (const void* p : ins)
+    if (p && !aligned(p, es)) return CSA_EINVAL;
+  if (a->bias_a && !aligned(a->bias_a, 4)) return CSA_EINVAL;
+  if (a->bias_b && !aligned(a->bias_b, 4)) return CSA_EINVAL;
+  if (a->out0_stride <= 0 || a->out0_seq_stride < 0) return CSA_EINVAL;
+  if (a->out_fmt == CSA_FMT_F32) {
+    if (!aligned(a->out0, 4) || a->out0_stride % 4 || a->out0_seq_stride % 4 ||
+        a->out0_stride < (int64_t)a->d * 4)
+      return CSA_EINVAL;
+  } else if (a->out_fmt == CSA_FMT_FP8_BF16) {
+    if (a->out1_stride <= 0 || a->out1_seq_stride < 0 || !aligned(a->out1, 2) || a->out1_stride % 2 ||
+        a->out1_seq_stride % 2)
+      return CSA_EINVAL;
+  } else {
+    if (a->d % 32 || a->d_rope != 0) return CSA_EUNSUPPORTED;
+    if (a->out1_stride <= 0 || a->out1_seq_stride < 0) return CSA_EINVAL;
+  }
+  return CSA_OK;
+}
+
+// ------------------------------------------------------------------ index / top-k
+
+int check_index(const CsaIndexArgs* a) {
+  if (!a) return CSA_EINVAL;
+  if (a->B < 1 || a->n_q < 1 || a->m < 1 || a->n_cap < 1 || a->H_I < 1 || a->d_I < 1 || a->top_k < 1)
+    return CSA_EINVAL;
+  if (!a->q_pos || !a->q0 || !a->w || !a->k0 || !a->out_idx) return CSA_EINVAL;
+  if (!aligned(a->q_pos, 8) || !aligned(a->w, 4) || !aligned(a->out_idx, 4)) return CSA_EINVAL;
+  if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
+  if (a->out_score && !aligned(a->out_score, 4)) return CSA_EINVAL;
+  if (a->fmt == CSA_FMT_MXFP4) {
+    if (!a->q1 || !a->k1) return CSA_EINVAL;
+    if (a->d_I != 128 || a->H_I % 16 || a->H_I > 64) return CSA_EUNSUPPORTED;
+    if (!aligned(a->q0, 16) || !aligned(a->k0, 16) || !aligned(a->k1, 4)) return CSA_EINVAL;
+  } else if (a->fmt == CSA_FMT_F32) {
+    if (a->d_I > 1024) return CSA_EUNSUPPORTED;
+    if (!aligned(a->q0, 4) || !aligned(a->k0, 4)) return CSA_EINVAL;
+  } else {
+    return CSA_EINVAL;
+  }
+  return CSA_OK;
+}
+
+struct IndexPlan {
+  int n_qb, n_chunks;
+  size_t off_scores, off_hist, off_state, off_counts, total;
+};
+
+IndexPlan plan_index(const CsaIndexArgs* a) {
+  IndexPlan p;
+  p.n_chunks = (a->n_cap + kIdxChunk - 1) / kIdxChunk;
+  if (a->out_score) {
+    p.n_qb = a->n_q;
+  } else {
+    int64_t per_q = (int64_t)a->B * a->n_cap;
+    int64_t n = kScoreBudget / (per_q > 0 ? per_q : 1);
+    if (n < 1) n = 1;
+    if (n > a->n_q) n = a->n_q;
+    if (n >= 4) n -= n % 4;
+    p.n_qb = (int)n;
+  }
+  const size_t nq = (size_t)a->B * p.n_qb;
+  size_t off = 0;
+  p.off_scores = off;
+  if (!a->out_score) off += align_up(nq * (size_t)a->n_cap * 4);
+  p.off_hist = off;
+  off += align_up(nq * 2048 * 4);
+  p.off_state = off;
+  off += align_up(nq * sizeof(csa::TopkState));
+  p.off_counts = off;
+  off += align_up(nq * (size_t)p.n_chunks * 2 * 4);
+  p.total = off;
+  return p;
+}
+
+// ------------------------------------------------------------------ attention
+
+int check_attend(const CsaAttendArgs* a, bool dense) {
+  if (!a) return CSA_EINVAL;
+  if (a->B < 1 || a->n_q < 1 || a->H < 1 || a->d < 1 || a->m < 1 || a->n_win < 1 || a->win_len < 0 ||
+      a->n_cap < 0)
+    return CSA_EINVAL;
+  if (a->d_rope < 0 || a->d_rope > a->d || (a->d_rope & 1)) return CSA_EINVAL;
+  if (a->d_rope > 0 && !(a->rope_theta > 0.0)) return CSA_EINVAL;
+  if (!(a->softmax_scale >= 0.0f)) return CSA_EINVAL;
+  if (!a->q_pos || !a->q || !a->sink || !a->out || !a->win_pos0) return CSA_EINVAL;
+  if (a->n_cap > 0 && !a->kv0) return CSA_EINVAL;
+  if (a->win_len > 0 && !a->win0) return CSA_EINVAL;
+  if (dense ? a->idx != nullptr : (a->idx == nullptr || a->top_k < 1)) return CSA_EINVAL;
+  if (!aligned(a->q_pos, 8) || !aligned(a->win_pos0, 8) || !aligned(a->sink, 4)) return CSA_EINVAL;
+  if (a->idx && !aligned(a->idx, 4)) return CSA_EINVAL;
+  if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
+  if (a->out_lse && !aligned(a->out_lse, 4)) return CSA_EINVAL;
+  if (a->kv_stride < 0 || a->kv_seq_stride < 0 || a->win_stride < 0 || a->win_seq_stride < 0)
+    return CSA_EINVAL;
+  if (a->fmt == CSA_FMT_FP8_BF16) {
+    if (a->d != 512 || a->d_rope != 64 || a->H % 16) return CSA_EUNSUPPORTED;
+    if (a->n_cap > 0 && !a->kv1) return CSA_EINVAL;
+    if (a->win_len > 0 && !a->win1) return CSA_EINVAL;
+    const void* ps[5] = {a->q, a->kv0, a->kv1, a->win0, a->win1};
+    for (const void* p : ps)
+      if (p && !aligned(p, 16)) return CSA_EINVAL;
+    if (!aligned(a->out, 8)) return CSA_EINVAL;
+    if (a->kv_stride % 16 || a->kv_seq_stride % 16 || a->win_stride % 16 || a->win_seq_stride % 16)
+      return CSA_EINVAL;
+  } else if (a->fmt == CSA_FMT_F32) {
+    if (a->d > 512 || (a->d & 1) || a->H > 65535) return CSA_EUNSUPPORTED;
+    const void* ps[3] = {a->q, a->kv0, a->win0};
+    for (const void* p : ps)
+      if (p && !aligned(p, 4)) return CSA_EINVAL;
+    if (!aligned(a->out, 4)) return CSA_EINVAL;
+    if (a->kv_stride % 4 || a->kv_seq_stride % 4 || a->win_stride % 4 || a->win_seq_stride % 4)
+      return CSA_EINVAL;
+  } else {
+    return CSA_EINVAL;
+  }
+  return CSA_OK;
+}
+
+struct AttendPlan {
+  int n_splits, split_len, list_len;
+  size_t off_o, off_ml, total;
+};
+
+AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
+  AttendPlan p{};
+  const int64_t comp = dense ? a->n_cap : a->top_k;
+  int64_t list = comp + a->n_win;
+  if (list < 1) list = 1;
+  p.list_len = (int)list;
+  if (a->fmt == CSA_FMT_F32) {
+    p.n_splits = 1;
+    p.split_len = p.list_len;
+    p.total = 0;
+    return p;
+  }
+  const int64_t units = (int64_t)a->B * a->n_q * ((a->H + 63) / 64);
+  int64_t s = (512 + units - 1) / units;          // aim for ~2 workgroups per compute unit
+  int64_t s_max = (list + 63) / 64;               // at least two 32-entry tiles per split
+  if (s > s_max) s = s_max;
+  if (s < 1) s = 1;
+  int64_t len = (list + s - 1) / s;
+  len = (len + 31) / 32 * 32;
+  s = (list + len - 1) / len;
+  p.n_splits = (int)s;
+  p.split_len = (int)len;
+  if (s > 1) {
+    const size_t rows = (size_t)units * s * 64;
+    p.off_o = 0;
+    p.off_ml = align_up(rows * 512 * 4);
+    p.total = p.off_ml + align_up(rows * 2 * 4);
+  } else {
+    p.total = 0;
+  }
+  return p;
+}
+
+int run_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream, bool dense) {
+  int st = check_attend(a, dense);
+  if (st) return st;
+  const AttendPlan p = plan_attend(a, dense);
+  if (p.total > 0 && (!ws || ws_bytes < p.total || !aligned(ws, kAlign))) return CSA_EWORKSPACE;
+  csa::AttendLaunch L{};
+  L.B = a->B; L.n_q = a->n_q; L.H = a->H; L.d = a->d; L.d_rope = a->d_rope; L.m = a->m;
+  L.fmt = a->fmt; L.flags = a->flags;
+  L.log_theta = a->d_rope > 0 ? log(a->rope_theta) : 0.0;
+  const float scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf((float)a->d);
+  L.scale_log2 = scale * 1.4426950408889634f;
+  L.top_k = dense ? 0 : a->top_k;
+  L.n_cap = a->n_cap; L.n_win = a->n_win; L.win_len = a->win_len;
+  L.n_splits = p.n_splits; L.list_len = p.list_len; L.split_len = p.split_len;
+  L.q_pos = a->q_pos; L.q = a->q; L.kv0 = a->kv0;
+  L.kv1 = a->kv1;
+  L.kv_stride = a->kv_stride; L.kv_seq_stride = a->kv_seq_stride;
+  L.n_entries = a->n_entries; L.idx = dense ? nullptr : a->idx;
+  L.win0 = a->win0; L.win1 = a->win1; L.win_stride = a->win_stride; L.win_seq_stride = a->win_seq_stride;
+  L.win_pos0 = a->win_pos0; L.sink = a->sink; L.out = a->out; L.out_lse = a->out_lse;
+  if (p.total > 0) {
+    L.part_o = (float*)((char*)ws + p.off_o);
+    L.part_ml = (float*)((char*)ws + p.off_ml);
+  }
+  if (csa::launch_attend(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
+  return CSA_OK;
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+CSA_EXPORT const char* csa_strerror(int status) {
+  switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_EINVAL: return "invalid argument (null or misaligned pointer, or inconsistent shape)";
+    case CSA_EUNSUPPORTED: return "unsupported shape or format combination";
+    case CSA_EHIP: return "HIP runtime reported a launch error";
+    case CSA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    default: return "unknown status";
+  }
+}
+
+CSA_EXPORT size_t csa_args_size(int op) {
+  switch (op) {
+    case CSA_OP_COMPRESS: return sizeof(CsaCompressArgs);
+    case CSA_OP_INDEX_TOPK: return sizeof(CsaIndexArgs);
+    case CSA_OP_ATTEND:
+    case CSA_OP_HCA_ATTEND: return sizeof(CsaAttendArgs);
+    default: return 0;
+  }
+}
+
+CSA_EXPORT size_t csa_workspace_bytes(int op, const void* args) {
+  switch (op) {
+    case CSA_OP_COMPRESS:
+      return check_compress((const CsaCompressArgs*)args) ? (size_t)-1 : 0;
+    case CSA_OP_INDEX_TOPK: {
+      const CsaIndexArgs* a = (const CsaIndexArgs*)args;
+      if (check_index(a)) return (size_t)-1;
+      return plan_index(a).total;
+    }
+    case CSA_OP_ATTEND:
+    case CSA_OP_HCA_ATTEND: {
+      const CsaAttendArgs* a = (const CsaAttendArgs*)args;
+      const bool dense = op == CSA_OP_HCA_ATTEND;
+      if (check_attend(a, dense)) return (size_t)-1;
+      return plan_attend(a, dense).total;
+    }
+    default: return (size_t)-1;
+  }
+}
+
+CSA_EXPORT int csa_compress(const CsaCompressArgs* a, void* stream) {
+  int st = check_compress(a);
+  if (st) return st;
+  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
+  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  if (end <= first) return CSA_OK;
+  if (first < a->out_row0) return CSA_EINVAL;
+  if (end - first > INT32_MAX / 4) return CSA_EUNSUPPORTED;
+  csa::CompressLaunch L{};
+  L.B = a->B; L.d = a->d; L.d_rope = a->d_rope; L.m = a->m; L.in_dtype = a->in_dtype;
+  L.out_fmt = a->out_fmt; L.do_norm = a->do_norm; L.n_entries = (int32_t)(end - first);
+  L.rms_eps = a->rms_eps; L.log_theta = a->d_rope > 0 ? log(a->rope_theta) : 0.0;
+  L.pos0 = a->pos0; L.i_first = first; L.out_row0 = a->out_row0;
+  L.kv_a = a->kv_a; L.gate_a = a->gate_a; L.kv_b = a->kv_b; L.gate_b = a->gate_b;
+  L.in_row_stride = a->in_row_stride;
+  L.in_seq_stride = a->in_seq_stride;
+  L.bias_a = a->bias_a; L.bias_b = a->bias_b;
+  L.out0 = a->out0; L.out1 = a->out1;
+  L.out0_stride = a->out0_stride; L.out0_seq_stride = a->out0_seq_stride;
+  L.out1_stride = a->out1_stride; L.out1_seq_stride = a->out1_seq_stride;
+  if (csa::launch_compress(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
+  return CSA_OK;
+}
+
+CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_index(a);
+  if (st) return st;
+  const IndexPlan p = plan_index(a);
+  if (!ws || ws_bytes < p.total || !aligned(ws, kAlign)) return CSA_EWORKSPACE;
+  for (int q0 = 0; q0 < a->n_q; q0 += p.n_qb) {
+    csa::IndexLaunch L{};
+    L.B = a->B; L.n_q = a->n_q; L.m = a->m; L.n_cap = a->n_cap; L.H_I = a->H_I; L.d_I = a->d_I;
+    L.fmt = a->fmt; L.top_k = a->top_k; L.n_chunks = p.n_chunks;
+    L.q_first = q0;
+    L.n_qb = a->n_q - q0 < p.n_qb ? a->n_q - q0 : p.n_qb;
+    L.q_pos = a->q_pos; L.n_entries = a->n_entries;
+    L.q0 = a->q0; L.q1 = a->q1; L.w = a->w; L.k0 = a->k0; L.k1 = a->k1;
+    L.out_idx = a->out_idx; L.out_score = a->out_score;
+    L.scores = a->out_score ? a->out_score : (float*)((char*)ws + p.off_scores);
+    L.hist = (uint32_t*)((char*)ws + p.off_hist);
+    L.state = (csa::TopkState*)((char*)ws + p.off_state);
+    L.counts = (int32_t*)((char*)ws + p.off_counts);
+    if (csa::launch_index_topk(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
+  }
+  return CSA_OK;
+}
+
+CSA_EXPORT int csa_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_attend(a, ws, ws_bytes, stream, false);
+}
+
+CSA_EXPORT int hca_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_attend(a, ws, ws_bytes, stream, true);
+}

@@ -1,0 +1,84 @@
+// Launch descriptors passed by value from the validated host API to the
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressLaunch {
+  int32_t B, d, d_rope, m, in_dtype, out_fmt, do_norm, n_entries;
+  float rms_eps;
+  double log_theta;
+  int64_t pos0, i_first, out_row0;
+  const void* kv_a;
+  const void* gate_a;
+  const void* kv_b;
+  const void* gate_b;
+  int64_t in_row_stride, in_seq_stride;
+  const float* bias_a;
+  const float* bias_b;
+  void* out0;
+  void* out1;
+  int64_t out0_stride, out0_seq_stride, out1_stride, out1_seq_stride;
+};
+
+// Per-query radix-select state kept in the workspace.
+struct TopkState {
+  uint32_t prefix;    // high bits of the k-th largest order key found so far
+  uint32_t mask;      // which bits of `prefix` are fixed
+  int32_t k_rem;      // how many elements still to take inside the prefix bucket
+  int32_t n_vis;      // visible entries of the query
+};
+
+struct IndexLaunch {
+  int32_t B, n_q, m, n_cap, H_I, d_I, fmt, top_k;
+  int32_t n_chunks;          // score chunks per query (radix passes)
+  int32_t q_first;           // first query of this query block
+  int32_t n_qb;              // queries in this block
+  const int64_t* q_pos;
+  const int32_t* n_entries;
+  const void* q0;
+  const void* q1;
+  const float* w;
+  const void* k0;
+  const void* k1;
+  int32_t* out_idx;
+  float* out_score;          // full [B][n_q][n_cap] output (optional)
+  // workspace views (per query of the block: q_local = b * n_qb + r)
+  float* scores;             // [B * n_qb][n_cap]
+  uint32_t* hist;            // [B * n_qb][2048]
+  TopkState* state;          // [B * n_qb]
+  int32_t* counts;           // [B * n_qb][n_chunks][2]
+};
+
+struct AttendLaunch {
+  int32_t B, n_q, H, d, d_rope, m, fmt, flags;
+  double log_theta;
+  float scale_log2;          // softmax_scale * log2(e)
+  int32_t top_k, n_cap, n_win, win_len;
+  int32_t n_splits, list_len, split_len;
+  const int64_t* q_pos;
+  const void* q;
+  const void* kv0;
+  const void* kv1;
+  int64_t kv_stride, kv_seq_stride;
+  const int32_t* n_entries;
+  const int32_t* idx;        // NULL: dense (HCA)
+  const void* win0;
+  const void* win1;
+  int64_t win_stride, win_seq_stride;
+  const int64_t* win_pos0;
+  const float* sink;
+  void* out;
+  float* out_lse;
+  float* part_o;             // [units][n_splits][64][d] partial numerators
+  float* part_ml;            // [units][n_splits][64][2]  (running max, sum)
+};
+
+hipError_t launch_compress(const CompressLaunch& a, hipStream_t s);
+hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
+hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
+
+}  // namespace csa

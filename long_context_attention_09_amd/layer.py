@@ -1,0 +1,169 @@
+"""One CSA or HCA layer step driven through the C ABI (decode and prefill).
+
+Sequencing only: every step is one library call; this module owns the output
+and workspace buffers so repeated steps allocate nothing.
+
+Decode step of a layer at query position t = L (all L tokens before t are in
+the caches):
+  CSA: compress the newest main-KV entry (m = 4, overlapped pooling of rows
+       [L-8, L)), the newest indexer key (same rows, MXFP4) and the new
+       token's raw window row (m = 1), then index + top-k, then attend.
+  HCA: compress the newest entry (m' = 128, rows [L-128, L)), store the new
+       window row, then dense attend.
+The newest entry of a real decode completes once every m steps; compressing
+it on every step is the pessimistic bound.
+
+Prefill chunk of n_q tokens at positions L .. L+n_q-1: compress every entry
+the chunk completes (with the m-token context tail feeding the b-branch), store
+the chunk's raw window rows, then index + top-k and attend per query.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as K
+
+
+class LayerStep:
+    """Buffers and calls of one layer step over device-resident inputs.
+
+    shape: a synth.Shape-like object (B, L, n_q, H, d, d_r, m, overlap, top_k,
+    H_I, d_I, n_win, theta); inp: dict of device tensors laid out as the
+    seeded generator lays them out (decode: quant_decode_inputs, prefill:
+    quant_prefill_inputs)."""
+
+    def __init__(self, shape, inp, prefill: bool = False, copies: int = 1):
+        self.s = shape
+        self.inp = inp
+        self.prefill = prefill
+        s = shape
+        dev = inp["q"].device
+        B = s.B
+        self.caches = []
+        self.keys = []
+        if prefill:
+            n_old = s.L // s.m
+            n_cap = (s.L + s.n_q) // s.m
+            cache = torch.zeros(B, n_cap, 576, dtype=torch.uint8, device=dev)
+            cache[:, :n_old] = inp["cache_old"]
+            self.caches.append(cache)
+            win = torch.zeros(B, s.n_win - 1 + s.n_q, 576, dtype=torch.uint8, device=dev)
+            win[:, :s.n_win - 1] = inp["win_old"]
+            self.win = win
+            self.win_pos0 = inp["win_pos0"]
+            if s.csa:
+                kc = torch.zeros(B, n_cap, 64, dtype=torch.uint8, device=dev)
+                ks = torch.zeros(B, n_cap, 4, dtype=torch.uint8, device=dev)
+                kc[:, :n_old] = inp["keys_codes_old"]
+                ks[:, :n_old] = inp["keys_scales_old"]
+                self.keys.append((kc, ks))
+        else:
+            for c in range(copies):
+                sfx = "" if c == 0 else f"_{c}"
+                self.caches.append(inp["cache" + sfx])
+                if s.csa:
+                    self.keys.append((inp["keys_codes" + sfx], inp["keys_scales" + sfx]))
+            self.win = inp["win"]
+            self.win_pos0 = inp["win_pos0"]
+        self.out = torch.empty(B, s.n_q, s.H, s.d, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(B, s.n_q, s.H, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(B, s.n_q, max(s.top_k, 1), dtype=torch.int32, device=dev)
+        self.ws_index = None
+        self.ws_attend = None
+        self._alloc_workspaces()
+
+    # ------------------------------------------------------------ pieces
+
+    def _main_streams(self):
+        mn = self.inp["main"]
+        return dict(kv_a=mn["ca"], gate_a=mn["za"], bias_a=mn["ba"],
+                    kv_b=mn.get("cb"), gate_b=mn.get("zb"), bias_b=mn.get("bb"))
+
+    def _rows_pos0(self):
+        s = self.s
+        if self.prefill:
+            return s.L - (s.m if s.overlap else 0)
+        return s.L - s.m * (2 if s.overlap else 1)
+
+    def compress_main(self, c=0):
+        s = self.s
+        cache = self.caches[c]
+        nope, rope = K.split_main(cache)
+        K.compress(**self._main_streams(), m=s.m, pos0=self._rows_pos0(), out0=nope, out1=rope,
+                   d_rope=s.d_r, rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16)
+
+    def compress_index(self, c=0):
+        s = self.s
+        ix = self.inp["idx"]
+        kc, ks = self.keys[c]
+        K.compress(ix["ca"], gate_a=ix["za"], bias_a=ix["ba"], kv_b=ix["cb"], gate_b=ix["zb"],
+                   bias_b=ix["bb"], m=s.m, pos0=self._rows_pos0(), out0=kc, out1=ks, d_rope=0,
+                   do_norm=False, out_fmt=K.FMT_MXFP4)
+
+    def store_window(self):
+        """Raw window rows (m = 1, no gate): RMSNorm, RoPE at the token's own
+        position, FP8/BF16 storage into the window buffer, whose row 0 holds
+        position L - n_win + 1."""
+        s = self.s
+        nope, rope = K.split_main(self.win)
+        K.compress(self.inp["win_raw"], m=1, pos0=s.L, out0=nope, out1=rope, d_rope=s.d_r,
+                   rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16,
+                   out_row0=s.L - s.n_win + 1)
+
+    def index(self, c=0):
+        s = self.s
+        kc, ks = self.keys[c]
+        a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
+                         top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
+                         fmt=K.FMT_MXFP4)
+        self._call_index(a)
+
+    def _call_index(self, a):
+        import ctypes as C
+        _, n = self.ws_index
+        K._check(K.load().csa_index_topk(C.byref(a), K._ptr(self.ws_index[0]), n, K._stream()),
+                 "csa_index_topk")
+
+    def attend(self, c=0):
+        s = self.s
+        import ctypes as C
+        nope, rope = K.split_main(self.caches[c])
+        wn, wr = K.split_main(self.win)
+        a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0,
+                          self.inp["sink"], self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
+                          idx=self.idx if s.csa else None, out_lse=self.lse, d_rope=s.d_r,
+                          rope_theta=s.theta, fmt=K.FMT_FP8_BF16)
+        ws, n = self.ws_attend
+        fn = K.load().csa_attend if s.csa else K.load().hca_attend
+        K._check(fn(C.byref(a), K._ptr(ws), n, K._stream()), "attend")
+
+    def _alloc_workspaces(self):
+        s = self.s
+        dev = self.out.device
+        if s.csa:
+            kc, ks = self.keys[0]
+            a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
+                             top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
+                             fmt=K.FMT_MXFP4)
+            n = K.workspace_bytes(K.OP_INDEX_TOPK, a)
+            self.ws_index = (torch.empty(max(n, 256), dtype=torch.uint8, device=dev), n)
+        nope, rope = K.split_main(self.caches[0])
+        wn, wr = K.split_main(self.win)
+        a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0, self.inp["sink"],
+                          self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
+                          idx=self.idx if s.csa else None, d_rope=s.d_r, rope_theta=s.theta,
+                          fmt=K.FMT_FP8_BF16)
+        n = K.workspace_bytes(K.OP_ATTEND if s.csa else K.OP_HCA_ATTEND, a)
+        self.ws_attend = (torch.empty(max(n, 256), dtype=torch.uint8, device=dev) if n else None, n)
+
+    # ------------------------------------------------------------ whole step
+
+    def run(self, c=0):
+        """One full step on the current stream (no synchronisation)."""
+        self.compress_main(c)
+        if self.s.csa:
+            self.compress_index(c)
+        self.store_window()
+        if self.s.csa:
+            self.index(c)
+        self.attend(c)
