@@ -1,0 +1,231 @@
+"""Decode throughput of one CSA + HCA layer pair at 1M context on one MI355X.
+
+Workload (synthetic, seeded, generated on the device):
+  CSA layer: Pro-shaped decode, 8 sequences at 2^20 tokens of context
+             (262144 compressed entries each, 128 heads, head dim 512, indexer
+             64 heads x 128 in MXFP4, top-k 1024, window 128, sink).
+  HCA layer: Flash-shaped decode, 32 sequences at 2^20 tokens (8192 entries
+             each, 64 heads, window 128, sink).
+One step = one full decode step of each layer (compress of the newest
+blocks, window store, index + top-k for CSA, attention).  Per-token cost of
+the pair is t_csa / 8 + t_hca / 32, so the reported value is
+1 / (t_csa / 8 + t_hca / 32) decode tokens per second per layer pair.
+
+Caches are kept in three copies that consecutive steps rotate through, so the
+256 MB Infinity Cache cannot serve a step from the previous step's reads (each
+layer of a real model has caches of its own).  All inputs are resident in HBM
+before the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s per layer at 1M ctx (CSA+HCA) and % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+COPIES = 3
+
+
+class HipEvents:
+    """HIP events through the runtime's C API, for the library's timing hook."""
+
+    def __init__(self):
+        self.h = C.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [C.c_void_p]
+
+    def create(self):
+        e = C.c_void_p()
+        if self.h.hipEventCreate(C.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        self.h.hipEventSynchronize(C.c_void_p(b))
+        ms = C.c_float()
+        if self.h.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def algorithmic_bytes(shape, kind):
+    """Bytes the method must move per launch (inputs it reads, outputs it writes).
+
+    index: every visible key (64 B E2M1 + 4 B E8M0) plus the query heads
+           (MXFP4) and head weights, per sequence.
+    attend: every KV row attended (576 B: 448 FP8 + 64 BF16), the BF16 query
+            and the BF16 output, per sequence.
+    """
+    B, L = shape.B, shape.L
+    n_vis = L // shape.m
+    if kind == "index":
+        return B * (n_vis * 68 + shape.H_I * 68 + shape.H_I * 4)
+    rows = (shape.top_k if shape.csa else n_vis) + shape.n_win
+    return B * (rows * 576 + 2 * shape.H * shape.d * 2)
+
+
+def cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, budget_s=15.0):
+    """The fp64 oracle on this host's cores, on a bounded sample of the same
+    workload: whole decode steps of single sequences (CSA and HCA alternately)
+    until about budget_s seconds of CPU work; scaled to the pair rate."""
+    from oracle import pipeline as P
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+
+    def host_inputs(inp, b):
+        out = {}
+        for k, v in inp.items():
+            if isinstance(v, dict):
+                out[k] = {kk: vv[b:b + 1].cpu() if vv.dim() == 3 else vv.cpu() for kk, vv in v.items()}
+            elif isinstance(v, list):
+                continue
+            elif k.endswith(("_1", "_2")):
+                continue
+            elif v.dim() >= 1 and v.shape[0] == inp["q"].shape[0] and k not in ("sink",):
+                out[k] = v[b:b + 1].cpu()
+            else:
+                out[k] = v.cpu()
+        return out
+
+    t_csa, n_csa, t_hca, n_hca = 0.0, 0, 0.0, 0
+    b = 0
+    start = time.time()
+    while time.time() - start < budget_s and b < min(csa_shape.B, hca_shape.B):
+        hc = host_inputs(csa_inp, b)
+        t0 = time.perf_counter()
+        P.decode_step(csa_shape.replace(B=1), hc, 0)
+        t_csa += time.perf_counter() - t0
+        n_csa += 1
+        hh = host_inputs(hca_inp, b)
+        t0 = time.perf_counter()
+        P.decode_step(hca_shape.replace(B=1), hh, 0)
+        t_hca += time.perf_counter() - t0
+        n_hca += 1
+        b += 1
+    per_tok = t_csa / n_csa + t_hca / n_hca
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_csa} CSA + {n_hca} HCA single-sequence decode steps of the same "
+                      f"workload (fp64 NumPy oracle), {t_csa + t_hca:.1f} s of CPU time; "
+                      f"rate = 1 / (t_csa_seq + t_hca_seq)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer's decode is "
+              "measured on one GPU's share; see the design notes for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from long_context_attention_09_amd import _lib as K
+    from long_context_attention_09_amd.layer import LayerStep
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    K.load()
+    dev = "cuda"
+    csa_shape, hca_shape = synth.PRO_CSA_DECODE, synth.FLASH_HCA_DECODE
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    csa_inp = synth.quant_decode_inputs(csa_shape, device=dev, copies=COPIES)
+    hca_inp = synth.quant_decode_inputs(hca_shape, device=dev, copies=COPIES)
+    csa = LayerStep(csa_shape, csa_inp, copies=COPIES)
+    hca = LayerStep(hca_shape, hca_inp, copies=COPIES)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream()
+    n = args.warmup + args.steps
+    marks = [[ev.create() for _ in range(8)] for _ in range(n)]
+
+    def step(k, m):
+        c = k % COPIES
+        # op-level marks on the same stream, kernel-level marks through the library hook
+        ev.h.hipEventRecord(C.c_void_p(m[0]), C.c_void_p(stream.cuda_stream))
+        csa.compress_main(c)
+        csa.compress_index(c)
+        csa.store_window()
+        csa.index(c, events=(m[2], m[3]))
+        csa.attend(c)
+        ev.h.hipEventRecord(C.c_void_p(m[1]), C.c_void_p(stream.cuda_stream))
+        hca.compress_main(c)
+        hca.store_window()
+        hca.attend(c, events=(m[5], m[6]))
+        ev.h.hipEventRecord(C.c_void_p(m[4]), C.c_void_p(stream.cuda_stream))
+
+    ev.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for k in range(args.warmup):
+        step(k, marks[k])
+    torch.cuda.synchronize()
+    print("[bench] timed", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(args.warmup, n):
+        step(k, marks[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    timed = marks[args.warmup:]
+    t_csa = sum(ev.elapsed_ms(m[0], m[1]) for m in timed) / args.steps
+    t_hca = sum(ev.elapsed_ms(m[1], m[4]) for m in timed) / args.steps
+    k_idx = sum(ev.elapsed_ms(m[2], m[3]) for m in timed) / args.steps
+    k_hca = sum(ev.elapsed_ms(m[5], m[6]) for m in timed) / args.steps
+    rate_csa = csa_shape.B / (t_csa * 1e-3)
+    rate_hca = hca_shape.B / (t_hca * 1e-3)
+    value = 1.0 / (1.0 / rate_csa + 1.0 / rate_hca)
+
+    b_idx = algorithmic_bytes(csa_shape, "index")
+    b_hca = algorithmic_bytes(hca_shape, "attend")
+    kernels = {
+        "index_mxfp4_kernel": {"ms": k_idx, "bytes": b_idx, "GB/s": b_idx / (k_idx * 1e-3) / 1e9},
+        "attend_fp8_kernel(hca)": {"ms": k_hca, "bytes": b_hca, "GB/s": b_hca / (k_hca * 1e-3) / 1e9},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom = kernels[dom_name]
+    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GB/s"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": None}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8/bf16 kv, mxfp4 indexer, bf16 mfma fp32 acc", "data": "synthetic",
+        "config": {
+            "workload": "CSA+HCA layer-pair decode at 1M context: Pro CSA (B=8, H=128, top-k 1024, "
+                        "262144 entries) + Flash HCA (B=32, H=64, 8192 entries), window 128, sink",
+            "csa": {"B": csa_shape.B, "ctx": csa_shape.L, "ms_per_step": round(t_csa, 4),
+                    "tokens_per_s": round(rate_csa, 1)},
+            "hca": {"B": hca_shape.B, "ctx": hca_shape.L, "ms_per_step": round(t_hca, 4),
+                    "tokens_per_s": round(rate_hca, 1)},
+            "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
+            "cache_copies_rotated": COPIES,
+        },
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

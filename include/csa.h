@@ -179,6 +179,9 @@ typedef struct CsaCompressArgs {
  * n_cap >= 1; m >= 1.
  * Workspace: csa_workspace_bytes(CSA_OP_INDEX_TOPK, &args) bytes of device
  * memory, 256-byte aligned, contents undefined on entry and exit.
+ * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
+ * records on `stream` around its scoring kernel (with several internal query
+ * blocks, before the first block's and after the last block's).
  */
 typedef struct CsaIndexArgs {
   int32_t B;
@@ -198,6 +201,8 @@ typedef struct CsaIndexArgs {
   const void* k1;
   int32_t* out_idx;
   float* out_score;
+  void* ev_start;   /* optional hipEvent_t recorded just before the scoring kernel */
+  void* ev_stop;    /* optional hipEvent_t recorded just after it (NULL = none) */
 } CsaIndexArgs;
 
 /*
@@ -234,6 +239,8 @@ typedef struct CsaIndexArgs {
  * Constraints: FP8_BF16 needs d == 512, d_rope == 64 and H % 16 == 0;
  * F32 needs d <= 512 and H <= 128.  1 <= n_win, win_len >= 0.
  * Workspace: csa_workspace_bytes(CSA_OP_ATTEND / CSA_OP_HCA_ATTEND, &args).
+ * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
+ * records on `stream` around its attention kernel.
  */
 typedef struct CsaAttendArgs {
   int32_t B;
@@ -267,6 +274,8 @@ typedef struct CsaAttendArgs {
   const float* sink;
   void* out;
   float* out_lse;
+  void* ev_start;   /* optional hipEvent_t recorded just before the attention kernel */
+  void* ev_stop;    /* optional hipEvent_t recorded just after it (NULL = none) */
 } CsaAttendArgs;
 
 /* ABI version of the loaded library (CSA_ABI_VERSION). */

@@ -42,7 +42,8 @@ class IndexArgs(C.Structure):
     _fields_ = [("B", C.c_int32), ("n_q", C.c_int32), ("m", C.c_int32), ("n_cap", C.c_int32),
                 ("H_I", C.c_int32), ("d_I", C.c_int32), ("fmt", C.c_int32), ("top_k", C.c_int32),
                 ("q_pos", _vp), ("n_entries", _vp), ("q0", _vp), ("q1", _vp), ("w", _vp),
-                ("k0", _vp), ("k1", _vp), ("out_idx", _vp), ("out_score", _vp)]
+                ("k0", _vp), ("k1", _vp), ("out_idx", _vp), ("out_score", _vp),
+                ("ev_start", _vp), ("ev_stop", _vp)]
 
 
 class AttendArgs(C.Structure):
@@ -54,7 +55,8 @@ class AttendArgs(C.Structure):
                 ("kv_stride", C.c_int64), ("kv_seq_stride", C.c_int64),
                 ("n_entries", _vp), ("idx", _vp), ("win0", _vp), ("win1", _vp),
                 ("win_stride", C.c_int64), ("win_seq_stride", C.c_int64),
-                ("win_pos0", _vp), ("sink", _vp), ("out", _vp), ("out_lse", _vp)]
+                ("win_pos0", _vp), ("sink", _vp), ("out", _vp), ("out_lse", _vp),
+                ("ev_start", _vp), ("ev_stop", _vp)]
 
 
 _lib = None

@@ -27,6 +27,8 @@
 // A split that covers the whole list finalises in place (sink, normalisation,
 // inverse RoPE, BF16 store); otherwise (running max, sum, numerator) partials
 // go to the workspace and combine_kernel merges them.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -504,13 +506,13 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendLaunch a) {
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   if (a.fmt == CSA_FMT_F32) {
     dim3 grid(a.B * a.n_q, a.H);
-    attend_f32_kernel<<<grid, 256, 0, s>>>(a);
+    hipExtLaunchKernelGGL(attend_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
     return hipGetLastError();
   }
   const int n_hg = (a.H + 63) / 64;
   dim3 grid(a.n_splits, n_hg, a.B * a.n_q);
   const size_t smem = kTile * kRowBytes + kTile * sizeof(int);
-  attend_fp8_kernel<<<grid, 256, smem, s>>>(a);
+  hipExtLaunchKernelGGL(attend_fp8_kernel, grid, dim3(256), (uint32_t)smem, s, a.ev_start, a.ev_stop, 0, a);
   if (a.n_splits > 1) combine_kernel<<<a.B * a.n_q * n_hg, 256, 0, s>>>(a, n_hg);
   return hipGetLastError();
 }

@@ -219,6 +219,7 @@ int run_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream, 
   L.n_entries = a->n_entries; L.idx = dense ? nullptr : a->idx;
   L.win0 = a->win0; L.win1 = a->win1; L.win_stride = a->win_stride; L.win_seq_stride = a->win_seq_stride;
   L.win_pos0 = a->win_pos0; L.sink = a->sink; L.out = a->out; L.out_lse = a->out_lse;
+  L.ev_start = (hipEvent_t)a->ev_start; L.ev_stop = (hipEvent_t)a->ev_stop;
   if (p.total > 0) {
     L.part_o = (float*)((char*)ws + p.off_o);
     L.part_ml = (float*)((char*)ws + p.off_ml);
@@ -314,6 +315,8 @@ CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, 
     L.hist = (uint32_t*)((char*)ws + p.off_hist);
     L.state = (csa::TopkState*)((char*)ws + p.off_state);
     L.counts = (int32_t*)((char*)ws + p.off_counts);
+    L.ev_start = q0 == 0 ? (hipEvent_t)a->ev_start : nullptr;
+    L.ev_stop = q0 + p.n_qb >= a->n_q ? (hipEvent_t)a->ev_stop : nullptr;
     if (csa::launch_index_topk(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
   }
   return CSA_OK;

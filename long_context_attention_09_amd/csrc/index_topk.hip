@@ -24,6 +24,8 @@
 // emit the selected indices in ascending order.  Elements equal to the k-th
 // key are taken lowest index first.  Histograms use integer atomics only, so
 // the result is deterministic.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -400,14 +402,14 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
     const int kchunks = (a.n_cap + kKeysPerWG - 1) / kKeysPerWG;
     if (a.n_qb >= 4) {
       dim3 grid(kchunks, (a.n_qb + 3) / 4, a.B);
-      index_mxfp4_kernel<4><<<grid, 256, 0, s>>>(a);
+      hipExtLaunchKernelGGL(index_mxfp4_kernel<4>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
     } else {
       dim3 grid(kchunks, a.n_qb, a.B);
-      index_mxfp4_kernel<1><<<grid, 256, 0, s>>>(a);
+      hipExtLaunchKernelGGL(index_mxfp4_kernel<1>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
     }
   } else {
     dim3 grid((a.n_cap + 255) / 256, a.n_qb, a.B);
-    index_f32_kernel<<<grid, 256, 0, s>>>(a);
+    hipExtLaunchKernelGGL(index_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
   }
   dim3 g2(a.n_chunks, nq);
   topk_select_kernel<<<nq, 256, 0, s>>>(a, 0);

@@ -51,6 +51,7 @@ struct IndexLaunch {
   uint32_t* hist;            // [B * n_qb][2048]
   TopkState* state;          // [B * n_qb]
   int32_t* counts;           // [B * n_qb][n_chunks][2]
+  hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
 struct AttendLaunch {
@@ -75,6 +76,7 @@ struct AttendLaunch {
   float* out_lse;
   float* part_o;             // [units][n_splits][64][d] partial numerators
   float* part_ml;            // [units][n_splits][64][2]  (running max, sum)
+  hipEvent_t ev_start, ev_stop;  // recorded around the attention kernel (may be null)
 };
 
 hipError_t launch_compress(const CompressLaunch& a, hipStream_t s);

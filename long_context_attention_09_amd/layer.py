@@ -19,6 +19,8 @@ the chunk's raw window rows, then index + top-k and attend per query.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
 from . import _lib as K
@@ -110,29 +112,28 @@ class LayerStep:
                    rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16,
                    out_row0=s.L - s.n_win + 1)
 
-    def index(self, c=0):
+    def index(self, c=0, events=(None, None)):
+        """csa_index_topk; `events` = optional HIP event handles recorded around
+        the scoring kernel."""
         s = self.s
         kc, ks = self.keys[c]
         a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
                          top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
                          fmt=K.FMT_MXFP4)
-        self._call_index(a)
+        a.ev_start, a.ev_stop = events
+        ws, n = self.ws_index
+        K._check(K.load().csa_index_topk(C.byref(a), K._ptr(ws), n, K._stream()), "csa_index_topk")
 
-    def _call_index(self, a):
-        import ctypes as C
-        _, n = self.ws_index
-        K._check(K.load().csa_index_topk(C.byref(a), K._ptr(self.ws_index[0]), n, K._stream()),
-                 "csa_index_topk")
-
-    def attend(self, c=0):
+    def attend(self, c=0, events=(None, None)):
+        """csa_attend / hca_attend; `events` as for index()."""
         s = self.s
-        import ctypes as C
         nope, rope = K.split_main(self.caches[c])
         wn, wr = K.split_main(self.win)
         a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0,
                           self.inp["sink"], self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
                           idx=self.idx if s.csa else None, out_lse=self.lse, d_rope=s.d_r,
                           rope_theta=s.theta, fmt=K.FMT_FP8_BF16)
+        a.ev_start, a.ev_stop = events
         ws, n = self.ws_attend
         fn = K.load().csa_attend if s.csa else K.load().hca_attend
         K._check(fn(C.byref(a), K._ptr(ws), n, K._stream()), "attend")

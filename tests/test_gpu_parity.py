@@ -145,7 +145,10 @@ def _decode_check(shape, inp, step, batches, K):
             # the planted entries must rank at the top
             if s.planted:
                 pl = np.asarray(inp["planted"][b].cpu())
-                assert np.isin(pl, gsel).mean() > 0.99
+                if len(pl) >= s.top_k:      # more planted entries than slots: all slots planted
+                    assert np.isin(gsel, pl).mean() > 0.99
+                else:                       # every planted entry is selected
+                    assert np.isin(pl, gsel).all()
         out = bf16_to_np(step.out[b, 0])
         err = np.abs(out - ref["out"]).max()
         lerr = np.abs(step.lse[b, 0].cpu().numpy() - ref["lse"]).max()
@@ -276,7 +279,9 @@ def test_fp8_codec_on_device():
     torch.cuda.synchronize()
     got = out[0, :, :448].cpu().numpy().reshape(-1)[:len(x)]
     want = F.encode_e4m3fn(x.astype(np.float32).astype(np.float64))
-    assert np.array_equal(got, want)
+    # pooling one candidate adds its value to +0, so -0 comes out as +0: compare values
+    assert np.array_equal(F.decode_e4m3fn(got), F.decode_e4m3fn(want))
+    assert np.array_equal(got[want != 0x80], want[want != 0x80])
 
 
 def test_attend_single_entry_decodes_codes():
