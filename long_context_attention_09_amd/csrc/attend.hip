@@ -99,10 +99,29 @@ __device__ __forceinline__ uint32_t pack_hi16(float f0, float f1) {
   return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
+typedef __attribute__((address_space(1))) const i32x4 gbl_i32x4;
+
+// Global address of list position p (nope part; the rope part is at +rope_delta
+// for AoS rows and is resolved separately), or 0 when the position is masked.
+__device__ __forceinline__ void row_addrs(const AttendLaunch& a, int b, int r, const ListInfo& L, int p,
+                                          int p1, uint64_t* an, uint64_t* ar) {
+  const uint8_t *pn, *pr;
+  if (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) {
+    *an = (uint64_t)pn;
+    *ar = (uint64_t)pr;
+  } else {
+    *an = 0;
+    *ar = 0;
+  }
+}
+
+constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the true max
+
 __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* tile = smem;                                   // [kTile][kRowBytes]
-  int* valid = (int*)(smem + kTile * kRowBytes);          // [kTile]
+  uint8_t* tile = smem;                                              // [kTile][kRowBytes]
+  uint64_t* rowa = (uint64_t*)(smem + kTile * kRowBytes);            // [2][2][kTile] addresses
+  float* rope_cs = (float*)(rowa + 2 * 2 * kTile);                   // [2][32] cos, sin at t
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -118,6 +137,23 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
   int p1 = p0 + a.split_len;
   p1 = p1 < list_len ? p1 : list_len;
 
+  // RoPE table at the query position (fp64 angle), one pair per thread
+  if (tid < kDR / 2) {
+    float cs, sn;
+    rope_cos_sin((double)L.t, tid, kDR, a.log_theta, &cs, &sn);
+    rope_cs[tid] = cs;
+    rope_cs[32 + tid] = sn;
+  }
+  // row addresses of the first two tiles
+  if (tid < 2 * kTile) {
+    const int t = tid >> 5, e = tid & 31;
+    uint64_t an, ar;
+    row_addrs(a, b, r, L, p0 + t * kTile + e, p1, &an, &ar);
+    rowa[(t * 2 + 0) * kTile + e] = an;
+    rowa[(t * 2 + 1) * kTile + e] = ar;
+  }
+  __syncthreads();
+
   // ---- query operand: head `head`, dims 32kb + 8g + j, RMSNorm, RoPE at t, BF16
   bf16x8 qv[16];
   {
@@ -127,7 +163,7 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     float ss = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 16; ++kb) {
-      const i32x4 v = *(const i32x4*)(qrow + 32 * kb + 8 * g);
+      const i32x4 v = *(gbl_i32x4*)(qrow + 32 * kb + 8 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[kb][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
@@ -147,8 +183,7 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const int u = (32 * kb + 8 * g + j - kDN) >> 1;
-        float cs, sn;
-        rope_cos_sin((double)L.t, u, kDR, a.log_theta, &cs, &sn);
+        const float cs = rope_cs[u], sn = rope_cs[32 + u];
         const float xe = x[kb][j], xo = x[kb][j + 1];
         x[kb][j] = xe * cs - xo * sn;
         x[kb][j + 1] = xe * sn + xo * cs;
@@ -163,34 +198,34 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
   f32x4 acc_o[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;     // log2 domain, per head (same value in the 4 lanes of a head)
+  float m_run = -INFINITY;     // log2-domain reference max of head `col` (lags the true max by < 8)
   float l_part = 0.f;          // this lane's share of the running denominator
 
-  // ---- tile loader: 36 chunks of 16 B per row
+  // ---- tile loader: thread t < 252 owns sixteen-byte part (t % 36) of rows t/36 + 7k
+  const bool loader = tid < 7 * kChunksPerRow;
+  const int part = tid % kChunksPerRow;
+  const int row0 = tid / kChunksPerRow;
+  const int src_off = part < 28 ? part * 16 : (part - 28) * 16;
+  const int dst_off = part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16;
   i32x4 stage[kLoadsPerThread];
-  auto fetch = [&](int tile0) {
+  auto fetch = [&](int buf) {
+    const uint64_t* ad = rowa + (buf * 2 + (part < 28 ? 0 : 1)) * kTile;
 #pragma unroll
     for (int k = 0; k < kLoadsPerThread; ++k) {
-      const int c = tid + 256 * k;
+      const int e = row0 + 7 * k;
       stage[k] = (i32x4){0, 0, 0, 0};
-      if (c < kChunksPerTile) {
-        const int e = c / kChunksPerRow, part = c % kChunksPerRow;
-        const int p = tile0 + e;
-        const uint8_t *pn, *pr;
-        if (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) {
-          const uint8_t* src = part < 28 ? pn + part * 16 : pr + (part - 28) * 16;
-          stage[k] = *(const i32x4*)src;
-        }
+      if (loader && e < kTile) {
+        const uint64_t base = ad[e];
+        if (base) stage[k] = *(gbl_i32x4*)(base + src_off);
       }
     }
   };
-  auto commit = [&](int tile0) {
+  auto commit = [&]() {
 #pragma unroll
     for (int k = 0; k < kLoadsPerThread; ++k) {
-      const int c = tid + 256 * k;
-      if (c < kChunksPerTile) {
-        const int e = c / kChunksPerRow, part = c % kChunksPerRow;
-        uint8_t* row = tile + e * kRowBytes;
+      const int e = row0 + 7 * k;
+      if (loader && e < kTile) {
+        uint8_t* dst = tile + e * kRowBytes + dst_off;
         if (part < 28) {
           i32x4 lo, hi;
 #pragma unroll
@@ -202,41 +237,41 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
             if (j < 2) { lo[2 * j] = (int)w0; lo[2 * j + 1] = (int)w1; }
             else { hi[2 * (j - 2)] = (int)w0; hi[2 * (j - 2) + 1] = (int)w1; }
           }
-          *(i32x4*)(row + part * 32) = lo;
-          *(i32x4*)(row + part * 32 + 16) = hi;
+          *(i32x4*)dst = lo;
+          *(i32x4*)(dst + 16) = hi;
         } else {
-          *(i32x4*)(row + kDN * 2 + (part - 28) * 16) = stage[k];
+          *(i32x4*)dst = stage[k];
         }
       }
     }
-    if (tid < kTile) {
-      const uint8_t *pn, *pr;
-      const int p = tile0 + tid;
-      valid[tid] = (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) ? 1 : 0;
-    }
   };
 
+  int buf = 0;
   if (p0 < p1) {
-    fetch(p0);
-    commit(p0);
+    fetch(0);
+    commit();
   }
   __syncthreads();
 
   for (int tile0 = p0; tile0 < p1; tile0 += kTile) {
     const bool more = tile0 + kTile < p1;
-    if (more) fetch(tile0 + kTile);
+    if (more) fetch(buf ^ 1);
+    const uint64_t* vrow = rowa + (buf * 2) * kTile;   // masked rows have address 0
 
-    // S^T = K Q^T : two 16-entry blocks
+    // S^T = K Q^T : two 16-entry blocks, each split over two accumulators
     f32x4 s[2];
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb) {
-      s[eb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + 16 * g;
 #pragma unroll
-      for (int kb = 0; kb < 16; ++kb) {
-        const bf16x8 kv = *(const bf16x8*)(krow + 64 * kb);
-        s[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv[kb], s[eb], 0, 0, 0);
+      for (int kb = 0; kb < 16; kb += 2) {
+        const bf16x8 k0 = *(const bf16x8*)(krow + 64 * kb);
+        const bf16x8 k1 = *(const bf16x8*)(krow + 64 * (kb + 1));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv[kb], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[kb + 1], s1, 0, 0, 0);
       }
+      s[eb] = s0 + s1;
     }
     // online softmax (log2 domain); lane holds entries eb*16 + 4g + i of head `col`
     float mx = -INFINITY;
@@ -244,15 +279,17 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = valid[eb * 16 + 4 * g + i] ? s[eb][i] * a.scale_log2 : -INFINITY;
+        const float v = vrow[eb * 16 + 4 * g + i] ? s[eb][i] * a.scale_log2 : -INFINITY;
         s[eb][i] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    // the reference max moves only when the tile max overtakes it by the slack,
+    // so the O rescale below is rare; probabilities stay below 2^slack
+    const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);    // 0 while nothing was seen, 1 if the max holds
+    const float alpha = exp2f(m_run - m_use);
     bf16x8 pv;
     float psum = 0.f;
 #pragma unroll
@@ -263,12 +300,13 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
         psum += p;
         pv[eb * 4 + i] = u16_as_bf16(f32_to_bf16(p));
       }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
     if (__any(alpha != 1.0f)) {
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < 32; ++db) acc_o[db] *= alpha;
     }
+    l_part += psum;
+    m_run = m_new;
     // O^T += V^T P^T ; lane (g, col) supplies row 4g + col/4 (+16) at dims 16db + 4(col%4)
     const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + 8 * (col & 3);
 #pragma unroll
@@ -285,7 +323,17 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
       acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[db], 0, 0, 0);
     }
     __syncthreads();
-    if (more) commit(tile0 + kTile);
+    if (more) {
+      commit();
+      // addresses of the tile after next go where this tile's were
+      if (tid < kTile) {
+        uint64_t an, ar;
+        row_addrs(a, b, r, L, tile0 + 2 * kTile + tid, p1, &an, &ar);
+        rowa[(buf * 2 + 0) * kTile + tid] = an;
+        rowa[(buf * 2 + 1) * kTile + tid] = ar;
+      }
+    }
+    buf ^= 1;
     __syncthreads();
   }
 
@@ -300,17 +348,17 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     const float den = l_run * exp2f(m_run - top) + exp2f(z2 - top);
     const float inv = exp2f(m_run - top) / den;      // 0 when no row was seen
     uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
+    const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = acc_o[db][i] * inv;
-      if (db >= 28 && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
+      if (db >= 28 && inv_rope) {
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
           const int u = (16 * db + 4 * g + i - kDN) >> 1;
-          float cs, sn;
-          rope_cos_sin(-(double)L.t, u, kDR, a.log_theta, &cs, &sn);
+          const float cs = rope_cs[u], sn = -rope_cs[32 + u];   // rotation by -t
           const float xe = o[i], xo = o[i + 1];
           o[i] = xe * cs - xo * sn;
           o[i + 1] = xe * sn + xo * cs;
@@ -335,64 +383,67 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
   }
 }
 
-// Merge the split partials of one (query, 64-head group): 4 threads per head,
-// 128 dims each.
+// Merge the split partials: workgroup (unit, head quad), 64 threads per head,
+// 8 dims each.
 __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) {
+  __shared__ float rope_cs[64];
   const int unit = blockIdx.x;                 // br * n_hg + hg
   const int br = unit / n_hg, hg = unit % n_hg;
   const int b = br / a.n_q, r = br % a.n_q;
-  const int hl = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int hl = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int d0 = (threadIdx.x & 63) * 8;
   const int head = hg * 64 + hl;
-  if (head >= a.H) return;
   const int64_t t = a.q_pos[(int64_t)b * a.n_q + r];
+  if (threadIdx.x < 32) {
+    float cs, sn;
+    rope_cos_sin(-(double)t, threadIdx.x, kDR, a.log_theta, &cs, &sn);
+    rope_cs[threadIdx.x] = cs;
+    rope_cs[32 + threadIdx.x] = sn;
+  }
+  __syncthreads();
+  if (head >= a.H) return;
   const int64_t base = (int64_t)unit * a.n_splits * 64 + hl;
-  float top = a.sink[head] * kLog2e;
-  for (int s = 0; s < a.n_splits; ++s) top = fmaxf(top, a.part_ml[(base + s * 64) * 2]);
-  float den = exp2f(a.sink[head] * kLog2e - top);
-  float lsum = 0.f;
-  float o[128];
-#pragma unroll
-  for (int i = 0; i < 128; ++i) o[i] = 0.f;
-  float mmax = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) mmax = fmaxf(mmax, a.part_ml[(base + s * 64) * 2]);
+  const float z2 = a.sink[head] * kLog2e;
+  float top = z2, mmax = -INFINITY;
   for (int s = 0; s < a.n_splits; ++s) {
     const float ms = a.part_ml[(base + s * 64) * 2];
-    const float ls = a.part_ml[(base + s * 64) * 2 + 1];
+    top = fmaxf(top, ms);
+    mmax = fmaxf(mmax, ms);
+  }
+  float den = exp2f(z2 - top), lsum = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float ms = a.part_ml[(base + s * 64) * 2];
     if (ms == -INFINITY) continue;
+    const float ls = a.part_ml[(base + s * 64) * 2 + 1];
     const float wgt = exp2f(ms - top);
     den += ls * wgt;
     lsum += ls * exp2f(ms - mmax);
-    const float* po = a.part_o + (base + s * 64) * kD + part * 128;
+    const float* po = a.part_o + (base + s * 64) * kD + d0;
+    const f32x4 v0 = *(const f32x4*)po, v1 = *(const f32x4*)(po + 4);
 #pragma unroll
-    for (int i = 0; i < 128; i += 4) {
-      const f32x4 v = *(const f32x4*)(po + i);
-      o[i] += v[0] * wgt; o[i + 1] += v[1] * wgt; o[i + 2] += v[2] * wgt; o[i + 3] += v[3] * wgt;
-    }
+    for (int i = 0; i < 4; ++i) { o[i] += v0[i] * wgt; o[4 + i] += v1[i] * wgt; }
   }
   const float inv = 1.0f / den;
 #pragma unroll
-  for (int i = 0; i < 128; ++i) o[i] *= inv;
-  if (part == 3 && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
-    // dims 448 .. 511 are o[64 .. 127]
+  for (int i = 0; i < 8; ++i) o[i] *= inv;
+  if (d0 >= kDN && !(a.flags & CSA_ATTEND_NO_INV_ROPE)) {
 #pragma unroll
-    for (int i = 64; i < 128; i += 2) {
-      float cs, sn;
-      rope_cos_sin(-(double)t, (i - 64) >> 1, kDR, a.log_theta, &cs, &sn);
+    for (int i = 0; i < 8; i += 2) {
+      const int u = (d0 + i - kDN) >> 1;
+      const float cs = rope_cs[u], sn = rope_cs[32 + u];
       const float xe = o[i], xo = o[i + 1];
       o[i] = xe * cs - xo * sn;
       o[i + 1] = xe * sn + xo * cs;
     }
   }
-  uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD + part * 128;
+  uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD + d0;
+  i32x4 w;
 #pragma unroll
-  for (int i = 0; i < 128; i += 8) {
-    i32x4 w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (int)((uint32_t)f32_to_bf16(o[i + 2 * j]) | ((uint32_t)f32_to_bf16(o[i + 2 * j + 1]) << 16));
-    *(i32x4*)(orow + i) = w;
-  }
-  if (a.out_lse && part == 0)
+  for (int j = 0; j < 4; ++j)
+    w[j] = (int)((uint32_t)f32_to_bf16(o[2 * j]) | ((uint32_t)f32_to_bf16(o[2 * j + 1]) << 16));
+  *(i32x4*)orow = w;
+  if (a.out_lse && (threadIdx.x & 63) == 0)
     a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
         lsum > 0.f ? (mmax + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
 }
@@ -511,9 +562,9 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   }
   const int n_hg = (a.H + 63) / 64;
   dim3 grid(a.n_splits, n_hg, a.B * a.n_q);
-  const size_t smem = kTile * kRowBytes + kTile * sizeof(int);
+  const size_t smem = kTile * kRowBytes + 2 * 2 * kTile * sizeof(uint64_t) + 64 * sizeof(float);
   hipExtLaunchKernelGGL(attend_fp8_kernel, grid, dim3(256), (uint32_t)smem, s, a.ev_start, a.ev_stop, 0, a);
-  if (a.n_splits > 1) combine_kernel<<<a.B * a.n_q * n_hg, 256, 0, s>>>(a, n_hg);
+  if (a.n_splits > 1) combine_kernel<<<dim3(a.B * a.n_q * n_hg, 16), 256, 0, s>>>(a, n_hg);
   return hipGetLastError();
 }
 

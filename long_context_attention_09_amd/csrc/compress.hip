@@ -29,56 +29,97 @@ __device__ __forceinline__ void load_row(const T* row, int c0, int d, float* v) 
   for (int k = 0; k < CPT; ++k) v[k] = (c0 + k < d) ? load_elem<T>(row + c0 + k) : 0.0f;
 }
 
-template <typename T, int CPT>
+// WIDE: one workgroup per entry, its four wavefronts fold interleaved
+// candidates and merge their running (max, sum, weighted sum) through LDS
+// (the 128-token HCA blocks); otherwise one wavefront per entry.
+template <typename T, int CPT, bool WIDE>
 __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
   const int lane = threadIdx.x & 63;
-  const int entry_local = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
   const int b = blockIdx.y;
   if (entry_local >= a.n_entries) return;
   const int64_t i = a.i_first + entry_local;           // absolute entry index
   const int c0 = lane * CPT;
   const int d = a.d;
+  const int m = a.m;
   const char* base_ka = (const char*)a.kv_a + (int64_t)b * a.in_seq_stride;
   const char* base_ga = a.gate_a ? (const char*)a.gate_a + (int64_t)b * a.in_seq_stride : nullptr;
   const char* base_kb = a.kv_b ? (const char*)a.kv_b + (int64_t)b * a.in_seq_stride : nullptr;
   const char* base_gb = a.gate_b ? (const char*)a.gate_b + (int64_t)b * a.in_seq_stride : nullptr;
+  // candidates: c < m is token m*i + c of the a-branch (bias row c); m <= c < 2m
+  // is token m*(i-1) + c - m of the b-branch (bias row c - m); entry 0 has no b-branch
+  const int n_cand = (base_kb && i >= 1) ? 2 * m : m;
 
   float mx[CPT], sm[CPT], acc[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) { mx[k] = -INFINITY; sm[k] = 0.f; acc[k] = 0.f; }
 
-  auto fold = [&](const char* kb, const char* gb, const float* bias, int64_t row) {
-    float v[CPT], z[CPT];
-    load_row<T, CPT>((const T*)(kb + row * a.in_row_stride), c0, d, v);
-    if (gb) load_row<T, CPT>((const T*)(gb + row * a.in_row_stride), c0, d, z);
-    else {
+  const int c_first = WIDE ? wave : 0;
+  const int c_step = WIDE ? 4 : 1;
+  constexpr int kBatch = 4;
+  for (int cb = c_first; cb < n_cand; cb += kBatch * c_step) {
+    float v[kBatch][CPT], z[kBatch][CPT], bias[kBatch][CPT];
+    bool live[kBatch];
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) z[k] = 0.f;
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = cb + u * c_step;
+      live[u] = c < n_cand;
+      const bool a_side = c < m;
+      const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
+      const char* kbase = a_side ? base_ka : base_kb;
+      const char* gbase = a_side ? base_ga : base_gb;
+      const float* bb = a_side ? a.bias_a : a.bias_b;
+      const int brow = a_side ? c : c - m;
+      if (live[u]) {
+        load_row<T, CPT>((const T*)(kbase + row * a.in_row_stride), c0, d, v[u]);
+        if (gbase) load_row<T, CPT>((const T*)(gbase + row * a.in_row_stride), c0, d, z[u]);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          if (!gbase) z[u][k] = 0.f;
+          bias[u][k] = (bb && c0 + k < d) ? bb[(int64_t)brow * d + c0 + k] : 0.f;
+        }
+      }
     }
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const float lg = z[k] + (bias && c0 + k < d ? bias[c0 + k] : 0.f);
-      const float nm = fmaxf(mx[k], lg);
-      const float r = expf(mx[k] - nm);       // 0 on the first candidate (mx = -inf)
-      const float e = expf(lg - nm);
-      sm[k] = sm[k] * r + e;
-      acc[k] = acc[k] * r + e * v[k];
-      mx[k] = nm;
+    for (int u = 0; u < kBatch; ++u) {
+      if (!live[u]) continue;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float lg = z[u][k] + bias[u][k];
+        const float nm = fmaxf(mx[k], lg);
+        const float r = expf(mx[k] - nm);       // 0 on the first candidate (mx = -inf)
+        const float e = expf(lg - nm);
+        sm[k] = sm[k] * r + e;
+        acc[k] = acc[k] * r + e * v[u][k];
+        mx[k] = nm;
+      }
     }
-  };
-
-  const int m = a.m;
-  // a-branch: tokens m*i .. m*i+m-1, bias row = offset in the block
-  for (int r = 0; r < m; ++r) {
-    const int64_t row = m * i + r - a.pos0;
-    fold(base_ka, base_ga, a.bias_a ? a.bias_a + (int64_t)r * d : nullptr, row);
   }
-  // b-branch: tokens m*(i-1) .. m*i-1 (entry 0 has none)
-  if (base_kb && i >= 1) {
-    for (int r = 0; r < m; ++r) {
-      const int64_t row = m * (i - 1) + r - a.pos0;
-      fold(base_kb, base_gb, a.bias_b ? a.bias_b + (int64_t)r * d : nullptr, row);
+  if constexpr (WIDE) {
+    __shared__ float red[3][3][64 * CPT];          // waves 1..3: max, sum, weighted sum
+    if (wave > 0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        red[wave - 1][0][c0 + k] = mx[k];
+        red[wave - 1][1][c0 + k] = sm[k];
+        red[wave - 1][2][c0 + k] = acc[k];
+      }
     }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const float om = red[w][0][c0 + k];
+        const float nm = fmaxf(mx[k], om);
+        if (nm == -INFINITY) continue;
+        const float r0 = expf(mx[k] - nm), r1 = expf(om - nm);
+        sm[k] = sm[k] * r0 + red[w][1][c0 + k] * r1;
+        acc[k] = acc[k] * r0 + red[w][2][c0 + k] * r1;
+        mx[k] = nm;
+      }
   }
   float x[CPT];
 #pragma unroll
@@ -155,17 +196,24 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
   }
 }
 
+template <typename T, int CPT>
+static void launch_cpt(const CompressLaunch& a, hipStream_t s) {
+  if (a.m >= 16) {
+    compress_kernel<T, CPT, true><<<dim3(a.n_entries, a.B), 256, 0, s>>>(a);
+  } else {
+    compress_kernel<T, CPT, false><<<dim3((a.n_entries + 3) / 4, a.B), 256, 0, s>>>(a);
+  }
+}
+
 template <typename T>
 static hipError_t launch_t(const CompressLaunch& a, hipStream_t s) {
   int cpt = (a.d + 63) / 64;
   if (a.out_fmt == CSA_FMT_MXFP4 && cpt < 2) cpt = 2;  // a lane packs whole bytes
-  dim3 grid((a.n_entries + 3) / 4, a.B);
-  dim3 block(256);
-  if (cpt <= 1) compress_kernel<T, 1><<<grid, block, 0, s>>>(a);
-  else if (cpt <= 2) compress_kernel<T, 2><<<grid, block, 0, s>>>(a);
-  else if (cpt <= 4) compress_kernel<T, 4><<<grid, block, 0, s>>>(a);
-  else if (cpt <= 8) compress_kernel<T, 8><<<grid, block, 0, s>>>(a);
-  else compress_kernel<T, 16><<<grid, block, 0, s>>>(a);
+  if (cpt <= 1) launch_cpt<T, 1>(a, s);
+  else if (cpt <= 2) launch_cpt<T, 2>(a, s);
+  else if (cpt <= 4) launch_cpt<T, 4>(a, s);
+  else if (cpt <= 8) launch_cpt<T, 8>(a, s);
+  else launch_cpt<T, 16>(a, s);
   return hipGetLastError();
 }
 

@@ -101,18 +101,28 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         }
       }
     }
+    // issue every tile's loads first (16 B of codes + the scale word per lane and
+    // tile), so a wave keeps 4 KiB of keys in flight, then score them
+    i32x4 kbuf[kTilesPerWave];
+    uint32_t kscw[kTilesPerWave];
+#pragma unroll
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int64_t key = key_base + t * 16 + col;
+      kbuf[t] = (i32x4){0, 0, 0, 0};
+      kscw[t] = 0x7f7f7f7fu;
+      if (key < nvis_max && key < a.n_cap) {
+        kbuf[t] = *(const i32x4*)(kc + key * 64 + g * 16);
+        kscw[t] = ks[key];
+      }
+    }
+#pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
       const int64_t key0 = key_base + t * 16;
       if (key0 >= nvis_max) break;
       const int64_t key = key0 + col;
       const bool in_cap = key < a.n_cap;
-      i32x8 kb = {0, 0, 0, 0, 0, 0, 0, 0};
-      int ksc = 127;
-      if (in_cap) {
-        const i32x4 v = *(const i32x4*)(kc + key * 64 + g * 16);
-        kb[0] = v[0]; kb[1] = v[1]; kb[2] = v[2]; kb[3] = v[3];
-        ksc = (int)((ks[key] >> (8 * g)) & 0xffu);
-      }
+      const i32x8 kb = {kbuf[t][0], kbuf[t][1], kbuf[t][2], kbuf[t][3], 0, 0, 0, 0};
+      const int ksc = (int)((kscw[t] >> (8 * g)) & 0xffu);
 #pragma unroll
       for (int qi = 0; qi < QT; ++qi) {
         float part = 0.f;
