@@ -160,15 +160,9 @@ def main():
         c = k % COPIES
         # op-level marks on the same stream, kernel-level marks through the library hook
         ev.h.hipEventRecord(C.c_void_p(m[0]), C.c_void_p(stream.cuda_stream))
-        csa.compress_main(c)
-        csa.compress_index(c)
-        csa.store_window()
-        csa.index(c, events=(m[2], m[3]))
-        csa.attend(c)
+        csa.run(c, events={"index": (m[2], m[3])})
         ev.h.hipEventRecord(C.c_void_p(m[1]), C.c_void_p(stream.cuda_stream))
-        hca.compress_main(c)
-        hca.store_window()
-        hca.attend(c, events=(m[5], m[6]))
+        hca.run(c, events={"attend": (m[5], m[6])})
         ev.h.hipEventRecord(C.c_void_p(m[4]), C.c_void_p(stream.cuda_stream))
 
     ev.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]

@@ -174,11 +174,14 @@ typedef struct CsaCompressArgs {
  *   out_idx    device int32 [B][n_q][top_k].
  *   out_score  optional device fp32 [B][n_q][n_cap]: I_i for i < n_vis,
  *              -inf beyond.
- * Constraints: d_I % 32 == 0 and d_I <= 256 for MXFP4 (d_I == 128 and
- * H_I % 16 == 0 take the matrix-core path); 1 <= top_k <= 4096;
- * n_cap >= 1; m >= 1.
+ * Constraints: MXFP4 needs d_I == 128 and H_I a multiple of 16 up to 64
+ * (the matrix-core path); F32 needs d_I <= 1024; top_k >= 1; n_cap >= 1;
+ * m >= 1.
  * Workspace: csa_workspace_bytes(CSA_OP_INDEX_TOPK, &args) bytes of device
- * memory, 256-byte aligned, contents undefined on entry and exit.
+ * memory, 256-byte aligned, used by this op only.  It must be zero-filled
+ * before its first use; every call leaves its counters and histogram zeroed
+ * again, so later calls need no refill (refill after a failed launch).
+ * Constraint: n_cap <= 4194304.
  * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
  * records on `stream` around its scoring kernel (with several internal query
  * blocks, before the first block's and after the last block's).
@@ -293,6 +296,14 @@ size_t csa_args_size(int op);
 size_t csa_workspace_bytes(int op, const void* args);
 
 int csa_compress(const CsaCompressArgs* args, void* stream);
+
+/* n_jobs independent csa_compress calls in as few launches as possible (one
+ * launch per run of up to four jobs that share in_dtype): e.g. the newest
+ * main-KV entry, the newest indexer key and the new raw window row of one
+ * decode step.  Every job is validated before anything is launched; the
+ * status is that of the first invalid job, else of the launches.  Jobs must
+ * not write to overlapping outputs. */
+int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void* stream);
 int csa_index_topk(const CsaIndexArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 int csa_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 int hca_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);

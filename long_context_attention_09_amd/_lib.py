@@ -78,10 +78,11 @@ def load(path: str = LIB_PATH):
     lib.csa_workspace_bytes.restype = C.c_size_t
     lib.csa_workspace_bytes.argtypes = [C.c_int, _vp]
     lib.csa_compress.argtypes = [C.POINTER(CompressArgs), _vp]
+    lib.csa_compress_batch.argtypes = [C.POINTER(CompressArgs), C.c_int, _vp]
     lib.csa_index_topk.argtypes = [C.POINTER(IndexArgs), _vp, C.c_size_t, _vp]
     lib.csa_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
     lib.hca_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
-    for fn in ("csa_compress", "csa_index_topk", "csa_attend", "hca_attend"):
+    for fn in ("csa_compress", "csa_compress_batch", "csa_index_topk", "csa_attend", "hca_attend"):
         getattr(lib, fn).restype = C.c_int
     if lib.csa_abi_version() != ABI_VERSION:
         raise RuntimeError("libcsa.so ABI version mismatch")
@@ -133,21 +134,21 @@ def _workspace(op, args, ws):
     if need == 0:
         return None, 0
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        # zero-filled once: the ops keep their counters zeroed from call to call
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     return ws, ws.numel()
 
 
 # ---------------------------------------------------------------- compress
 
 
-def compress(kv_a, *, m, pos0, out0, out1=None, gate_a=None, bias_a=None, kv_b=None, gate_b=None,
-             bias_b=None, d_rope=0, rope_theta=160000.0, do_norm=True, rms_eps=1e-6,
-             out_fmt=FMT_FP8_BF16, out_row0=0):
-    """csa_compress over inputs [B, n_rows, d] (fp32 or bf16, last dim contiguous).
+def compress_args(kv_a, *, m, pos0, out0, out1=None, gate_a=None, bias_a=None, kv_b=None,
+                  gate_b=None, bias_b=None, d_rope=0, rope_theta=160000.0, do_norm=True,
+                  rms_eps=1e-6, out_fmt=FMT_FP8_BF16, out_row0=0):
+    """CompressArgs over inputs [B, n_rows, d] (fp32 or bf16, last dim contiguous).
 
-    out0/out1 are [B, n_cap, ...] tensors whose entry i receives pooled entry i
-    (see include/csa.h for the formats), written at row i - out_row0."""
-    lib = load()
+    out0/out1 are [B, n_cap, ...] tensors whose row i - out_row0 receives pooled
+    entry i (see include/csa.h for the formats)."""
     _on_gpu(kv_a, gate_a, kv_b, gate_b, bias_a, bias_b, out0, out1)
     if kv_a.dim() != 3 or kv_a.stride(2) != 1:
         raise ValueError("kv_a must be [B, n_rows, d] with a contiguous last dim")
@@ -159,16 +160,28 @@ def compress(kv_a, *, m, pos0, out0, out1=None, gate_a=None, bias_a=None, kv_b=N
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise ValueError("biases are contiguous fp32 [m, d]")
     B, n_rows, d = kv_a.shape
-    a = CompressArgs(B=B, n_rows=n_rows, pos0=pos0, m=m, overlap=1 if kv_b is not None else 0, d=d,
-                     d_rope=d_rope, in_dtype=dt, out_fmt=out_fmt, do_norm=1 if do_norm else 0,
-                     rms_eps=rms_eps, rope_theta=rope_theta,
-                     kv_a=_ptr(kv_a), gate_a=_ptr(gate_a), kv_b=_ptr(kv_b), gate_b=_ptr(gate_b),
-                     in_row_stride=_bytes_stride(kv_a, 1), in_seq_stride=_bytes_stride(kv_a, 0),
-                     bias_a=_ptr(bias_a), bias_b=_ptr(bias_b), out0=_ptr(out0), out1=_ptr(out1),
-                     out_row0=out_row0, out0_stride=_bytes_stride(out0, 1), out0_seq_stride=_bytes_stride(out0, 0),
-                     out1_stride=_bytes_stride(out1, 1) if out1 is not None else 0,
-                     out1_seq_stride=_bytes_stride(out1, 0) if out1 is not None else 0)
-    _check(lib.csa_compress(C.byref(a), _stream()), "csa_compress")
+    return CompressArgs(B=B, n_rows=n_rows, pos0=pos0, m=m, overlap=1 if kv_b is not None else 0, d=d,
+                        d_rope=d_rope, in_dtype=dt, out_fmt=out_fmt, do_norm=1 if do_norm else 0,
+                        rms_eps=rms_eps, rope_theta=rope_theta,
+                        kv_a=_ptr(kv_a), gate_a=_ptr(gate_a), kv_b=_ptr(kv_b), gate_b=_ptr(gate_b),
+                        in_row_stride=_bytes_stride(kv_a, 1), in_seq_stride=_bytes_stride(kv_a, 0),
+                        bias_a=_ptr(bias_a), bias_b=_ptr(bias_b), out0=_ptr(out0), out1=_ptr(out1),
+                        out_row0=out_row0, out0_stride=_bytes_stride(out0, 1),
+                        out0_seq_stride=_bytes_stride(out0, 0),
+                        out1_stride=_bytes_stride(out1, 1) if out1 is not None else 0,
+                        out1_seq_stride=_bytes_stride(out1, 0) if out1 is not None else 0)
+
+
+def compress(kv_a, **kw):
+    """csa_compress (arguments as compress_args)."""
+    a = compress_args(kv_a, **kw)
+    _check(load().csa_compress(C.byref(a), _stream()), "csa_compress")
+
+
+def compress_batch(jobs):
+    """csa_compress_batch over a list of CompressArgs."""
+    arr = (CompressArgs * len(jobs))(*jobs)
+    _check(load().csa_compress_batch(arr, len(jobs), _stream()), "csa_compress_batch")
 
 
 # ---------------------------------------------------------------- index + top-k

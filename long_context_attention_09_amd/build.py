@@ -21,6 +21,10 @@ LIB = os.path.join(PKG, "libcsa.so")
 
 SOURCES = ["csa_api.hip", "compress.hip", "index_topk.hip", "attend.hip"]
 
+# Per-source extra flags: the indexer keeps its small MFMA accumulators in
+# ordinary VGPRs (no AGPR round trips before the ReLU / head-weight epilogue).
+EXTRA_FLAGS = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -37,7 +41,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

@@ -23,22 +23,67 @@ __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-template <typename T, int CPT>
+// CPT consecutive channels of one row starting at channel c0 (0 beyond d).
+// VEC: the row and every lane's slice are aligned to the slice size, so the
+// slice is fetched with the widest loads (16 B per instruction).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// CPT consecutive channels of one row starting at channel c0 (0 beyond d).
+// VEC: the row and every lane's slice are aligned to the slice size, so the
+// slice is fetched with the widest loads (16 B per instruction).
+// CPT consecutive channels of one row starting at channel c0 (0 beyond d).
+// VEC: the row and every lane's slice are aligned to the slice size and d is
+// a multiple of CPT (d % 8 == 0, CPT <= 8), so a lane's slice is either wholly
+// inside the row or wholly past it; it is fetched with the widest loads and no
+// branch (a lane past the row re-reads channel 0 and zeroes it).
+template <typename T, int CPT, bool VEC>
 __device__ __forceinline__ void load_row(const T* row, int c0, int d, float* v) {
+  constexpr int kBytes = CPT * (int)sizeof(T);
+  if constexpr (VEC && kBytes >= 4 && CPT <= 8) {
+    const bool in = c0 < d;
+    constexpr int kWords = kBytes / 4;
+    uint32_t w[kWords];
+    const char* src = (const char*)(row + (in ? c0 : 0));
+    if constexpr (kWords % 4 == 0) {
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) v[k] = (c0 + k < d) ? load_elem<T>(row + c0 + k) : 0.0f;
+      for (int k = 0; k < kWords; k += 4) {
+        const u32x4 x = *(const u32x4*)(src + 4 * k);
+        w[k] = x[0]; w[k + 1] = x[1]; w[k + 2] = x[2]; w[k + 3] = x[3];
+      }
+    } else if constexpr (kWords == 2) {
+      const u32x2 x = *(const u32x2*)src;
+      w[0] = x[0]; w[1] = x[1];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kWords; ++k) w[k] = ((const uint32_t*)src)[k];
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      float x;
+      if constexpr (sizeof(T) == 2) x = bf16_to_f32((uint16_t)((w[k >> 1] >> (16 * (k & 1))) & 0xffffu));
+      else x = __uint_as_float(w[k]);
+      v[k] = in ? x : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) v[k] = (c0 + k < d) ? load_elem<T>(row + c0 + k) : 0.0f;
+  }
 }
 
-// WIDE: one workgroup per entry, its four wavefronts fold interleaved
-// candidates and merge their running (max, sum, weighted sum) through LDS
-// (the 128-token HCA blocks); otherwise one wavefront per entry.
-template <typename T, int CPT, bool WIDE>
-__global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
+// WIDE: one 512-thread workgroup per entry, its eight wavefronts fold
+// interleaved candidates and merge their running (max, sum, weighted sum)
+// through LDS (the 128-token HCA blocks); otherwise one wavefront per entry.
+// blockIdx.z selects one of up to kMaxJobs independent jobs of one launch.
+template <typename T, int CPT, bool WIDE, bool VEC>
+__global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatch batch) {
+  const CompressLaunch& a = batch.job[blockIdx.z];
+  constexpr int kWaves = WIDE ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
   const int b = blockIdx.y;
-  if (entry_local >= a.n_entries) return;
+  if (b >= a.B || entry_local >= a.n_entries) return;
   const int64_t i = a.i_first + entry_local;           // absolute entry index
   const int c0 = lane * CPT;
   const int d = a.d;
@@ -56,40 +101,46 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
   for (int k = 0; k < CPT; ++k) { mx[k] = -INFINITY; sm[k] = 0.f; acc[k] = 0.f; }
 
   const int c_first = WIDE ? wave : 0;
-  const int c_step = WIDE ? 4 : 1;
-  constexpr int kBatch = 4;
+  const int c_step = WIDE ? kWaves : 1;
+  constexpr int kBatch = CPT >= 16 ? 4 : 8;   // candidates whose loads are in flight together
+  // Branch-free batches: a dead slot re-reads candidate 0 and gets logit -inf.
   for (int cb = c_first; cb < n_cand; cb += kBatch * c_step) {
     float v[kBatch][CPT], z[kBatch][CPT], bias[kBatch][CPT];
     bool live[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int c = cb + u * c_step;
+      int c = cb + u * c_step;
       live[u] = c < n_cand;
+      c = live[u] ? c : 0;
       const bool a_side = c < m;
       const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
       const char* kbase = a_side ? base_ka : base_kb;
       const char* gbase = a_side ? base_ga : base_gb;
       const float* bb = a_side ? a.bias_a : a.bias_b;
       const int brow = a_side ? c : c - m;
-      if (live[u]) {
-        load_row<T, CPT>((const T*)(kbase + row * a.in_row_stride), c0, d, v[u]);
-        if (gbase) load_row<T, CPT>((const T*)(gbase + row * a.in_row_stride), c0, d, z[u]);
+      load_row<T, CPT, VEC>((const T*)(kbase + row * a.in_row_stride), c0, d, v[u]);
+      if (gbase) {
+        load_row<T, CPT, VEC>((const T*)(gbase + row * a.in_row_stride), c0, d, z[u]);
+      } else {
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-          if (!gbase) z[u][k] = 0.f;
-          bias[u][k] = (bb && c0 + k < d) ? bb[(int64_t)brow * d + c0 + k] : 0.f;
-        }
+        for (int k = 0; k < CPT; ++k) z[u][k] = 0.f;
+      }
+      if (bb) {
+        load_row<float, CPT, VEC>(bb + (int64_t)brow * d, c0, d, bias[u]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) bias[u][k] = 0.f;
       }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (!live[u]) continue;
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
-        const float lg = z[u][k] + bias[u][k];
+        // softmax taken in base 2; a dead slot contributes exp2(-inf) = 0
+        const float lg = live[u] ? (z[u][k] + bias[u][k]) * kLog2e : -INFINITY;
         const float nm = fmaxf(mx[k], lg);
-        const float r = expf(mx[k] - nm);       // 0 on the first candidate (mx = -inf)
-        const float e = expf(lg - nm);
+        const float r = nm == -INFINITY ? 1.0f : exp2f(mx[k] - nm);   // 0 on the first live slot
+        const float e = lg == -INFINITY ? 0.0f : exp2f(lg - nm);
         sm[k] = sm[k] * r + e;
         acc[k] = acc[k] * r + e * v[u][k];
         mx[k] = nm;
@@ -97,7 +148,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
     }
   }
   if constexpr (WIDE) {
-    __shared__ float red[3][3][64 * CPT];          // waves 1..3: max, sum, weighted sum
+    __shared__ float red[kWaves - 1][3][64 * CPT];  // waves 1..: max, sum, weighted sum
     if (wave > 0) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
@@ -109,13 +160,13 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         const float om = red[w][0][c0 + k];
         const float nm = fmaxf(mx[k], om);
         if (nm == -INFINITY) continue;
-        const float r0 = expf(mx[k] - nm), r1 = expf(om - nm);
+        const float r0 = exp2f(mx[k] - nm), r1 = exp2f(om - nm);
         sm[k] = sm[k] * r0 + red[w][1][c0 + k] * r1;
         acc[k] = acc[k] * r0 + red[w][2][c0 + k] * r1;
         mx[k] = nm;
@@ -196,29 +247,58 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressLaunch a) {
   }
 }
 
-template <typename T, int CPT>
-static void launch_cpt(const CompressLaunch& a, hipStream_t s) {
-  if (a.m >= 16) {
-    compress_kernel<T, CPT, true><<<dim3(a.n_entries, a.B), 256, 0, s>>>(a);
+template <typename T, int CPT, bool VEC>
+static void launch_cpt(const CompressBatch& bt, int B, int n_entries, bool wide, hipStream_t s) {
+  if (wide) {
+    compress_kernel<T, CPT, true, VEC><<<dim3(n_entries, B, bt.n_jobs), 512, 0, s>>>(bt);
   } else {
-    compress_kernel<T, CPT, false><<<dim3((a.n_entries + 3) / 4, a.B), 256, 0, s>>>(a);
+    compress_kernel<T, CPT, false, VEC><<<dim3((n_entries + 3) / 4, B, bt.n_jobs), 256, 0, s>>>(bt);
   }
 }
 
+// Every input slice a lane reads starts on a multiple of its size (capped at 16 B).
+template <typename T, int CPT>
+static bool vec_ok(const CompressLaunch& a) {
+  const uint64_t al = CPT * sizeof(T) < 16 ? CPT * sizeof(T) : 16;
+  const uint64_t alb = CPT * 4 < 16 ? CPT * 4 : 16;
+  auto ok = [](const void* p, uint64_t n) { return p == nullptr || ((uint64_t)p % n) == 0; };
+  return ok(a.kv_a, al) && ok(a.gate_a, al) && ok(a.kv_b, al) && ok(a.gate_b, al) &&
+         (uint64_t)a.in_row_stride % al == 0 && (uint64_t)a.in_seq_stride % al == 0 &&
+         ok(a.bias_a, alb) && ok(a.bias_b, alb) && ((uint64_t)a.d * 4) % alb == 0;
+}
+
+template <typename T, int CPT>
+static void launch_cpt(const CompressBatch& bt, int B, int n_entries, bool wide, hipStream_t s) {
+  bool vec = true;
+  for (int j = 0; j < bt.n_jobs; ++j) vec = vec && vec_ok<T, CPT>(bt.job[j]);
+  if (vec) launch_cpt<T, CPT, true>(bt, B, n_entries, wide, s);
+  else launch_cpt<T, CPT, false>(bt, B, n_entries, wide, s);
+}
+
 template <typename T>
-static hipError_t launch_t(const CompressLaunch& a, hipStream_t s) {
-  int cpt = (a.d + 63) / 64;
-  if (a.out_fmt == CSA_FMT_MXFP4 && cpt < 2) cpt = 2;  // a lane packs whole bytes
-  if (cpt <= 1) launch_cpt<T, 1>(a, s);
-  else if (cpt <= 2) launch_cpt<T, 2>(a, s);
-  else if (cpt <= 4) launch_cpt<T, 4>(a, s);
-  else if (cpt <= 8) launch_cpt<T, 8>(a, s);
-  else launch_cpt<T, 16>(a, s);
+static hipError_t launch_t(const CompressBatch& bt, hipStream_t s) {
+  int cpt = 1, B = 1, n_entries = 1;
+  bool wide = false;
+  for (int j = 0; j < bt.n_jobs; ++j) {
+    const CompressLaunch& a = bt.job[j];
+    int c = (a.d + 63) / 64;
+    if (a.out_fmt == CSA_FMT_MXFP4 && c < 2) c = 2;  // a lane packs whole bytes
+    cpt = c > cpt ? c : cpt;
+    B = a.B > B ? a.B : B;
+    n_entries = a.n_entries > n_entries ? a.n_entries : n_entries;
+    wide = wide || a.m >= 16;
+  }
+  if (cpt <= 1) launch_cpt<T, 1>(bt, B, n_entries, wide, s);
+  else if (cpt <= 2) launch_cpt<T, 2>(bt, B, n_entries, wide, s);
+  else if (cpt <= 4) launch_cpt<T, 4>(bt, B, n_entries, wide, s);
+  else if (cpt <= 8) launch_cpt<T, 8>(bt, B, n_entries, wide, s);
+  else launch_cpt<T, 16>(bt, B, n_entries, wide, s);
   return hipGetLastError();
 }
 
-hipError_t launch_compress(const CompressLaunch& a, hipStream_t s) {
-  return a.in_dtype == CSA_DT_F32 ? launch_t<float>(a, s) : launch_t<uint16_t>(a, s);
+// All jobs of a batch share the input dtype (the host splits batches that do not).
+hipError_t launch_compress(const CompressBatch& bt, hipStream_t s) {
+  return bt.job[0].in_dtype == CSA_DT_F32 ? launch_t<float>(bt, s) : launch_t<uint16_t>(bt, s);
 }
 
 }  // namespace csa

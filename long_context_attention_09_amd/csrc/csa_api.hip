@@ -16,7 +16,8 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kIdxChunk = 4096;       // scores per workgroup in the radix passes
-constexpr int64_t kScoreBudget = int64_t(1) << 28;   // fp32 scores held per query block (1 GiB)
+constexpr int64_t kWorkspaceBudget = int64_t(3) << 30;   // per-query-block score + candidate bytes
+constexpr int64_t kMaxIndexCap = int64_t(1024) * 4096;  // entries per sequence the top-k handles
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -68,6 +69,7 @@ int check_index(const CsaIndexArgs* a) {
   if (!a) return CSA_EINVAL;
   if (a->B < 1 || a->n_q < 1 || a->m < 1 || a->n_cap < 1 || a->H_I < 1 || a->d_I < 1 || a->top_k < 1)
     return CSA_EINVAL;
+  if (a->n_cap > kMaxIndexCap) return CSA_EUNSUPPORTED;
   if (!a->q_pos || !a->q0 || !a->w || !a->k0 || !a->out_idx) return CSA_EINVAL;
   if (!aligned(a->q_pos, 8) || !aligned(a->w, 4) || !aligned(a->out_idx, 4)) return CSA_EINVAL;
   if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
@@ -87,7 +89,7 @@ int check_index(const CsaIndexArgs* a) {
 
 struct IndexPlan {
   int n_qb, n_chunks;
-  size_t off_scores, off_hist, off_state, off_counts, total;
+  size_t off_scores, off_hist, off_state, off_ckey, off_ccnt, off_above, off_sel, off_eq, total;
 };
 
 IndexPlan plan_index(const CsaIndexArgs* a) {
@@ -96,8 +98,9 @@ IndexPlan plan_index(const CsaIndexArgs* a) {
   if (a->out_score) {
     p.n_qb = a->n_q;
   } else {
-    int64_t per_q = (int64_t)a->B * a->n_cap;
-    int64_t n = kScoreBudget / (per_q > 0 ? per_q : 1);
+    // scores + candidate keys: 8 bytes per (query, entry)
+    const int64_t per_q = (int64_t)a->B * a->n_cap * 8;
+    int64_t n = kWorkspaceBudget / (per_q > 0 ? per_q : 1);
     if (n < 1) n = 1;
     if (n > a->n_q) n = a->n_q;
     if (n >= 4) n -= n % 4;
@@ -107,12 +110,13 @@ IndexPlan plan_index(const CsaIndexArgs* a) {
   size_t off = 0;
   p.off_scores = off;
   if (!a->out_score) off += align_up(nq * (size_t)a->n_cap * 4);
-  p.off_hist = off;
-  off += align_up(nq * 2048 * 4);
-  p.off_state = off;
-  off += align_up(nq * sizeof(csa::TopkState));
-  p.off_counts = off;
-  off += align_up(nq * (size_t)p.n_chunks * 2 * 4);
+  p.off_hist = off;   off += align_up(nq * 4096 * 4);
+  p.off_state = off;  off += align_up(nq * sizeof(csa::TopkState));
+  p.off_ckey = off;   off += align_up(nq * (size_t)a->n_cap * 4);
+  p.off_ccnt = off;   off += align_up(nq * (size_t)p.n_chunks * 4);
+  p.off_above = off;  off += align_up(nq * (size_t)p.n_chunks * 4);
+  p.off_sel = off;    off += align_up(nq * (size_t)p.n_chunks * 4);
+  p.off_eq = off;     off += align_up(nq * (size_t)p.n_chunks * 4);
   p.total = off;
   return p;
 }
@@ -179,7 +183,7 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
     return p;
   }
   const int64_t units = (int64_t)a->B * a->n_q * ((a->H + 63) / 64);
-  int64_t s = (512 + units - 1) / units;          // aim for ~2 workgroups per compute unit
+  int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
   int64_t s_max = (list + 63) / 64;               // at least two 32-entry tiles per split
   if (s > s_max) s = s_max;
   if (s < 1) s = 1;
@@ -273,28 +277,65 @@ CSA_EXPORT size_t csa_workspace_bytes(int op, const void* args) {
   }
 }
 
-CSA_EXPORT int csa_compress(const CsaCompressArgs* a, void* stream) {
-  int st = check_compress(a);
-  if (st) return st;
+namespace {
+
+// Fill the launch descriptor of one validated job; false when it has no entry.
+bool compress_job(const CsaCompressArgs* a, csa::CompressLaunch* L) {
+  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
+  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  if (end <= first) return false;
+  *L = csa::CompressLaunch{};
+  L->B = a->B; L->d = a->d; L->d_rope = a->d_rope; L->m = a->m; L->in_dtype = a->in_dtype;
+  L->out_fmt = a->out_fmt; L->do_norm = a->do_norm; L->n_entries = (int32_t)(end - first);
+  L->rms_eps = a->rms_eps; L->log_theta = a->d_rope > 0 ? log(a->rope_theta) : 0.0;
+  L->pos0 = a->pos0; L->i_first = first; L->out_row0 = a->out_row0;
+  L->kv_a = a->kv_a; L->gate_a = a->gate_a; L->kv_b = a->kv_b; L->gate_b = a->gate_b;
+  L->in_row_stride = a->in_row_stride;
+  L->in_seq_stride = a->in_seq_stride;
+  L->bias_a = a->bias_a; L->bias_b = a->bias_b;
+  L->out0 = a->out0; L->out1 = a->out1;
+  L->out0_stride = a->out0_stride; L->out0_seq_stride = a->out0_seq_stride;
+  L->out1_stride = a->out1_stride; L->out1_seq_stride = a->out1_seq_stride;
+  return true;
+}
+
+int check_compress_entries(const CsaCompressArgs* a) {
   const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
   const int64_t end = (a->pos0 + a->n_rows) / a->m;
   if (end <= first) return CSA_OK;
   if (first < a->out_row0) return CSA_EINVAL;
   if (end - first > INT32_MAX / 4) return CSA_EUNSUPPORTED;
-  csa::CompressLaunch L{};
-  L.B = a->B; L.d = a->d; L.d_rope = a->d_rope; L.m = a->m; L.in_dtype = a->in_dtype;
-  L.out_fmt = a->out_fmt; L.do_norm = a->do_norm; L.n_entries = (int32_t)(end - first);
-  L.rms_eps = a->rms_eps; L.log_theta = a->d_rope > 0 ? log(a->rope_theta) : 0.0;
-  L.pos0 = a->pos0; L.i_first = first; L.out_row0 = a->out_row0;
-  L.kv_a = a->kv_a; L.gate_a = a->gate_a; L.kv_b = a->kv_b; L.gate_b = a->gate_b;
-  L.in_row_stride = a->in_row_stride;
-  L.in_seq_stride = a->in_seq_stride;
-  L.bias_a = a->bias_a; L.bias_b = a->bias_b;
-  L.out0 = a->out0; L.out1 = a->out1;
-  L.out0_stride = a->out0_stride; L.out0_seq_stride = a->out0_seq_stride;
-  L.out1_stride = a->out1_stride; L.out1_seq_stride = a->out1_seq_stride;
-  if (csa::launch_compress(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
   return CSA_OK;
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void* stream) {
+  if (!jobs || n_jobs < 0) return CSA_EINVAL;
+  for (int j = 0; j < n_jobs; ++j) {
+    int st = check_compress(&jobs[j]);
+    if (!st) st = check_compress_entries(&jobs[j]);
+    if (st) return st;
+  }
+  // one launch per run of up to kMaxJobs jobs of the same input dtype
+  for (int dt = CSA_DT_F32; dt <= CSA_DT_BF16; ++dt) {
+    csa::CompressBatch bt{};
+    for (int j = 0; j < n_jobs; ++j) {
+      if (jobs[j].in_dtype != dt) continue;
+      if (compress_job(&jobs[j], &bt.job[bt.n_jobs])) ++bt.n_jobs;
+      if (bt.n_jobs == csa::kMaxJobs) {
+        if (csa::launch_compress(bt, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
+        bt.n_jobs = 0;
+      }
+    }
+    if (bt.n_jobs > 0 && csa::launch_compress(bt, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
+  }
+  return CSA_OK;
+}
+
+CSA_EXPORT int csa_compress(const CsaCompressArgs* a, void* stream) {
+  if (!a) return CSA_EINVAL;
+  return csa_compress_batch(a, 1, stream);
 }
 
 CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, void* stream) {
@@ -314,7 +355,11 @@ CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, 
     L.scores = a->out_score ? a->out_score : (float*)((char*)ws + p.off_scores);
     L.hist = (uint32_t*)((char*)ws + p.off_hist);
     L.state = (csa::TopkState*)((char*)ws + p.off_state);
-    L.counts = (int32_t*)((char*)ws + p.off_counts);
+    L.cand_key = (uint32_t*)((char*)ws + p.off_ckey);
+    L.chunk_cand = (int32_t*)((char*)ws + p.off_ccnt);
+    L.chunk_above = (int32_t*)((char*)ws + p.off_above);
+    L.chunk_sel = (int32_t*)((char*)ws + p.off_sel);
+    L.chunk_eq = (int32_t*)((char*)ws + p.off_eq);
     L.ev_start = q0 == 0 ? (hipEvent_t)a->ev_start : nullptr;
     L.ev_stop = q0 + p.n_qb >= a->n_q ? (hipEvent_t)a->ev_stop : nullptr;
     if (csa::launch_index_topk(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;

@@ -18,12 +18,22 @@
 // sum.  The kernel also builds the histogram of the top 11 bits of every
 // score's order key for the first radix-select pass.
 //
-// Top-k: a three-pass radix select on the 32-bit order key (11 + 11 + 10 bits),
-// each pass a multi-workgroup histogram of the still-undecided bucket followed
-// by a one-workgroup bucket search; then a count pass and a write pass that
-// emit the selected indices in ascending order.  Elements equal to the k-th
-// key are taken lowest index first.  Histograms use integer atomics only, so
-// the result is deterministic.
+// Top-k over the 32-bit order keys of the scores.  The scoring kernel builds a
+// histogram of the top 12 key bits, then three small kernels follow:
+//   collect finds (in every workgroup) the bucket holding the k-th key, counts,
+//           per 4096-score chunk, the keys above that bucket and appends the
+//           keys inside it to the chunk's region of the candidate list;
+//   refine  (one workgroup per query) radix-selects the k-th key T among the
+//           candidates (10 + 10 more bits) and turns per-chunk counts into the
+//           output offset of every chunk;
+//   write   emits every chunk's selected indices at its offset, in index
+//           order, so the output is ascending; among keys equal to T the
+//           lowest indices are taken.
+// Histograms use integer atomics only and candidate lists are compacted per
+// chunk by block scans, so the result does not depend on any ordering and is
+// deterministic.  The histogram is left zeroed by every call.  Kernel
+// boundaries order the stages: on a multi-XCD part a device-wide fence or a
+// contended device-scope atomic inside a kernel costs more than a launch.
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -31,10 +41,13 @@
 
 namespace csa {
 
-constexpr int kTilesPerWave = 16;                    // 16 keys per tile
-constexpr int kKeysPerWG = 4 * kTilesPerWave * 16;   // 1024
-constexpr int kChunk = 4096;                         // scores per workgroup in the radix passes
-constexpr int kBins1 = 2048;
+constexpr int kTilesPerWave = 64;                    // 16 keys per tile: 1024 keys per wave
+constexpr int kRing = 8;                             // tiles of keys in flight per wave
+constexpr int kKeysPerWG = 4 * kTilesPerWave * 16;   // 4096
+constexpr int kChunk = 4096;                         // scores per workgroup in collect / write
+constexpr int kBins1 = 4096;                         // 12-bit first digit
+constexpr int kShift1 = 20;
+constexpr int kMaxChunks = 1024;                     // per query (n_cap <= 4M)
 
 __device__ __forceinline__ int query_n_vis(const IndexLaunch& a, int b, int r) {
   const int64_t t = a.q_pos[(int64_t)b * a.n_q + a.q_first + r];
@@ -51,6 +64,40 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lh, uint32_t* gh, int
     const uint32_t c = lh[i];
     if (c) atomicAdd(gh + i, c);
   }
+}
+
+// Bucket search over `bins` counts in LDS (bins a multiple of 256): the bucket
+// d holding the k-th largest element (buckets in descending order) and k's
+// rank inside it.  Every thread of the (256-thread) block calls it.
+__device__ void bucket_search(const uint32_t* cnt, int bins, uint32_t k, uint32_t* digit,
+                              uint32_t* k_in) {
+  __shared__ uint32_t tot[256];
+  const int per = bins / 256;
+  const int hi = bins - per * threadIdx.x;      // this thread owns buckets [hi - per, hi)
+  uint32_t my = 0;
+  for (int j = 0; j < per; ++j) my += cnt[hi - 1 - j];
+  tot[threadIdx.x] = my;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t v = threadIdx.x >= o ? tot[threadIdx.x - o] : 0;
+    __syncthreads();
+    tot[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const uint32_t before = threadIdx.x ? tot[threadIdx.x - 1] : 0;
+  if (before < k && k <= before + my) {
+    uint32_t acc = before;
+    for (int j = 0; j < per; ++j) {
+      const uint32_t c = cnt[hi - 1 - j];
+      if (k <= acc + c) {
+        *digit = (uint32_t)(hi - 1 - j);
+        *k_in = k - acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ MXFP4 indexer
@@ -101,50 +148,57 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         }
       }
     }
-    // issue every tile's loads first (16 B of codes + the scale word per lane and
-    // tile), so a wave keeps 4 KiB of keys in flight, then score them
-    i32x4 kbuf[kTilesPerWave];
-    uint32_t kscw[kTilesPerWave];
-#pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) {
+    // ring of kRing tiles in flight: 16 B of codes + the scale word per lane
+    // and tile; tile t + kRing is requested as soon as tile t is scored
+    i32x4 kbuf[kRing];
+    uint32_t kscw[kRing];
+    auto fetch = [&](int t, int u) {
       const int64_t key = key_base + t * 16 + col;
-      kbuf[t] = (i32x4){0, 0, 0, 0};
-      kscw[t] = 0x7f7f7f7fu;
-      if (key < nvis_max && key < a.n_cap) {
-        kbuf[t] = *(const i32x4*)(kc + key * 64 + g * 16);
-        kscw[t] = ks[key];
+      kbuf[u] = (i32x4){0, 0, 0, 0};
+      kscw[u] = 0x7f7f7f7fu;
+      if (t < kTilesPerWave && key < nvis_max && key < a.n_cap) {
+        kbuf[u] = *(const i32x4*)(kc + key * 64 + g * 16);
+        kscw[u] = ks[key];
       }
-    }
+    };
 #pragma unroll
-    for (int t = 0; t < kTilesPerWave; ++t) {
-      const int64_t key0 = key_base + t * 16;
-      if (key0 >= nvis_max) break;
-      const int64_t key = key0 + col;
-      const bool in_cap = key < a.n_cap;
-      const i32x8 kb = {kbuf[t][0], kbuf[t][1], kbuf[t][2], kbuf[t][3], 0, 0, 0, 0};
-      const int ksc = (int)((kscw[t] >> (8 * g)) & 0xffu);
+    for (int u = 0; u < kRing; ++u) fetch(u, u);
+    for (int t0 = 0; t0 < kTilesPerWave; t0 += kRing) {
+      if (key_base + t0 * 16 >= nvis_max) break;
 #pragma unroll
-      for (int qi = 0; qi < QT; ++qi) {
-        float part = 0.f;
+      for (int u = 0; u < kRing; ++u) {
+        const int t = t0 + u;
+        const int64_t key0 = key_base + t * 16;
+        if (key0 < nvis_max) {
+          const int64_t key = key0 + col;
+          const bool in_cap = key < a.n_cap;
+          const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
+          const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-          if (hg < nhg) {
-            i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0, qs[qi][hg],
-                                                                   0, ksc);
+          for (int qi = 0; qi < QT; ++qi) {
+            float part = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part += wv[qi][hg][i] * fmaxf(acc[i], 0.f);
+            for (int hg = 0; hg < 4; ++hg) {
+              if (hg < nhg) {
+                i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0,
+                                                                       qs[qi][hg], 0, ksc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part += wv[qi][hg][i] * fmaxf(acc[i], 0.f);
+              }
+            }
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (g == 0 && r0 + qi < a.n_qb && in_cap) {
+              const bool vis = key < nvis[qi];
+              const float sc = vis ? part : -INFINITY;
+              a.scores[((int64_t)b * a.n_qb + r0 + qi) * a.n_cap + key] = sc;
+              if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
+            }
           }
         }
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
-        if (g == 0 && r0 + qi < a.n_qb && in_cap) {
-          const bool vis = key < nvis[qi];
-          const float s = vis ? part : -INFINITY;
-          a.scores[((int64_t)b * a.n_qb + r0 + qi) * a.n_cap + key] = s;
-          if (vis) atomicAdd(&lhist[qi][order_key(s) >> 21], 1u);
-        }
+        fetch(t + kRing, u);
       }
     }
   }
@@ -186,7 +240,7 @@ __global__ void __launch_bounds__(256) index_f32_kernel(IndexLaunch a) {
         for (int c = 0; c < a.d_I; ++c) dot = fmaf(q[c], k[c], dot);
         s += a.w[qrow + h] * fmaxf(dot, 0.f);
       }
-      atomicAdd(&lhist[order_key(s) >> 21], 1u);
+      atomicAdd(&lhist[order_key(s) >> kShift1], 1u);
     }
     a.scores[((int64_t)b * a.n_qb + r) * a.n_cap + key] = s;
   }
@@ -194,114 +248,213 @@ __global__ void __launch_bounds__(256) index_f32_kernel(IndexLaunch a) {
   flush_hist(lhist, a.hist + ((int64_t)b * a.n_qb + r) * kBins1, kBins1);
 }
 
-// ------------------------------------------------------------------ radix select
+// ------------------------------------------------------------------ collect / refine / write
 
-// Bucket search over one histogram: pass 0 (bits 31..21), 1 (20..10), 2 (9..0).
-// Pass 0 also initialises the state.  Clears the histogram for the next pass.
-__global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a, int pass) {
-  const int q = blockIdx.x;                      // b * n_qb + r
-  const int b = q / a.n_qb, r = q % a.n_qb;
-  TopkState* st = a.state + q;
-  uint32_t* hist = a.hist + (int64_t)q * kBins1;
-  __shared__ uint32_t tot[256];
-  __shared__ TopkState s0;
-  if (threadIdx.x == 0) {
-    if (pass == 0) {
-      s0.prefix = 0; s0.mask = 0;
-      s0.n_vis = query_n_vis(a, b, r);
-      s0.k_rem = s0.n_vis <= a.top_k ? -1 : a.top_k;   // -1: every visible entry is taken
-    } else {
-      s0 = *st;
-    }
-  }
+__device__ __forceinline__ int block_sum_int(int v, int* red) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   __syncthreads();
-  const int bins = pass == 2 ? 1024 : 2048;
-  const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-  const int per = bins / 256;                    // bins per thread, top bins first
-  const int hi = bins - per * threadIdx.x;       // thread t owns bins [hi - per, hi)
-  uint32_t cnt[8];
-  uint32_t my = 0;
-  for (int j = 0; j < per; ++j) { cnt[j] = hist[hi - 1 - j]; my += cnt[j]; }
-  tot[threadIdx.x] = my;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  // inclusive scan over threads (thread 0 = highest bins)
-  for (int o = 1; o < 256; o <<= 1) {
-    uint32_t v = threadIdx.x >= o ? tot[threadIdx.x - o] : 0;
-    __syncthreads();
-    tot[threadIdx.x] += v;
-    __syncthreads();
-  }
-  const int k_rem = s0.k_rem;
-  __shared__ TopkState ns;
-  if (threadIdx.x == 0) ns = s0;
-  __syncthreads();
-  if (k_rem > 0) {
-    const uint32_t before = threadIdx.x ? tot[threadIdx.x - 1] : 0;
-    if (before < (uint32_t)k_rem && (uint32_t)k_rem <= before + my) {
-      uint32_t acc = before;
-      for (int j = 0; j < per; ++j) {
-        if ((uint32_t)k_rem <= acc + cnt[j]) {
-          const uint32_t digit = (uint32_t)(hi - 1 - j);
-          ns.prefix = s0.prefix | (digit << shift);
-          ns.mask = s0.mask | ((uint32_t)(bins - 1) << shift);
-          ns.k_rem = k_rem - (int)acc;
-          break;
-        }
-        acc += cnt[j];
-      }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) *st = ns;
-  __syncthreads();
-  for (int j = threadIdx.x; j < kBins1; j += 256) hist[j] = 0;
+  return red[0] + red[1] + red[2] + red[3];
 }
 
-// Histogram of the next digit among the elements inside the current bucket.
-__global__ void __launch_bounds__(256) topk_hist_kernel(IndexLaunch a, int pass) {
-  __shared__ uint32_t lh[kBins1];
-  const int q = blockIdx.y;
+// Exclusive scan over the block (256 threads) in thread order.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wv; ++w) off += wsum[w];
+  return off + incl - v;
+}
+
+// Candidate g of a query, its chunk found by binary search over the
+// exclusive per-chunk prefix `pref` (n_act entries, in LDS).
+__device__ __forceinline__ int chunk_of(const int* pref, int n_act, int g) {
+  int lo = 0, hi = n_act - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr int kLdsCand = 8192;   // candidates the refine kernel stages in LDS
+
+// One workgroup per query: radix-select the k_rem-th largest key among the
+// candidates (bits 19..10, then 9..0), then per-chunk output offsets.  Up to
+// kLdsCand candidates are staged in LDS with their chunk; more are re-read
+// from the workspace on every pass.
+__global__ void __launch_bounds__(256) topk_refine_kernel(IndexLaunch a) {
+  const int q = blockIdx.x;
+  {
+    uint32_t* gh = a.hist + (int64_t)q * kBins1;   // zeroed for the next call
+    for (int i = threadIdx.x; i < kBins1; i += 256) gh[i] = 0;
+  }
   const TopkState st = a.state[q];
   if (st.k_rem <= 0) return;
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  if (c0 >= st.n_vis) return;
-  for (int i = threadIdx.x; i < kBins1; i += 256) lh[i] = 0;
-  __syncthreads();
-  const int shift = pass == 1 ? 10 : 0;
-  const uint32_t dmask = pass == 1 ? 2047u : 1023u;
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
-  const int64_t end = c0 + kChunk < st.n_vis ? c0 + kChunk : st.n_vis;
-  for (int64_t i = c0 + threadIdx.x; i < end; i += 256) {
-    const uint32_t k = order_key(sc[i]);
-    if ((k & st.mask) == st.prefix) atomicAdd(&lh[(k >> shift) & dmask], 1u);
+  __shared__ uint32_t bins[1024];
+  __shared__ int pref[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
+  __shared__ uint32_t lkey[kLdsCand];
+  __shared__ uint16_t lchunk[kLdsCand];
+  __shared__ uint32_t s_digit, s_kin;
+  __shared__ int red[4];
+  const int n_act = (st.n_vis + kChunk - 1) / kChunk;
+  const int* ccnt = a.chunk_cand + (int64_t)q * a.n_chunks;
+  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
+  // exclusive prefix of the per-chunk candidate counts
+  int total = 0;
+  for (int base = 0; base < n_act; base += 256) {
+    const int c = base + threadIdx.x;
+    const int v = c < n_act ? ccnt[c] : 0;
+    const int ex = total + block_excl_scan(v, red);
+    if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
+    total += block_sum_int(v, red);
   }
   __syncthreads();
-  flush_hist(lh, a.hist + (int64_t)q * kBins1, pass == 1 ? 2048 : 1024);
+  const int n_cand = total;
+  const bool staged = n_cand <= kLdsCand;
+  if (staged) {
+    // eight independent loads in flight per thread
+    for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
+      uint32_t kv[8];
+      int cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = g0 + 256 * u;
+        cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
+        kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = g0 + 256 * u;
+        if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
+      }
+    }
+    __syncthreads();
+  }
+  auto cand = [&](int g, int* chunk) -> uint32_t {
+    if (staged) {
+      *chunk = lchunk[g];
+      return lkey[g];
+    }
+    const int c = chunk_of(pref, n_act, g);
+    *chunk = c;
+    return ck[(int64_t)c * kChunk + (g - pref[c])];
+  };
+  uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
+  uint32_t k = (uint32_t)st.k_rem;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    for (int i = threadIdx.x; i < 1024; i += 256) bins[i] = 0;
+    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
+    __syncthreads();
+    for (int g = threadIdx.x; g < n_cand; g += 256) {
+      int c;
+      const uint32_t key = cand(g, &c);
+      if ((key & mask) == prefix) atomicAdd(&bins[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    bucket_search(bins, 1024, k, &s_digit, &s_kin);
+    prefix |= s_digit << shift;
+    mask |= 1023u << shift;
+    k = s_kin;
+  }
+  const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
+  for (int g = threadIdx.x; g < n_cand; g += 256) {
+    int c;
+    const uint32_t key = cand(g, &c);
+    if (key > T) atomicAdd(&cgt[c], 1);
+    else if (key == T) atomicAdd(&ceq[c], 1);
+  }
+  __syncthreads();
+  // exclusive prefixes over chunks, 256 chunks per round
+  int sel_acc = 0, eq_acc = 0;
+  const int* above = a.chunk_above + (int64_t)q * a.n_chunks;
+  for (int base = 0; base < n_act; base += 256) {
+    const int c = base + threadIdx.x;
+    const bool in = c < n_act;
+    const int neq = in ? ceq[c] : 0;
+    const int eq_ex = eq_acc + block_excl_scan(neq, red);
+    int take = (int)k - eq_ex;
+    take = take < 0 ? 0 : (take > neq ? neq : take);
+    const int nsel = in ? above[c] + cgt[c] + take : 0;
+    const int sel_ex = sel_acc + block_excl_scan(nsel, red);
+    if (in) {
+      a.chunk_sel[(int64_t)q * a.n_chunks + c] = sel_ex;
+      a.chunk_eq[(int64_t)q * a.n_chunks + c] = eq_ex;
+    }
+    sel_acc += block_sum_int(nsel, red);
+    eq_acc += block_sum_int(neq, red);
+  }
+  if (threadIdx.x == 0) {
+    TopkState ns = st;
+    ns.T = T;
+    ns.k_eq = (int)k;
+    a.state[q] = ns;
+  }
 }
 
-// Per chunk: how many visible elements beat the k-th key, and how many equal it.
-__global__ void __launch_bounds__(256) topk_count_kernel(IndexLaunch a) {
+// Per chunk: keys above the first-digit bucket are counted, keys inside it go
+// to the chunk's own region of the query's candidate list (no global atomics).
+__global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   const int q = blockIdx.y;
-  const TopkState st = a.state[q];
+  const int b = q / a.n_qb, r = q % a.n_qb;
+  const int n_vis = query_n_vis(a, b, r);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  int gt = 0, eq = 0;
-  if (st.k_rem > 0 && c0 < st.n_vis) {
-    const float* sc = a.scores + (int64_t)q * a.n_cap;
-    const int64_t end = c0 + kChunk < st.n_vis ? c0 + kChunk : st.n_vis;
-    for (int64_t i = c0 + threadIdx.x; i < end; i += 256) {
-      const uint32_t k = order_key(sc[i]);
-      gt += k > st.prefix;
-      eq += k == st.prefix;
+  if (n_vis <= a.top_k) {                       // every visible entry is taken
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      TopkState st = {};
+      st.n_vis = n_vis;
+      st.k_rem = -1;
+      a.state[q] = st;
     }
+    return;
   }
-  __shared__ int sgt[4], seq[4];
-  for (int o = 32; o >= 1; o >>= 1) { gt += __shfl_xor(gt, o, 64); eq += __shfl_xor(eq, o, 64); }
-  if ((threadIdx.x & 63) == 0) { sgt[threadIdx.x >> 6] = gt; seq[threadIdx.x >> 6] = eq; }
+  if (c0 >= n_vis) return;
+  // every workgroup finds the first-digit bucket of the k-th largest score
+  __shared__ uint32_t lbins[kBins1];
+  __shared__ uint32_t s_digit, s_kin;
+  const uint32_t* gh = a.hist + (int64_t)q * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += 256) lbins[i] = gh[i];
+  if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
   __syncthreads();
+  bucket_search(lbins, kBins1, (uint32_t)a.top_k, &s_digit, &s_kin);
+  TopkState st = {};
+  st.n_vis = n_vis;
+  st.b1 = s_digit;
+  st.k_rem = (int)s_kin;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
+  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
+  int above = 0;
+  uint32_t want = 0;
+  uint32_t keys[kChunk / 256];
+#pragma unroll
+  for (int j = 0; j < kChunk / 256; ++j) {
+    const int64_t i = c0 + j * 256 + threadIdx.x;
+    const bool in = i < st.n_vis;
+    keys[j] = in ? order_key(sc[i]) : 0u;
+    const uint32_t d1 = keys[j] >> kShift1;
+    above += (in && d1 > st.b1) ? 1 : 0;
+    want |= (uint32_t)(in && d1 == st.b1) << j;
+  }
+  __shared__ int red[4];
+  int slot = block_excl_scan(__popc(want), red);
+#pragma unroll
+  for (int j = 0; j < kChunk / 256; ++j)
+    if (want >> j & 1u) ck[slot++] = keys[j];
+  const int n_here = block_sum_int(__popc(want), red);
+  above = block_sum_int(above, red);
   if (threadIdx.x == 0) {
-    int* c = a.counts + ((int64_t)q * a.n_chunks + blockIdx.x) * 2;
-    c[0] = sgt[0] + sgt[1] + sgt[2] + sgt[3];
-    c[1] = seq[0] + seq[1] + seq[2] + seq[3];
+    a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = above;
+    a.chunk_cand[(int64_t)q * a.n_chunks + blockIdx.x] = n_here;
   }
 }
 
@@ -314,8 +467,7 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
   int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
-  const bool all = st.k_rem < 0;
-  if (all) {
+  if (st.k_rem < 0) {
     // every visible entry, in order; chunk 0 also writes the padding
     for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
     if (chunk == 0)
@@ -323,91 +475,44 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
     return;
   }
   if (c0 >= st.n_vis) return;
-  // selected before this chunk
-  __shared__ int s_red[2][4];
-  int sel_before = 0, eq_before = 0;
-  {
-    // pass over previous chunks: eq_before is a prefix sum, so do it serially
-    // per 64-chunk window with a wave scan
-    const int* cnt = a.counts + (int64_t)q * a.n_chunks * 2;
-    int acc_sel = 0, acc_eq = 0;
-    if (threadIdx.x < 64) {
-      for (int base = 0; base < chunk; base += 64) {
-        const int c = base + threadIdx.x;
-        const int ngt = c < chunk ? cnt[2 * c] : 0;
-        const int neq = c < chunk ? cnt[2 * c + 1] : 0;
-        // exclusive scan of neq within the wave
-        int incl = neq;
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_up(incl, o, 64);
-          if ((int)threadIdx.x >= o) incl += v;
-        }
-        const int excl = incl - neq + acc_eq;
-        int take = st.k_rem - excl;
-        take = take < 0 ? 0 : (take > neq ? neq : take);
-        int s = ngt + take;
-        for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-        acc_sel += s;
-        acc_eq += __shfl(incl, 63, 64);
-      }
-      if (threadIdx.x == 0) { s_red[0][0] = acc_sel; s_red[1][0] = acc_eq; }
-    }
-    __syncthreads();
-    sel_before = s_red[0][0];
-    eq_before = s_red[1][0];
-  }
-  // each thread owns 16 consecutive elements of the chunk
+  const int sel_before = a.chunk_sel[(int64_t)q * a.n_chunks + chunk];
+  const int eq_before = a.chunk_eq[(int64_t)q * a.n_chunks + chunk];
   const float* sc = a.scores + (int64_t)q * a.n_cap;
   const int64_t e0 = c0 + threadIdx.x * 16;
   uint32_t gtmask = 0, eqmask = 0;
-  for (int j = 0; j < 16; ++j) {
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
     const int64_t i = e0 + j;
-    if (i < st.n_vis) {
-      const uint32_t k = order_key(sc[i]);
-      gtmask |= (uint32_t)(k > st.prefix) << j;
-      eqmask |= (uint32_t)(k == st.prefix) << j;
+    float v[4];
+    if (i + 3 < st.n_vis && (((uintptr_t)(sc + i)) & 15) == 0) {
+      const f32x4 x = *(const f32x4*)(sc + i);
+      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = i + u < st.n_vis ? sc[i + u] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i + u < st.n_vis) {
+        const uint32_t k = order_key(v[u]);
+        gtmask |= (uint32_t)(k > st.T) << (j + u);
+        eqmask |= (uint32_t)(k == st.T) << (j + u);
+      }
     }
   }
-  // block exclusive scans of the eq counts, then of the selected counts
   __shared__ int wsum[4];
-  auto block_excl_scan = [&](int v) -> int {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    int incl = v;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += u;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int off = 0;
-    for (int w = 0; w < wv; ++w) off += wsum[w];
-    return off + incl - v;
-  };
-  const int eq_excl = eq_before + block_excl_scan(__popc(eqmask));
-  // take the first (k_rem - eq_excl) equal elements of this thread
-  int can = st.k_rem - eq_excl;
+  const int eq_excl = eq_before + block_excl_scan(__popc(eqmask), wsum);
+  int can = st.k_eq - eq_excl;                // equal keys this thread may still take
   uint32_t selmask = gtmask;
   for (int j = 0; j < 16 && can > 0; ++j)
     if (eqmask >> j & 1u) { selmask |= 1u << j; --can; }
-  int pos = sel_before + block_excl_scan(__popc(selmask));
+  int pos = sel_before + block_excl_scan(__popc(selmask), wsum);
   for (int j = 0; j < 16; ++j)
     if ((selmask >> j & 1u) && pos < a.top_k) out[pos++] = (int32_t)(e0 + j);
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
-  {
-    const int64_t n = (int64_t)nq * kBins1;
-    int blocks = (int)((n + 255) / 256);
-    blocks = blocks > 4096 ? 4096 : blocks;
-    zero_u32_kernel<<<blocks, 256, 0, s>>>(a.hist, n);
-  }
   if (a.fmt == CSA_FMT_MXFP4) {
     const int kchunks = (a.n_cap + kKeysPerWG - 1) / kKeysPerWG;
     if (a.n_qb >= 4) {
@@ -422,12 +527,8 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
     hipExtLaunchKernelGGL(index_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
   }
   dim3 g2(a.n_chunks, nq);
-  topk_select_kernel<<<nq, 256, 0, s>>>(a, 0);
-  topk_hist_kernel<<<g2, 256, 0, s>>>(a, 1);
-  topk_select_kernel<<<nq, 256, 0, s>>>(a, 1);
-  topk_hist_kernel<<<g2, 256, 0, s>>>(a, 2);
-  topk_select_kernel<<<nq, 256, 0, s>>>(a, 2);
-  topk_count_kernel<<<g2, 256, 0, s>>>(a);
+  topk_collect_kernel<<<g2, 256, 0, s>>>(a);
+  topk_refine_kernel<<<nq, 256, 0, s>>>(a);
   topk_write_kernel<<<g2, 256, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -24,17 +24,19 @@ struct CompressLaunch {
   int64_t out0_stride, out0_seq_stride, out1_stride, out1_seq_stride;
 };
 
-// Per-query radix-select state kept in the workspace.
+// Per-query top-k state kept in the workspace.
 struct TopkState {
-  uint32_t prefix;    // high bits of the k-th largest order key found so far
-  uint32_t mask;      // which bits of `prefix` are fixed
-  int32_t k_rem;      // how many elements still to take inside the prefix bucket
+  uint32_t b1;        // 12-bit bucket (key >> 20) holding the k-th largest key
+  int32_t k_rem;      // how many to take inside bucket b1 (-1: every visible entry)
   int32_t n_vis;      // visible entries of the query
+  uint32_t T;         // the k-th largest order key
+  int32_t k_eq;       // keys equal to T to take, lowest index first
+  int32_t pad[3];
 };
 
 struct IndexLaunch {
   int32_t B, n_q, m, n_cap, H_I, d_I, fmt, top_k;
-  int32_t n_chunks;          // score chunks per query (radix passes)
+  int32_t n_chunks;          // 4096-score chunks per query
   int32_t q_first;           // first query of this query block
   int32_t n_qb;              // queries in this block
   const int64_t* q_pos;
@@ -48,9 +50,13 @@ struct IndexLaunch {
   float* out_score;          // full [B][n_q][n_cap] output (optional)
   // workspace views (per query of the block: q_local = b * n_qb + r)
   float* scores;             // [B * n_qb][n_cap]
-  uint32_t* hist;            // [B * n_qb][2048]
+  uint32_t* hist;            // [B * n_qb][4096]            zeroed after use
   TopkState* state;          // [B * n_qb]
-  int32_t* counts;           // [B * n_qb][n_chunks][2]
+  uint32_t* cand_key;        // [B * n_qb][n_cap]: chunk c's candidates at [c * 4096, ...)
+  int32_t* chunk_cand;       // [B * n_qb][n_chunks] candidates per chunk
+  int32_t* chunk_above;      // [B * n_qb][n_chunks]
+  int32_t* chunk_sel;        // [B * n_qb][n_chunks] selected before the chunk
+  int32_t* chunk_eq;         // [B * n_qb][n_chunks] keys equal to T before the chunk
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
@@ -79,7 +85,13 @@ struct AttendLaunch {
   hipEvent_t ev_start, ev_stop;  // recorded around the attention kernel (may be null)
 };
 
-hipError_t launch_compress(const CompressLaunch& a, hipStream_t s);
+constexpr int kMaxJobs = 4;
+struct CompressBatch {
+  CompressLaunch job[kMaxJobs];
+  int32_t n_jobs;
+};
+
+hipError_t launch_compress(const CompressBatch& b, hipStream_t s);
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 

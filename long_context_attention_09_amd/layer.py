@@ -87,30 +87,48 @@ class LayerStep:
             return s.L - (s.m if s.overlap else 0)
         return s.L - s.m * (2 if s.overlap else 1)
 
-    def compress_main(self, c=0):
+    def _main_job(self, c=0):
         s = self.s
-        cache = self.caches[c]
-        nope, rope = K.split_main(cache)
-        K.compress(**self._main_streams(), m=s.m, pos0=self._rows_pos0(), out0=nope, out1=rope,
-                   d_rope=s.d_r, rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16)
+        nope, rope = K.split_main(self.caches[c])
+        return K.compress_args(**self._main_streams(), m=s.m, pos0=self._rows_pos0(), out0=nope,
+                               out1=rope, d_rope=s.d_r, rope_theta=s.theta, do_norm=True,
+                               out_fmt=K.FMT_FP8_BF16)
 
-    def compress_index(self, c=0):
+    def _index_job(self, c=0):
         s = self.s
         ix = self.inp["idx"]
         kc, ks = self.keys[c]
-        K.compress(ix["ca"], gate_a=ix["za"], bias_a=ix["ba"], kv_b=ix["cb"], gate_b=ix["zb"],
-                   bias_b=ix["bb"], m=s.m, pos0=self._rows_pos0(), out0=kc, out1=ks, d_rope=0,
-                   do_norm=False, out_fmt=K.FMT_MXFP4)
+        return K.compress_args(ix["ca"], gate_a=ix["za"], bias_a=ix["ba"], kv_b=ix["cb"],
+                               gate_b=ix["zb"], bias_b=ix["bb"], m=s.m, pos0=self._rows_pos0(),
+                               out0=kc, out1=ks, d_rope=0, do_norm=False, out_fmt=K.FMT_MXFP4)
 
-    def store_window(self):
+    def _window_job(self):
         """Raw window rows (m = 1, no gate): RMSNorm, RoPE at the token's own
         position, FP8/BF16 storage into the window buffer, whose row 0 holds
         position L - n_win + 1."""
         s = self.s
         nope, rope = K.split_main(self.win)
-        K.compress(self.inp["win_raw"], m=1, pos0=s.L, out0=nope, out1=rope, d_rope=s.d_r,
-                   rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16,
-                   out_row0=s.L - s.n_win + 1)
+        return K.compress_args(self.inp["win_raw"], m=1, pos0=s.L, out0=nope, out1=rope,
+                               d_rope=s.d_r, rope_theta=s.theta, do_norm=True,
+                               out_fmt=K.FMT_FP8_BF16, out_row0=s.L - s.n_win + 1)
+
+    def compress_main(self, c=0):
+        K.compress_batch([self._main_job(c)])
+
+    def compress_index(self, c=0):
+        K.compress_batch([self._index_job(c)])
+
+    def store_window(self):
+        K.compress_batch([self._window_job()])
+
+    def compress_all(self, c=0):
+        """Every store of the step in one batched call: the newest entry (and,
+        for CSA, the newest indexer key) and the raw window rows."""
+        jobs = [self._main_job(c)]
+        if self.s.csa:
+            jobs.append(self._index_job(c))
+        jobs.append(self._window_job())
+        K.compress_batch(jobs)
 
     def index(self, c=0, events=(None, None)):
         """csa_index_topk; `events` = optional HIP event handles recorded around
@@ -147,7 +165,7 @@ class LayerStep:
                              top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
                              fmt=K.FMT_MXFP4)
             n = K.workspace_bytes(K.OP_INDEX_TOPK, a)
-            self.ws_index = (torch.empty(max(n, 256), dtype=torch.uint8, device=dev), n)
+            self.ws_index = (torch.zeros(max(n, 256), dtype=torch.uint8, device=dev), n)
         nope, rope = K.split_main(self.caches[0])
         wn, wr = K.split_main(self.win)
         a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0, self.inp["sink"],
@@ -155,16 +173,16 @@ class LayerStep:
                           idx=self.idx if s.csa else None, d_rope=s.d_r, rope_theta=s.theta,
                           fmt=K.FMT_FP8_BF16)
         n = K.workspace_bytes(K.OP_ATTEND if s.csa else K.OP_HCA_ATTEND, a)
-        self.ws_attend = (torch.empty(max(n, 256), dtype=torch.uint8, device=dev) if n else None, n)
+        self.ws_attend = (torch.zeros(max(n, 256), dtype=torch.uint8, device=dev) if n else None, n)
 
     # ------------------------------------------------------------ whole step
 
-    def run(self, c=0):
-        """One full step on the current stream (no synchronisation)."""
-        self.compress_main(c)
+    def run(self, c=0, events=None):
+        """One full step on the current stream (no synchronisation).  `events`
+        optionally maps 'index' / 'attend' to (start, stop) HIP event handles
+        recorded around the scoring and attention kernels."""
+        ev = events or {}
+        self.compress_all(c)
         if self.s.csa:
-            self.compress_index(c)
-        self.store_window()
-        if self.s.csa:
-            self.index(c)
-        self.attend(c)
+            self.index(c, events=ev.get("index", (None, None)))
+        self.attend(c, events=ev.get("attend", (None, None)))

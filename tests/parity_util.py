@@ -5,10 +5,13 @@ Tolerances:
   * quantised mode: max abs error 2e-2 on attention outputs (BF16 output; the
     oracle consumes the stored FP8/BF16/MXFP4 codes decoded exactly).
   * storage codes (FP8, BF16, MXFP4): equal, except where the oracle's fp64
-    value lies within REL_CODE of a rounding midpoint of the two candidate
-    codes (or of a power-of-two MXFP4 scale boundary).  REL_CODE = 1e-4 bounds
-    the fp32 rounding of the GPU's pooling (expf, <= 2*m multiply-adds),
-    RMSNorm (a 512-term sum of squares) and rotation.
+    value x lies within REL_CODE * max(|x|, 1) of a rounding midpoint of the
+    two candidate codes (or of a power-of-two MXFP4 scale boundary).  The
+    entries are O(1) (unit RMS after RMSNorm; pooled N(0,1) rows for the
+    indexer), and the GPU computes them in fp32: a 2^-24 rounding per step over
+    the pooling (exp2, <= 2m multiply-adds), RMSNorm (a 512-term sum of
+    squares) and rotation stays below 1e-5 absolute, so 1e-4 leaves a 10x
+    margin; the max(|x|, 1) floor covers entries that cancel to near zero.
   * top-k: both sets have the same size and every index in their symmetric
     difference scores within 1e-3 * |s_k| of the oracle's k-th score s_k.
 """
@@ -26,7 +29,7 @@ TIE_REL = 1e-3
 
 def _near_midpoint(exact, a, b, rel=REL_CODE):
     mid = (a + b) / 2
-    return np.abs(exact - mid) <= rel * np.maximum(np.abs(exact), 1e-30)
+    return np.abs(exact - mid) <= rel * np.maximum(np.abs(exact), 1.0)
 
 
 def check_fp8_codes(gpu_codes, exact, rel=REL_CODE):
@@ -58,8 +61,9 @@ def check_mxfp4_codes(gpu_codes, gpu_scales, exact, rel=REL_CODE):
     amax = np.abs(blocks).max(-1)
     scale_diff = gpu_scales != want_s
     if scale_diff.any():
-        l2 = np.log2(np.maximum(amax[scale_diff], 1e-300))
-        assert np.all(np.abs(l2 - np.round(l2)) <= rel * 2), "MXFP4 scale differs off a boundary"
+        am = amax[scale_diff]
+        edge = np.exp2(np.round(np.log2(np.maximum(am, 1e-300))))
+        assert np.all(np.abs(am - edge) <= rel * np.maximum(am, 1.0)), "MXFP4 scale differs off a boundary"
     g = F.decode_mxfp4(gpu_codes, gpu_scales)
     w = F.decode_mxfp4(want_c, want_s)
     same_scale = np.repeat(~scale_diff, 32, axis=-1).reshape(exact.shape)
