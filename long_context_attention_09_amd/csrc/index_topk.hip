@@ -15,7 +15,7 @@
 // each lane loads 16 bytes straight into its operand registers, so keys
 // stream from HBM exactly once.  ReLU and the head weights are applied to the
 // 4 accumulator rows a lane holds, and two cross-lane adds finish the head
-// sum.  The kernel also builds the histogram of the top 11 bits of every
+// sum.  The kernel also builds the histogram of the top 12 bits of every
 // score's order key for the first radix-select pass.
 //
 // Top-k over the 32-bit order keys of the scores.  The scoring kernel builds a
