@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s per layer at 1M ctx (CSA+HCA) and % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 COPIES = 3
+EVENT_DISABLE_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 CSRC = os.path.join(ROOT, "long_context_attention_09_amd", "csrc")
 
 # HBM traffic per launch from rocprofv3 --pmc runs of this script (FETCH_SIZE
@@ -65,9 +66,11 @@ class HipEvents:
         self.h.hipEventSynchronize.argtypes = [C.c_void_p]
 
     def create(self):
+        # timing events without the system-scope fence at each record (nothing
+        # on the host reads memory through them)
         e = C.c_void_p()
-        if self.h.hipEventCreate(C.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.h.hipEventCreateWithFlags(C.byref(e), C.c_uint(EVENT_DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         return e.value
 
     def elapsed_ms(self, a, b):

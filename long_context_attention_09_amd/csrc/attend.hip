@@ -101,41 +101,77 @@ __device__ __forceinline__ uint32_t pack_hi16(float f0, float f1) {
 
 typedef __attribute__((address_space(1))) const i32x4 gbl_i32x4;
 
-// Global address of list position p (nope part; the rope part is at +rope_delta
-// for AoS rows and is resolved separately), or 0 when the position is masked.
-__device__ __forceinline__ void row_addrs(const AttendLaunch& a, int b, int r, const ListInfo& L, int p,
-                                          int p1, uint64_t* an, uint64_t* ar) {
-  const uint8_t *pn, *pr;
-  if (p < p1 && list_row(a, b, r, L, p, &pn, &pr)) {
-    *an = (uint64_t)pn;
-    *ar = (uint64_t)pr;
-  } else {
-    *an = 0;
-    *ar = 0;
-  }
-}
-
 constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the true max
 
-__global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* tile = smem;                                              // [kTile][kRowBytes]
-  uint64_t* rowa = (uint64_t*)(smem + kTile * kRowBytes);            // [2][2][kTile] addresses
-  float* rope_cs = (float*)(rowa + 2 * 2 * kTile);                   // [2][32] cos, sin at t
+// Workgroup of 8 wavefronts: wave w owns 16 heads (w & 3) and one half of the
+// 512 dims (w >> 2).  The two waves of a head group each form the scores over
+// their half of the dims and swap the partial sums through LDS, so both hold
+// the full scores, run the same online softmax, and accumulate the output for
+// their own 256 dims.  Two wavefronts per SIMD hide each other's LDS latency.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kDHalf = kD / 2;
+
+// Raw-row ring: tiles travel from HBM straight into LDS (global_load_lds,
+// 16 bytes per lane) kRing - 1 tiles ahead of the one in use, so several
+// tiles' worth of loads are in flight per workgroup without holding registers.
+constexpr int kRing = 4;                                  // raw tile slots
+constexpr int kRawRow = kDN + kDR * 2;                    // 576 bytes as stored
+constexpr int kSlotBytes = kTile * kRawRow;               // 18432 = 18 wave loads of 1 KiB
+constexpr int kTileLoads = kSlotBytes / 1024;             // 18: waves 0, 1 issue 3, the others 2
+constexpr int kAddrSlots = 8;                             // row-address ring (tiles)
+constexpr int kIdxMax = kAttendIdxMax;                    // selected indices staged per split
+
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void gbl_void;
+
+// Byte address inside LDS of a pointer to shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + [15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+constexpr int waitcnt_vm_lgkm0(int n) { return waitcnt_vm(n) & kWaitLgkm0; }
+
+// Workgroup barrier without the full memory fence of __syncthreads: the
+// caller states which counters to drain first, so ring loads stay in flight.
+#define ATTEND_BARRIER(waitimm)                  \
+  do {                                           \
+    __builtin_amdgcn_s_waitcnt(waitimm);         \
+    __asm__ __volatile__("" ::: "memory");       \
+    __builtin_amdgcn_s_barrier();                \
+    __asm__ __volatile__("" ::: "memory");       \
+  } while (0)
+
+__global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
+  // Separate LDS objects, so the compiler can tell reads of the BF16 tile
+  // from the ring's in-flight loads (it then leaves those loads in flight).
+  __shared__ __attribute__((aligned(16))) uint8_t raw[kRing * kSlotBytes];   // raw tile slots
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kRowBytes];   // BF16 rows
+  __shared__ __attribute__((aligned(16))) float xch[kWaves * 64 * 8];        // score halves
+  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                          // [slot][nope|rope][row]
+  __shared__ float rope_cs[64];                                              // cos, sin at t
+  __shared__ int lidx[kIdxMax];                                              // staged indices (CSA)
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = wave & 3, dh = wave >> 2;
   const int g = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
-  const int head = hg * 64 + wave * 16 + col;
+  const int head = hg * 64 + hq * 16 + col;
   const bool head_ok = head < a.H;
   const ListInfo L = list_info(a, b, r);
   const int list_len = L.n_comp + L.n_w;
   const int p0 = split * a.split_len;
   int p1 = p0 + a.split_len;
   p1 = p1 < list_len ? p1 : list_len;
+  const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
 
   // RoPE table at the query position (fp64 angle), one pair per thread
   if (tid < kDR / 2) {
@@ -144,134 +180,226 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     rope_cs[tid] = cs;
     rope_cs[32 + tid] = sn;
   }
-  // row addresses of the first two tiles
-  if (tid < 2 * kTile) {
-    const int t = tid >> 5, e = tid & 31;
-    uint64_t an, ar;
-    row_addrs(a, b, r, L, p0 + t * kTile + e, p1, &an, &ar);
-    rowa[(t * 2 + 0) * kTile + e] = an;
-    rowa[(t * 2 + 1) * kTile + e] = ar;
+  // the split's selected indices (CSA), staged once
+  if (a.idx) {
+    const int* src = a.idx + ((int64_t)b * a.n_q + r) * a.top_k;
+    const int n_sel = (p1 < L.n_comp ? p1 : L.n_comp) - p0;
+    for (int i = tid; i < n_sel; i += kThreads) lidx[i] = src[p0 + i];
   }
   __syncthreads();
 
-  // ---- query operand: head `head`, dims 32kb + 8g + j, RMSNorm, RoPE at t, BF16
-  bf16x8 qv[16];
+  // Row addresses of tile t (list positions p0 + 32t ...): 0 marks a masked row.
+  auto tile_addrs = [&](int t) {
+    if (tid < kTile) {
+      const int p = p0 + t * kTile + tid;
+      uint64_t an = 0, ar = 0;
+      if (p < p1) {
+        if (p < L.n_comp) {
+          const int e = a.idx ? lidx[p - p0] : p;
+          if (!a.idx || (e >= 0 && e < L.n_vis)) {
+            const int64_t off = (int64_t)b * a.kv_seq_stride + (int64_t)e * a.kv_stride;
+            an = (uint64_t)((const uint8_t*)a.kv0 + off);
+            ar = (uint64_t)((const uint8_t*)a.kv1 + off);
+          }
+        } else {
+          const int w = p - L.n_comp;
+          if (w < L.n_w) {
+            const int64_t off = (int64_t)b * a.win_seq_stride + (int64_t)(L.win_lo + w) * a.win_stride;
+            an = (uint64_t)((const uint8_t*)a.win0 + off);
+            ar = (uint64_t)((const uint8_t*)a.win1 + off);
+          }
+        }
+      }
+      uint64_t* slot = rowa + (t % kAddrSlots) * 2 * kTile;
+      slot[tid] = an;
+      slot[kTile + tid] = ar;
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < kRing; ++t) tile_addrs(t);
+  __syncthreads();
+
+  // Loader: load i of wave w moves 1 KiB block j = w + 8i of the tile; lane
+  // `lane` carries sixteen-byte chunk c = 64j + lane (row c / 36, part c % 36:
+  // parts 0..27 are the FP8 bytes, 28..35 the BF16 RoPE dims) to byte 16c of
+  // the slot, so a slot holds the tile's rows back to back as stored.  Masked
+  // rows read harmless bytes (the query) and are zeroed at conversion.
+  const int n_loads = wave < kTileLoads - 2 * kWaves ? 3 : 2;   // waves 0, 1 carry blocks 16, 17
+  int ld_row[3], ld_off[3];
+  bool ld_rope[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int c = (wave + kWaves * i) * 64 + lane;
+    const int part = c % kChunksPerRow;
+    ld_row[i] = c < kChunksPerTile ? c / kChunksPerRow : 0;
+    ld_rope[i] = part >= 28;
+    ld_off[i] = part < 28 ? part * 16 : (part - 28) * 16;
+  }
+  const uint64_t dummy = (uint64_t)a.q;      // any readable bytes (q holds >= 16 KiB)
+  auto issue = [&](int t) {
+    const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
+    uint8_t* dst = raw + (t % kRing) * kSlotBytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (i < n_loads) {
+        const uint64_t base = slot_a[(ld_rope[i] ? kTile : 0) + ld_row[i]];
+        const uint64_t src = (base ? base : dummy) + (uint64_t)ld_off[i];
+        __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + (wave + kWaves * i) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
+
+  // ---- query operand: head `head`, dims 256 dh + 32 kb + 8 g + j, RMSNorm, RoPE at t, BF16
+  bf16x8 qv[8];
   {
-    const int hq = head_ok ? head : 0;
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + hq) * kD;
-    float x[16][8];
+    const int hq_ = head_ok ? head : 0;
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + hq_) * kD;
+    float x[8][8];
     float ss = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      const i32x4 v = *(gbl_i32x4*)(qrow + 32 * kb + 8 * g);
+    for (int kb = 0; kb < 8; ++kb) {
+      const i32x4 v = *(gbl_i32x4*)(qrow + kDHalf * dh + 32 * kb + 8 * g);
+      const i32x4 o = *(gbl_i32x4*)(qrow + kDHalf * (1 - dh) + 32 * kb + 8 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[kb][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
         x[kb][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
-        ss += x[kb][2 * j] * x[kb][2 * j] + x[kb][2 * j + 1] * x[kb][2 * j + 1];
+        const float y0 = __uint_as_float(((uint32_t)o[j]) << 16);
+        const float y1 = __uint_as_float(((uint32_t)o[j]) & 0xffff0000u);
+        ss += x[kb][2 * j] * x[kb][2 * j] + x[kb][2 * j + 1] * x[kb][2 * j + 1] + y0 * y0 + y1 * y1;
       }
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[kb][j] *= rs;
+    if (dh == 1) {
 #pragma unroll
-    for (int kb = 14; kb < 16; ++kb) {
+      for (int kb = 6; kb < 8; ++kb) {
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const int u = (32 * kb + 8 * g + j - kDN) >> 1;
-        const float cs = rope_cs[u], sn = rope_cs[32 + u];
-        const float xe = x[kb][j], xo = x[kb][j + 1];
-        x[kb][j] = xe * cs - xo * sn;
-        x[kb][j + 1] = xe * sn + xo * cs;
+        for (int j = 0; j < 8; j += 2) {
+          const int u = (kDHalf + 32 * kb + 8 * g + j - kDN) >> 1;
+          const float cs = rope_cs[u], sn = rope_cs[32 + u];
+          const float xe = x[kb][j], xo = x[kb][j + 1];
+          x[kb][j] = xe * cs - xo * sn;
+          x[kb][j + 1] = xe * sn + xo * cs;
+        }
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) qv[kb][j] = u16_as_bf16(f32_to_bf16(x[kb][j]));
   }
 
-  f32x4 acc_o[32];
+  // first kRing - 1 tiles in flight (the q loads above have been consumed, so
+  // from here on the vector-memory counter tracks only the ring)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kRing - 1; ++t) issue(t);
+
+  f32x4 acc_o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;     // log2-domain reference max of head `col` (lags the true max by < 8)
   float l_part = 0.f;          // this lane's share of the running denominator
+  float* xmine = xch + (wave * 64 + lane) * 8;
+  const float* xpart = xch + ((wave ^ 4) * 64 + lane) * 8;
 
-  // ---- tile loader: thread t < 252 owns sixteen-byte part (t % 36) of rows t/36 + 7k
-  const bool loader = tid < 7 * kChunksPerRow;
-  const int part = tid % kChunksPerRow;
-  const int row0 = tid / kChunksPerRow;
-  const int src_off = part < 28 ? part * 16 : (part - 28) * 16;
-  const int dst_off = part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16;
-  i32x4 stage[kLoadsPerThread];
-  auto fetch = [&](int buf) {
-    const uint64_t* ad = rowa + (buf * 2 + (part < 28 ? 0 : 1)) * kTile;
+  for (int t = 0; t < n_tiles; ++t) {
+    // keep the ring full: tile t + 3 goes into the slot tile t - 1 used
+    // (always issued, so the count of loads in flight is the same every
+    // iteration; past the list the rows are masked and read harmless bytes)
+    issue(t + kRing - 1);
+    tile_addrs(t + kRing);
+    // this wave's loads of tile t are done once at most (kRing - 1) tiles' remain
+    if (n_loads == 3) ATTEND_BARRIER(waitcnt_vm_lgkm0((kRing - 1) * 3));
+    else ATTEND_BARRIER(waitcnt_vm_lgkm0((kRing - 1) * 2));
+
+    // widen tile t to BF16 rows (zeros for masked rows)
+    {
+      const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
+      // The slot is read with the wait written out: the loads that fill it
+      // are counted by hand above, and a plain LDS read here would make the
+      // compiler drain every load in flight, the other slots' included.
+      i32x4 vin[3];
+      {
+        const uint32_t base = lds_addr(raw) + (uint32_t)((t % kRing) * kSlotBytes);
+        uint32_t ad[3];
 #pragma unroll
-    for (int k = 0; k < kLoadsPerThread; ++k) {
-      const int e = row0 + 7 * k;
-      stage[k] = (i32x4){0, 0, 0, 0};
-      if (loader && e < kTile) {
-        const uint64_t base = ad[e];
-        if (base) stage[k] = *(gbl_i32x4*)(base + src_off);
+        for (int k = 0; k < 3; ++k) {
+          const int c = tid + kThreads * k;
+          ad[k] = base + (uint32_t)((c < kChunksPerTile ? c : 0) * 16);
+        }
+        __asm__ __volatile__(
+            "ds_read_b128 %0, %3\n\t"
+            "ds_read_b128 %1, %4\n\t"
+            "ds_read_b128 %2, %5\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(vin[0]), "=&v"(vin[1]), "=&v"(vin[2])
+            : "v"(ad[0]), "v"(ad[1]), "v"(ad[2])
+            : "memory");
       }
-    }
-  };
-  auto commit = [&]() {
 #pragma unroll
-    for (int k = 0; k < kLoadsPerThread; ++k) {
-      const int e = row0 + 7 * k;
-      if (loader && e < kTile) {
-        uint8_t* dst = tile + e * kRowBytes + dst_off;
-        if (part < 28) {
-          i32x4 lo, hi;
+      for (int k = 0; k < 3; ++k) {
+        const int c = tid + kThreads * k;
+        if (c < kChunksPerTile) {
+          const int row = c / kChunksPerRow, part = c % kChunksPerRow;
+          const bool live = slot_a[row] != 0;
+          const i32x4 v = vin[k];
+          uint8_t* dst = tile + row * kRowBytes;
+          if (part < 28) {
+            i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (live) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(stage[k][j], false);
-            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(stage[k][j], true);
-            const uint32_t w0 = pack_hi16(f01[0], f01[1]);
-            const uint32_t w1 = pack_hi16(f23[0], f23[1]);
-            if (j < 2) { lo[2 * j] = (int)w0; lo[2 * j + 1] = (int)w1; }
-            else { hi[2 * (j - 2)] = (int)w0; hi[2 * (j - 2) + 1] = (int)w1; }
+              for (int j = 0; j < 4; ++j) {
+                const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[j], false);
+                const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[j], true);
+                const uint32_t w0 = pack_hi16(f01[0], f01[1]);
+                const uint32_t w1 = pack_hi16(f23[0], f23[1]);
+                if (j < 2) { lo[2 * j] = (int)w0; lo[2 * j + 1] = (int)w1; }
+                else { hi[2 * (j - 2)] = (int)w0; hi[2 * (j - 2) + 1] = (int)w1; }
+              }
+            }
+            *(i32x4*)(dst + part * 32) = lo;
+            *(i32x4*)(dst + part * 32 + 16) = hi;
+          } else {
+            *(i32x4*)(dst + kDN * 2 + (part - 28) * 16) = live ? v : (i32x4){0, 0, 0, 0};
           }
-          *(i32x4*)dst = lo;
-          *(i32x4*)(dst + 16) = hi;
-        } else {
-          *(i32x4*)dst = stage[k];
         }
       }
     }
-  };
+    ATTEND_BARRIER(kWaitLgkm0);
+    const uint64_t* vrow = rowa + (t % kAddrSlots) * 2 * kTile;   // masked rows have address 0
 
-  int buf = 0;
-  if (p0 < p1) {
-    fetch(0);
-    commit();
-  }
-  __syncthreads();
-
-  for (int tile0 = p0; tile0 < p1; tile0 += kTile) {
-    const bool more = tile0 + kTile < p1;
-    if (more) fetch(buf ^ 1);
-    const uint64_t* vrow = rowa + (buf * 2) * kTile;   // masked rows have address 0
-
-    // S^T = K Q^T : two 16-entry blocks, each split over two accumulators
+    // partial S^T = K Q^T over this wave's 256 dims: two 16-entry blocks,
+    // each split over two accumulators
     f32x4 s[2];
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + 16 * g;
+      const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + kDHalf * 2 * dh + 16 * g;
 #pragma unroll
-      for (int kb = 0; kb < 16; kb += 2) {
+      for (int kb = 0; kb < 8; kb += 2) {
         const bf16x8 k0 = *(const bf16x8*)(krow + 64 * kb);
         const bf16x8 k1 = *(const bf16x8*)(krow + 64 * (kb + 1));
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv[kb], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[kb + 1], s1, 0, 0, 0);
       }
       s[eb] = s0 + s1;
+    }
+    // swap halves with the partner wave (same heads, other dims)
+    *(f32x4*)xmine = s[0];
+    *(f32x4*)(xmine + 4) = s[1];
+    ATTEND_BARRIER(kWaitLgkm0);
+    {
+      const f32x4 o0 = *(const f32x4*)xpart, o1 = *(const f32x4*)(xpart + 4);
+      // the same sum in both waves (a + b == b + a), so both run the same softmax
+      s[0] = dh == 0 ? s[0] + o0 : o0 + s[0];
+      s[1] = dh == 0 ? s[1] + o1 : o1 + s[1];
     }
     // online softmax (log2 domain); lane holds entries eb*16 + 4g + i of head `col`
     float mx = -INFINITY;
@@ -303,14 +431,15 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     if (__any(alpha != 1.0f)) {
       l_part *= alpha;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) acc_o[db] *= alpha;
+      for (int db = 0; db < 16; ++db) acc_o[db] *= alpha;
     }
     l_part += psum;
     m_run = m_new;
-    // O^T += V^T P^T ; lane (g, col) supplies row 4g + col/4 (+16) at dims 16db + 4(col%4)
-    const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + 8 * (col & 3);
+    // O^T += V^T P^T over this wave's dims; lane (g, col) supplies row
+    // 4g + col/4 (+16) at dims 256 dh + 16 db + 4 (col % 4)
+    const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + kDHalf * 2 * dh + 8 * (col & 3);
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
+    for (int db = 0; db < 16; ++db) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * db));
       const i16x4 hi =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRowBytes + 32 * db));
@@ -322,22 +451,11 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
       }
       acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[db], 0, 0, 0);
     }
-    __syncthreads();
-    if (more) {
-      commit();
-      // addresses of the tile after next go where this tile's were
-      if (tid < kTile) {
-        uint64_t an, ar;
-        row_addrs(a, b, r, L, tile0 + 2 * kTile + tid, p1, &an, &ar);
-        rowa[(buf * 2 + 0) * kTile + tid] = an;
-        rowa[(buf * 2 + 1) * kTile + tid] = ar;
-      }
-    }
-    buf ^= 1;
-    __syncthreads();
   }
+  // the ring's trailing loads (past the list) must land before the wave ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue
+  // ---- epilogue: this wave's 256 dims of its 16 heads
   float l_run = l_part + __shfl_xor(l_part, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (!head_ok) return;
@@ -347,17 +465,17 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
     const float top = fmaxf(m_run, z2);
     const float den = l_run * exp2f(m_run - top) + exp2f(z2 - top);
     const float inv = exp2f(m_run - top) / den;      // 0 when no row was seen
-    uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
+    uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD + kDHalf * dh;
     const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
+    for (int db = 0; db < 16; ++db) {
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = acc_o[db][i] * inv;
-      if (db >= 28 && inv_rope) {
+      if (dh == 1 && db >= 12 && inv_rope) {
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const int u = (16 * db + 4 * g + i - kDN) >> 1;
+          const int u = (kDHalf + 16 * db + 4 * g + i - kDN) >> 1;
           const float cs = rope_cs[u], sn = -rope_cs[32 + u];   // rotation by -t
           const float xe = o[i], xo = o[i + 1];
           o[i] = xe * cs - xo * sn;
@@ -368,15 +486,15 @@ __global__ void __launch_bounds__(256, 1) attend_fp8_kernel(AttendLaunch a) {
       const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
       *(i32x2*)(orow + 16 * db + 4 * g) = (i32x2){(int)w0, (int)w1};
     }
-    if (a.out_lse && g == 0)
+    if (a.out_lse && g == 0 && dh == 0)
       a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
           l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   } else {
-    const int64_t ps = (unit * a.n_splits + split) * 64 + wave * 16 + col;
-    float* po = a.part_o + ps * kD;
+    const int64_t ps = (unit * a.n_splits + split) * 64 + hq * 16 + col;
+    float* po = a.part_o + ps * kD + kDHalf * dh;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *(f32x4*)(po + 16 * db + 4 * g) = acc_o[db];
-    if (g == 0) {
+    for (int db = 0; db < 16; ++db) *(f32x4*)(po + 16 * db + 4 * g) = acc_o[db];
+    if (g == 0 && dh == 0) {
       a.part_ml[ps * 2] = m_run;
       a.part_ml[ps * 2 + 1] = l_run;
     }
@@ -562,8 +680,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   }
   const int n_hg = (a.H + 63) / 64;
   dim3 grid(a.n_splits, n_hg, a.B * a.n_q);
-  const size_t smem = kTile * kRowBytes + 2 * 2 * kTile * sizeof(uint64_t) + 64 * sizeof(float);
-  hipExtLaunchKernelGGL(attend_fp8_kernel, grid, dim3(256), (uint32_t)smem, s, a.ev_start, a.ev_stop, 0, a);
+  hipExtLaunchKernelGGL(attend_fp8_kernel, grid, dim3(kThreads), 0, s, a.ev_start, a.ev_stop, 0, a);
   if (a.n_splits > 1) combine_kernel<<<dim3(a.B * a.n_q * n_hg, 16), 256, 0, s>>>(a, n_hg);
   return hipGetLastError();
 }

@@ -19,6 +19,11 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 2^x on the hardware exp2 unit (one instruction).  Results below 2^-126
+// flush to zero; every caller passes x <= 0 for softmax weights relative to a
+// running maximum, where such weights are negligible.  exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------ BF16
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {

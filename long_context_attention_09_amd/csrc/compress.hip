@@ -126,19 +126,31 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
         for (int k = 0; k < CPT; ++k) bias[u][k] = 0.f;
       }
     }
+    // Softmax in base 2, folded one batch at a time: the batch's largest
+    // logit per channel is found first, so the running state is rescaled once
+    // per batch and every candidate costs one exp2.  Dead slots have logit
+    // -inf and weight exp2(-inf) = 0.
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int k = 0; k < CPT; ++k) {
+      float lg[kBatch];
+      float bm = mx[k];
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        // softmax taken in base 2; a dead slot contributes exp2(-inf) = 0
-        const float lg = live[u] ? (z[u][k] + bias[u][k]) * kLog2e : -INFINITY;
-        const float nm = fmaxf(mx[k], lg);
-        const float r = nm == -INFINITY ? 1.0f : exp2f(mx[k] - nm);   // 0 on the first live slot
-        const float e = lg == -INFINITY ? 0.0f : exp2f(lg - nm);
-        sm[k] = sm[k] * r + e;
-        acc[k] = acc[k] * r + e * v[u][k];
-        mx[k] = nm;
+      for (int u = 0; u < kBatch; ++u) {
+        lg[u] = live[u] ? (z[u][k] + bias[u][k]) * kLog2e : -INFINITY;
+        bm = fmaxf(bm, lg[u]);
       }
+      const float base = bm == -INFINITY ? 0.f : bm;
+      const float r = fast_exp2(mx[k] - base);       // 0 while nothing was folded
+      float sum = sm[k] * r, num = acc[k] * r;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float e = fast_exp2(lg[u] - base);
+        sum += e;
+        num = fmaf(e, v[u][k], num);
+      }
+      sm[k] = sum;
+      acc[k] = num;
+      mx[k] = bm;
     }
   }
   if constexpr (WIDE) {
@@ -160,7 +172,7 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
         const float om = red[w][0][c0 + k];
         const float nm = fmaxf(mx[k], om);
         if (nm == -INFINITY) continue;
-        const float r0 = exp2f(mx[k] - nm), r1 = exp2f(om - nm);
+        const float r0 = fast_exp2(mx[k] - nm), r1 = fast_exp2(om - nm);
         sm[k] = sm[k] * r0 + red[w][1][c0 + k] * r1;
         acc[k] = acc[k] * r0 + red[w][2][c0 + k] * r1;
         mx[k] = nm;
@@ -184,15 +196,35 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
   if (a.d_rope > 0) {
     const double pos = (double)m * (double)i;
     if constexpr (CPT % 2 == 0) {
+      const int n_pairs = a.d_rope >> 1;
+      if (n_pairs <= 64) {
+        // lane u forms the angle of pair u once; lanes holding rotated
+        // channels fetch their pairs' cos / sin from those lanes
+        float cs_l = 1.f, sn_l = 0.f;
+        if (lane < n_pairs) rope_cos_sin(pos, lane, a.d_rope, a.log_theta, &cs_l, &sn_l);
 #pragma unroll
-      for (int k = 0; k < CPT; k += 2) {
-        const int c = c0 + k;
-        if (c >= d0 && c < d) {
-          float cs, sn;
-          rope_cos_sin(pos, (c - d0) >> 1, a.d_rope, a.log_theta, &cs, &sn);
-          const float xe = x[k], xo = x[k + 1];
-          x[k] = xe * cs - xo * sn;
-          x[k + 1] = xe * sn + xo * cs;
+        for (int k = 0; k < CPT; k += 2) {
+          const int c = c0 + k;
+          const int u = (c - d0) >> 1;
+          const int src = (c >= d0 && c < d) ? u : 0;
+          const float cs = __shfl(cs_l, src, 64), sn = __shfl(sn_l, src, 64);
+          if (c >= d0 && c < d) {
+            const float xe = x[k], xo = x[k + 1];
+            x[k] = xe * cs - xo * sn;
+            x[k + 1] = xe * sn + xo * cs;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPT; k += 2) {
+          const int c = c0 + k;
+          if (c >= d0 && c < d) {
+            float cs, sn;
+            rope_cos_sin(pos, (c - d0) >> 1, a.d_rope, a.log_theta, &cs, &sn);
+            const float xe = x[k], xo = x[k + 1];
+            x[k] = xe * cs - xo * sn;
+            x[k + 1] = xe * sn + xo * cs;
+          }
         }
       }
     } else {

@@ -186,9 +186,14 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
   int64_t s_max = (list + 63) / 64;               // at least two 32-entry tiles per split
   if (s > s_max) s = s_max;
+  if (!dense) {                                   // a CSA split's indices fit the kernel's stage
+    const int64_t s_min = (list + csa::kAttendIdxMax - 1) / csa::kAttendIdxMax;
+    if (s < s_min) s = s_min;
+  }
   if (s < 1) s = 1;
   int64_t len = (list + s - 1) / s;
   len = (len + 31) / 32 * 32;
+  if (!dense && len > csa::kAttendIdxMax) len = csa::kAttendIdxMax;
   s = (list + len - 1) / len;
   p.n_splits = (int)s;
   p.split_len = (int)len;

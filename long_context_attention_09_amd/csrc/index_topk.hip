@@ -36,18 +36,31 @@
 // contended device-scope atomic inside a kernel costs more than a launch.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.hpp"
+
 #include "kernels.hpp"
 
 namespace csa {
 
 constexpr int kTilesPerWave = 64;                    // 16 keys per tile: 1024 keys per wave
 constexpr int kRing = 8;                             // tiles of keys in flight per wave
-constexpr int kKeysPerWG = 4 * kTilesPerWave * 16;   // 4096
+constexpr int kWaveKeys = kTilesPerWave * 16;        // 1024
+constexpr int kKeysPerWG = 4 * kWaveKeys;            // 4096
 constexpr int kChunk = 4096;                         // scores per workgroup in collect / write
 constexpr int kBins1 = 4096;                         // 12-bit first digit
 constexpr int kShift1 = 20;
 constexpr int kMaxChunks = 1024;                     // per query (n_cap <= 4M)
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format, the value the ROCm libraries use for untyped buffer loads).
+constexpr int kBufferWord3 = 0x00020000;
+
+// max(x, 0) as one integer max on the bit pattern: negative floats (sign bit
+// set) are negative integers and map to +0; non-negative floats are unchanged.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
 
 __device__ __forceinline__ int query_n_vis(const IndexLaunch& a, int b, int r) {
   const int64_t t = a.q_pos[(int64_t)b * a.n_q + a.q_first + r];
@@ -102,16 +115,16 @@ __device__ void bucket_search(const uint32_t* cnt, int bins, uint32_t k, uint32_
 
 // ------------------------------------------------------------------ MXFP4 indexer
 
-template <int QT>
+template <int QT, int NHG>
 __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   __shared__ uint32_t lhist[QT][kBins1];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;       // k-group of the operand / row group of the result
   const int col = lane & 15;
   const int b = blockIdx.z;
   const int r0 = blockIdx.y * QT;
-  const int nhg = a.H_I >> 4;    // head groups of 16
+  constexpr int nhg = NHG;       // head groups of 16 (H_I / 16)
 
   for (int i = threadIdx.x; i < QT * kBins1; i += 256) (&lhist[0][0])[i] = 0;
 
@@ -119,7 +132,8 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   int nvis_max = 0;
 #pragma unroll
   for (int qi = 0; qi < QT; ++qi) {
-    nvis[qi] = (r0 + qi < a.n_qb) ? query_n_vis(a, b, r0 + qi) : 0;
+    // the counts are uniform over the workgroup: keep them in scalar registers
+    nvis[qi] = __builtin_amdgcn_readfirstlane((r0 + qi < a.n_qb) ? query_n_vis(a, b, r0 + qi) : 0);
     nvis_max = nvis[qi] > nvis_max ? nvis[qi] : nvis_max;
   }
   __syncthreads();
@@ -148,69 +162,91 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         }
       }
     }
+    // Keys and scores go through per-wave buffer resources that cover only
+    // this wave's keys (and only visible keys for the loads): the hardware
+    // range check returns zeros for loads past the end and drops stores past
+    // it, so no memory instruction in the loop is conditional.  That keeps
+    // the compiler's count of loads in flight exact across iterations, and
+    // the ring stays full instead of draining once per round.
+    const int64_t vis_here = (int64_t)nvis_max - key_base;             // > 0
+    const uint32_t n_load = (uint32_t)(vis_here < kWaveKeys ? vis_here : kWaveKeys);
+    const int64_t cap_here = (int64_t)a.n_cap - key_base;              // >= vis_here
+    const uint32_t n_store = (uint32_t)(cap_here < kWaveKeys ? cap_here : kWaveKeys);
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kc + key_base * 64), 0, (int)(n_load * 64u), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(ks + key_base), 0, (int)(n_load * 4u), kBufferWord3);
+    __amdgpu_buffer_rsrc_t rsc[QT];
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      const bool live = r0 + qi < a.n_qb;
+      float* srow = a.scores + ((int64_t)b * a.n_qb + (live ? r0 + qi : r0)) * a.n_cap + key_base;
+      rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)(n_store * 4u) : 0, kBufferWord3);
+    }
+    const uint32_t off_c = (uint32_t)col * 64u + (uint32_t)g * 16u;
+    const uint32_t off_s = (uint32_t)col * 4u;
+    // lanes of row groups 1..3 hold copies of the head sum: their stores are
+    // sent past the end of the score buffer and dropped
+    const uint32_t off_o = g == 0 ? (uint32_t)col * 4u : 0x40000000u;
     // ring of kRing tiles in flight: 16 B of codes + the scale word per lane
     // and tile; tile t + kRing is requested as soon as tile t is scored
+    // (tiles past the wave's keys read as zeros without touching memory)
     i32x4 kbuf[kRing];
     uint32_t kscw[kRing];
     auto fetch = [&](int t, int u) {
-      const int64_t key = key_base + t * 16 + col;
-      kbuf[u] = (i32x4){0, 0, 0, 0};
-      kscw[u] = 0x7f7f7f7fu;
-      if (t < kTilesPerWave && key < nvis_max && key < a.n_cap) {
-        kbuf[u] = *(const i32x4*)(kc + key * 64 + g * 16);
-        kscw[u] = ks[key];
-      }
+      kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rc, off_c + (uint32_t)t * 1024u, 0, 0));
+      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)t * 64u, 0, 0);
     };
+    // issue the first round in ring order (the loop consumes it in that order)
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) fetch(u, u);
-    for (int t0 = 0; t0 < kTilesPerWave; t0 += kRing) {
-      if (key_base + t0 * 16 >= nvis_max) break;
+    for (int u = 0; u < kRing; ++u) {
+      fetch(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int xor16 = (lane ^ 16) << 2, xor32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
+    const int n_rounds = (int)((n_load + 16 * kRing - 1) / (16 * kRing));
+    for (int t0 = 0; t0 < n_rounds * kRing; t0 += kRing) {
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;
-        const int64_t key0 = key_base + t * 16;
-        if (key0 < nvis_max) {
-          const int64_t key = key0 + col;
-          const bool in_cap = key < a.n_cap;
-          const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
-          const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
+        const uint32_t kl = (uint32_t)(t * 16 + col);         // key - key_base
+        const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
+        const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
 #pragma unroll
-          for (int qi = 0; qi < QT; ++qi) {
-            float part = 0.f;
+        for (int qi = 0; qi < QT; ++qi) {
+          float part = 0.f;
 #pragma unroll
-            for (int hg = 0; hg < 4; ++hg) {
-              if (hg < nhg) {
-                i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0,
-                                                                       qs[qi][hg], 0, ksc);
+          for (int hg = 0; hg < nhg; ++hg) {
+            i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0,
+                                                                   qs[qi][hg], 0, ksc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part += wv[qi][hg][i] * fmaxf(acc[i], 0.f);
-              }
-            }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            if (g == 0 && r0 + qi < a.n_qb && in_cap) {
-              const bool vis = key < nvis[qi];
-              const float sc = vis ? part : -INFINITY;
-              a.scores[((int64_t)b * a.n_qb + r0 + qi) * a.n_cap + key] = sc;
-              if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
-            }
+            for (int i = 0; i < 4; ++i) part = fmaf(wv[qi][hg][i], relu(acc[i]), part);
           }
+          part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(part)));
+          part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(part)));
+          const bool vis = (int64_t)kl < (int64_t)nvis[qi] - key_base;
+          const float sc = vis ? part : -INFINITY;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + (uint32_t)t * 64u, 0, 0);
+          if (g == 0 && vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
         }
         fetch(t + kRing, u);
       }
     }
-  }
-  // keys in tiles past every query's visible range still get -inf
-  {
-    const int64_t wave_end = key_base + kTilesPerWave * 16;
-    int64_t start = key_base;
-    if (nvis_max > key_base) start = key_base + (((int64_t)nvis_max - key_base + 15) / 16) * 16;
+    // keys of this wave that the rounds did not reach get -inf
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi)
+      for (uint32_t k = (uint32_t)(n_rounds * kRing * 16) + lane; k < n_store; k += 64)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], k * 4u, 0, 0);
+  } else {
+    // no query sees any key of this wave
     for (int qi = 0; qi < QT; ++qi) {
       if (r0 + qi >= a.n_qb) break;
       float* row = a.scores + ((int64_t)b * a.n_qb + r0 + qi) * a.n_cap;
-      for (int64_t k = start + lane; k < wave_end && k < a.n_cap; k += 64) row[k] = -INFINITY;
+      const int64_t wave_end = key_base + kWaveKeys;
+      for (int64_t k = key_base + lane; k < wave_end && k < a.n_cap; k += 64) row[k] = -INFINITY;
     }
   }
   __syncthreads();
@@ -515,12 +551,23 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
   if (a.fmt == CSA_FMT_MXFP4) {
     const int kchunks = (a.n_cap + kKeysPerWG - 1) / kKeysPerWG;
+    const int nhg = a.H_I / 16;
+    auto go = [&](auto qt, auto hg) {
+      constexpr int QT = decltype(qt)::value, HG = decltype(hg)::value;
+      dim3 grid(kchunks, (a.n_qb + QT - 1) / QT, a.B);
+      hipExtLaunchKernelGGL(index_mxfp4_kernel<QT, HG>, grid, dim3(256), 0, s, a.ev_start,
+                            a.ev_stop, 0, a);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
     if (a.n_qb >= 4) {
-      dim3 grid(kchunks, (a.n_qb + 3) / 4, a.B);
-      hipExtLaunchKernelGGL(index_mxfp4_kernel<4>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+      if (nhg == 4) go(I4{}, I4{}); else if (nhg == 3) go(I4{}, I3{});
+      else if (nhg == 2) go(I4{}, I2{}); else go(I4{}, I1{});
     } else {
-      dim3 grid(kchunks, a.n_qb, a.B);
-      hipExtLaunchKernelGGL(index_mxfp4_kernel<1>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+      if (nhg == 4) go(I1{}, I4{}); else if (nhg == 3) go(I1{}, I3{});
+      else if (nhg == 2) go(I1{}, I2{}); else go(I1{}, I1{});
     }
   } else {
     dim3 grid((a.n_cap + 255) / 256, a.n_qb, a.B);

@@ -60,6 +60,9 @@ struct IndexLaunch {
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
+// Longest split of a CSA selection list the FP8 attention kernel stages in LDS.
+constexpr int kAttendIdxMax = 4096;
+
 struct AttendLaunch {
   int32_t B, n_q, H, d, d_rope, m, fmt, flags;
   double log_theta;
