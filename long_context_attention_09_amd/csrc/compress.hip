@@ -23,9 +23,6 @@ __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-
 // CPT consecutive channels of one row starting at channel c0 (0 beyond d).
 // VEC: the row and every lane's slice are aligned to the slice size and d is
 // a multiple of CPT (d % 8 == 0, CPT <= 8), so a lane's slice is either wholly

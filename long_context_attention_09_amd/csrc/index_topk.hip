@@ -79,38 +79,55 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lh, uint32_t* gh, int
   }
 }
 
-// Bucket search over `bins` counts in LDS (bins a multiple of 256): the bucket
-// d holding the k-th largest element (buckets in descending order) and k's
-// rank inside it.  Every thread of the (256-thread) block calls it.
-__device__ void bucket_search(const uint32_t* cnt, int bins, uint32_t k, uint32_t* digit,
-                              uint32_t* k_in) {
-  __shared__ uint32_t tot[256];
-  const int per = bins / 256;
-  const int hi = bins - per * threadIdx.x;      // this thread owns buckets [hi - per, hi)
+// Bucket search: the bucket holding the k-th largest element and k's rank
+// inside it.  Thread t of the 256-thread block holds the counts of buckets
+// hi-1, hi-2, ..., hi-PER (hi = 256 PER - PER t) in v[0..PER), i.e. the
+// buckets in descending order are spread over the threads in thread order.
+// A wave-level scan and one exchange of wave totals find the owner thread,
+// which writes the bucket to *digit and the rank to *k_in (shared memory,
+// set by the caller for the case where no thread matches).  Two barriers.
+template <int PER>
+__device__ void bucket_search(const uint32_t (&v)[PER], uint32_t k, uint32_t* digit, uint32_t* k_in) {
+  __shared__ uint32_t wtot[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t my = 0;
-  for (int j = 0; j < per; ++j) my += cnt[hi - 1 - j];
-  tot[threadIdx.x] = my;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const uint32_t v = threadIdx.x >= o ? tot[threadIdx.x - o] : 0;
-    __syncthreads();
-    tot[threadIdx.x] += v;
-    __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) my += v[j];
+  uint32_t incl = my;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
   }
-  const uint32_t before = threadIdx.x ? tot[threadIdx.x - 1] : 0;
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  uint32_t before = incl - my;
+  for (int w = 0; w < wv; ++w) before += wtot[w];
   if (before < k && k <= before + my) {
+    const int hi = PER * 256 - PER * (int)threadIdx.x;
     uint32_t acc = before;
-    for (int j = 0; j < per; ++j) {
-      const uint32_t c = cnt[hi - 1 - j];
-      if (k <= acc + c) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (acc < k && k <= acc + v[j]) {
         *digit = (uint32_t)(hi - 1 - j);
         *k_in = k - acc;
-        break;
       }
-      acc += c;
+      acc += v[j];
     }
   }
   __syncthreads();
+}
+
+// The PER counts of this thread's buckets (see bucket_search) from a bin array.
+template <int PER>
+__device__ __forceinline__ void my_buckets(const uint32_t* cnt, uint32_t (&v)[PER]) {
+  const int lo = PER * 256 - PER * ((int)threadIdx.x + 1);   // lowest bucket of the thread
+#pragma unroll
+  for (int j = 0; j < PER; j += 4) {
+    const u32x4 w = *(const u32x4*)(cnt + lo + j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[PER - 1 - (j + i)] = w[i];
+  }
 }
 
 // ------------------------------------------------------------------ MXFP4 indexer
@@ -294,8 +311,9 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Exclusive scan over the block (256 threads) in thread order.
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+// Exclusive scan over the block (256 threads) in thread order; *total gets
+// the block sum when given.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total = nullptr) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int incl = v;
   for (int o = 1; o < 64; o <<= 1) {
@@ -307,6 +325,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
   __syncthreads();
   int off = 0;
   for (int w = 0; w < wv; ++w) off += wsum[w];
+  if (total) *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   return off + incl - v;
 }
 
@@ -329,112 +348,119 @@ constexpr int kLdsCand = 8192;   // candidates the refine kernel stages in LDS
 // from the workspace on every pass.
 __global__ void __launch_bounds__(256) topk_refine_kernel(IndexLaunch a) {
   const int q = blockIdx.x;
-  {
-    uint32_t* gh = a.hist + (int64_t)q * kBins1;   // zeroed for the next call
-    for (int i = threadIdx.x; i < kBins1; i += 256) gh[i] = 0;
-  }
   const TopkState st = a.state[q];
-  if (st.k_rem <= 0) return;
-  __shared__ uint32_t bins[1024];
+  __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
   __shared__ int pref[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
   __shared__ uint32_t lkey[kLdsCand];
   __shared__ uint16_t lchunk[kLdsCand];
-  __shared__ uint32_t s_digit, s_kin;
-  __shared__ int red[4];
-  const int n_act = (st.n_vis + kChunk - 1) / kChunk;
-  const int* ccnt = a.chunk_cand + (int64_t)q * a.n_chunks;
-  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
-  // exclusive prefix of the per-chunk candidate counts
-  int total = 0;
-  for (int base = 0; base < n_act; base += 256) {
-    const int c = base + threadIdx.x;
-    const int v = c < n_act ? ccnt[c] : 0;
-    const int ex = total + block_excl_scan(v, red);
-    if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
-    total += block_sum_int(v, red);
-  }
-  __syncthreads();
-  const int n_cand = total;
-  const bool staged = n_cand <= kLdsCand;
-  if (staged) {
-    // eight independent loads in flight per thread
-    for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
-      uint32_t kv[8];
-      int cv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int g = g0 + 256 * u;
-        cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
-        kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int g = g0 + 256 * u;
-        if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
-      }
+  __shared__ uint32_t s_digit[2], s_kin[2];
+  __shared__ int red[4][4];
+  if (st.k_rem > 0) {
+    const int n_act = (st.n_vis + kChunk - 1) / kChunk;
+    const int* ccnt = a.chunk_cand + (int64_t)q * a.n_chunks;
+    const int* above = a.chunk_above + (int64_t)q * a.n_chunks;
+    const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
+    for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
+    if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
+    // exclusive prefix of the per-chunk candidate counts
+    int total = 0;
+    for (int base = 0; base < n_act; base += 256) {
+      const int c = base + threadIdx.x;
+      const int v = c < n_act ? ccnt[c] : 0;
+      int sum;
+      const int ex = total + block_excl_scan(v, red[0], &sum);
+      if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
+      total += sum;
     }
     __syncthreads();
-  }
-  auto cand = [&](int g, int* chunk) -> uint32_t {
+    const int n_cand = total;
+    const bool staged = n_cand <= kLdsCand;
     if (staged) {
-      *chunk = lchunk[g];
-      return lkey[g];
+      // eight independent loads in flight per thread
+      for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
+        uint32_t kv[8];
+        int cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int g = g0 + 256 * u;
+          cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
+          kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int g = g0 + 256 * u;
+          if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
+        }
+      }
+      __syncthreads();
     }
-    const int c = chunk_of(pref, n_act, g);
-    *chunk = c;
-    return ck[(int64_t)c * kChunk + (g - pref[c])];
-  };
-  uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
-  uint32_t k = (uint32_t)st.k_rem;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    for (int i = threadIdx.x; i < 1024; i += 256) bins[i] = 0;
-    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
-    __syncthreads();
+    auto cand = [&](int g, int* chunk) -> uint32_t {
+      if (staged) {
+        *chunk = lchunk[g];
+        return lkey[g];
+      }
+      const int c = chunk_of(pref, n_act, g);
+      *chunk = c;
+      return ck[(int64_t)c * kChunk + (g - pref[c])];
+    };
+    // radix select of the k_rem-th largest candidate: bits 19..10, then 9..0
+    uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
+    uint32_t k = (uint32_t)st.k_rem;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      for (int g = threadIdx.x; g < n_cand; g += 256) {
+        int c;
+        const uint32_t key = cand(g, &c);
+        if ((key & mask) == prefix) atomicAdd(&bins[pass][(key >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      uint32_t v[4];
+      my_buckets(bins[pass], v);
+      bucket_search(v, k, &s_digit[pass], &s_kin[pass]);
+      prefix |= s_digit[pass] << shift;
+      mask |= 1023u << shift;
+      k = s_kin[pass];
+    }
+    const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
     for (int g = threadIdx.x; g < n_cand; g += 256) {
       int c;
       const uint32_t key = cand(g, &c);
-      if ((key & mask) == prefix) atomicAdd(&bins[(key >> shift) & 1023u], 1u);
+      if (key > T) atomicAdd(&cgt[c], 1);
+      else if (key == T) atomicAdd(&ceq[c], 1);
     }
     __syncthreads();
-    bucket_search(bins, 1024, k, &s_digit, &s_kin);
-    prefix |= s_digit << shift;
-    mask |= 1023u << shift;
-    k = s_kin;
-  }
-  const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
-  for (int g = threadIdx.x; g < n_cand; g += 256) {
-    int c;
-    const uint32_t key = cand(g, &c);
-    if (key > T) atomicAdd(&cgt[c], 1);
-    else if (key == T) atomicAdd(&ceq[c], 1);
-  }
-  __syncthreads();
-  // exclusive prefixes over chunks, 256 chunks per round
-  int sel_acc = 0, eq_acc = 0;
-  const int* above = a.chunk_above + (int64_t)q * a.n_chunks;
-  for (int base = 0; base < n_act; base += 256) {
-    const int c = base + threadIdx.x;
-    const bool in = c < n_act;
-    const int neq = in ? ceq[c] : 0;
-    const int eq_ex = eq_acc + block_excl_scan(neq, red);
-    int take = (int)k - eq_ex;
-    take = take < 0 ? 0 : (take > neq ? neq : take);
-    const int nsel = in ? above[c] + cgt[c] + take : 0;
-    const int sel_ex = sel_acc + block_excl_scan(nsel, red);
-    if (in) {
-      a.chunk_sel[(int64_t)q * a.n_chunks + c] = sel_ex;
-      a.chunk_eq[(int64_t)q * a.n_chunks + c] = eq_ex;
+    // exclusive prefixes over chunks, 256 chunks per round
+    int sel_acc = 0, eq_acc = 0;
+    for (int base = 0; base < n_act; base += 256) {
+      const int c = base + threadIdx.x;
+      const bool in = c < n_act;
+      const int above_c = in ? above[c] : 0;
+      const int neq = in ? ceq[c] : 0;
+      int eq_sum, sel_sum;
+      const int eq_ex = eq_acc + block_excl_scan(neq, red[1], &eq_sum);
+      int take = (int)k - eq_ex;
+      take = take < 0 ? 0 : (take > neq ? neq : take);
+      const int nsel = in ? above_c + cgt[c] + take : 0;
+      const int sel_ex = sel_acc + block_excl_scan(nsel, red[2], &sel_sum);
+      if (in) {
+        a.chunk_sel[(int64_t)q * a.n_chunks + c] = sel_ex;
+        a.chunk_eq[(int64_t)q * a.n_chunks + c] = eq_ex;
+      }
+      sel_acc += sel_sum;
+      eq_acc += eq_sum;
     }
-    sel_acc += block_sum_int(nsel, red);
-    eq_acc += block_sum_int(neq, red);
+    if (threadIdx.x == 0) {
+      TopkState ns = st;
+      ns.T = T;
+      ns.k_eq = (int)k;
+      a.state[q] = ns;
+    }
   }
-  if (threadIdx.x == 0) {
-    TopkState ns = st;
-    ns.T = T;
-    ns.k_eq = (int)k;
-    a.state[q] = ns;
-  }
+  // leave the first-digit histogram zeroed for the next call (nothing after
+  // the scoring kernel of this call reads it past collect)
+  uint32_t* gh = a.hist + (int64_t)q * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += 256) gh[i] = 0;
 }
 
 // Per chunk: keys above the first-digit bucket are counted, keys inside it go
@@ -454,20 +480,27 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
     return;
   }
   if (c0 >= n_vis) return;
+  // this chunk's scores are requested first: they do not depend on the search
+  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  float sv[kChunk / 256];
+#pragma unroll
+  for (int j = 0; j < kChunk / 256; ++j) {
+    const int64_t i = c0 + j * 256 + threadIdx.x;
+    sv[j] = i < n_vis ? sc[i] : 0.f;
+  }
   // every workgroup finds the first-digit bucket of the k-th largest score
-  __shared__ uint32_t lbins[kBins1];
   __shared__ uint32_t s_digit, s_kin;
-  const uint32_t* gh = a.hist + (int64_t)q * kBins1;
-  for (int i = threadIdx.x; i < kBins1; i += 256) lbins[i] = gh[i];
   if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
-  __syncthreads();
-  bucket_search(lbins, kBins1, (uint32_t)a.top_k, &s_digit, &s_kin);
+  {
+    uint32_t v[kBins1 / 256];
+    my_buckets(a.hist + (int64_t)q * kBins1, v);
+    bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
+  }
   TopkState st = {};
   st.n_vis = n_vis;
   st.b1 = s_digit;
   st.k_rem = (int)s_kin;
   if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
   uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
   int above = 0;
   uint32_t want = 0;
@@ -476,17 +509,17 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   for (int j = 0; j < kChunk / 256; ++j) {
     const int64_t i = c0 + j * 256 + threadIdx.x;
     const bool in = i < st.n_vis;
-    keys[j] = in ? order_key(sc[i]) : 0u;
+    keys[j] = in ? order_key(sv[j]) : 0u;
     const uint32_t d1 = keys[j] >> kShift1;
     above += (in && d1 > st.b1) ? 1 : 0;
     want |= (uint32_t)(in && d1 == st.b1) << j;
   }
   __shared__ int red[4];
-  int slot = block_excl_scan(__popc(want), red);
+  int n_here;
+  int slot = block_excl_scan(__popc(want), red, &n_here);
 #pragma unroll
   for (int j = 0; j < kChunk / 256; ++j)
     if (want >> j & 1u) ck[slot++] = keys[j];
-  const int n_here = block_sum_int(__popc(want), red);
   above = block_sum_int(above, red);
   if (threadIdx.x == 0) {
     a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = above;
@@ -503,6 +536,22 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
   int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
+  // this thread's 16 scores, requested together with the state (bounded by
+  // the capacity only, so the loads do not wait for the state)
+  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  const int64_t e0 = c0 + threadIdx.x * 16;
+  float sv[16];
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    const int64_t i = e0 + j;
+    if (i + 3 < a.n_cap && (((uintptr_t)(sc + i)) & 15) == 0) {
+      const f32x4 x = *(const f32x4*)(sc + i);
+      sv[j] = x[0]; sv[j + 1] = x[1]; sv[j + 2] = x[2]; sv[j + 3] = x[3];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
+    }
+  }
   if (st.k_rem < 0) {
     // every visible entry, in order; chunk 0 also writes the padding
     for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
@@ -513,27 +562,13 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
   if (c0 >= st.n_vis) return;
   const int sel_before = a.chunk_sel[(int64_t)q * a.n_chunks + chunk];
   const int eq_before = a.chunk_eq[(int64_t)q * a.n_chunks + chunk];
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
-  const int64_t e0 = c0 + threadIdx.x * 16;
   uint32_t gtmask = 0, eqmask = 0;
 #pragma unroll
-  for (int j = 0; j < 16; j += 4) {
-    const int64_t i = e0 + j;
-    float v[4];
-    if (i + 3 < st.n_vis && (((uintptr_t)(sc + i)) & 15) == 0) {
-      const f32x4 x = *(const f32x4*)(sc + i);
-      v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = i + u < st.n_vis ? sc[i + u] : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (i + u < st.n_vis) {
-        const uint32_t k = order_key(v[u]);
-        gtmask |= (uint32_t)(k > st.T) << (j + u);
-        eqmask |= (uint32_t)(k == st.T) << (j + u);
-      }
+  for (int j = 0; j < 16; ++j) {
+    if (e0 + j < st.n_vis) {
+      const uint32_t k = order_key(sv[j]);
+      gtmask |= (uint32_t)(k > st.T) << j;
+      eqmask |= (uint32_t)(k == st.T) << j;
     }
   }
   __shared__ int wsum[4];
