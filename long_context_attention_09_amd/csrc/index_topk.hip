@@ -19,16 +19,17 @@
 // score's order key for the first radix-select pass.
 //
 // Top-k over the 32-bit order keys of the scores.  The scoring kernel builds a
-// histogram of the top 12 key bits, then three small kernels follow:
-//   collect finds (in every workgroup) the bucket holding the k-th key, counts,
-//           per 4096-score chunk, the keys above that bucket and appends the
-//           keys inside it to the chunk's region of the candidate list;
-//   refine  (one workgroup per query) radix-selects the k-th key T among the
-//           candidates (10 + 10 more bits) and turns per-chunk counts into the
-//           output offset of every chunk;
-//   write   emits every chunk's selected indices at its offset, in index
-//           order, so the output is ascending; among keys equal to T the
-//           lowest indices are taken.
+// histogram of the top 12 key bits, then two kernels follow, one workgroup
+// per 4096-score chunk and query:
+//   collect finds (in every workgroup) the bucket holding the k-th key, counts
+//           the chunk's keys above that bucket and copies the keys inside it
+//           to the chunk's region of the candidate list;
+//   select  (every workgroup again) radix-selects the k-th key T among the
+//           query's candidates (10 + 10 more bits), derives from the
+//           per-chunk counts where its chunk's selection starts in the
+//           output, and emits the chunk's selected indices in index order,
+//           so the output is ascending; among keys equal to T the lowest
+//           indices are taken.
 // Histograms use integer atomics only and candidate lists are compacted per
 // chunk by block scans, so the result does not depend on any ordering and is
 // deterministic.  The histogram is left zeroed by every call.  Kernel
@@ -340,128 +341,8 @@ __device__ __forceinline__ int chunk_of(const int* pref, int n_act, int g) {
   return lo;
 }
 
-constexpr int kLdsCand = 8192;   // candidates the refine kernel stages in LDS
+constexpr int kLdsCand = 8192;   // candidates the select kernel stages in LDS
 
-// One workgroup per query: radix-select the k_rem-th largest key among the
-// candidates (bits 19..10, then 9..0), then per-chunk output offsets.  Up to
-// kLdsCand candidates are staged in LDS with their chunk; more are re-read
-// from the workspace on every pass.
-__global__ void __launch_bounds__(256) topk_refine_kernel(IndexLaunch a) {
-  const int q = blockIdx.x;
-  const TopkState st = a.state[q];
-  __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
-  __shared__ int pref[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
-  __shared__ uint32_t lkey[kLdsCand];
-  __shared__ uint16_t lchunk[kLdsCand];
-  __shared__ uint32_t s_digit[2], s_kin[2];
-  __shared__ int red[4][4];
-  if (st.k_rem > 0) {
-    const int n_act = (st.n_vis + kChunk - 1) / kChunk;
-    const int* ccnt = a.chunk_cand + (int64_t)q * a.n_chunks;
-    const int* above = a.chunk_above + (int64_t)q * a.n_chunks;
-    const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
-    for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
-    if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
-    // exclusive prefix of the per-chunk candidate counts
-    int total = 0;
-    for (int base = 0; base < n_act; base += 256) {
-      const int c = base + threadIdx.x;
-      const int v = c < n_act ? ccnt[c] : 0;
-      int sum;
-      const int ex = total + block_excl_scan(v, red[0], &sum);
-      if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
-      total += sum;
-    }
-    __syncthreads();
-    const int n_cand = total;
-    const bool staged = n_cand <= kLdsCand;
-    if (staged) {
-      // eight independent loads in flight per thread
-      for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
-        uint32_t kv[8];
-        int cv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int g = g0 + 256 * u;
-          cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
-          kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int g = g0 + 256 * u;
-          if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
-        }
-      }
-      __syncthreads();
-    }
-    auto cand = [&](int g, int* chunk) -> uint32_t {
-      if (staged) {
-        *chunk = lchunk[g];
-        return lkey[g];
-      }
-      const int c = chunk_of(pref, n_act, g);
-      *chunk = c;
-      return ck[(int64_t)c * kChunk + (g - pref[c])];
-    };
-    // radix select of the k_rem-th largest candidate: bits 19..10, then 9..0
-    uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
-    uint32_t k = (uint32_t)st.k_rem;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 10 : 0;
-      for (int g = threadIdx.x; g < n_cand; g += 256) {
-        int c;
-        const uint32_t key = cand(g, &c);
-        if ((key & mask) == prefix) atomicAdd(&bins[pass][(key >> shift) & 1023u], 1u);
-      }
-      __syncthreads();
-      uint32_t v[4];
-      my_buckets(bins[pass], v);
-      bucket_search(v, k, &s_digit[pass], &s_kin[pass]);
-      prefix |= s_digit[pass] << shift;
-      mask |= 1023u << shift;
-      k = s_kin[pass];
-    }
-    const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
-    for (int g = threadIdx.x; g < n_cand; g += 256) {
-      int c;
-      const uint32_t key = cand(g, &c);
-      if (key > T) atomicAdd(&cgt[c], 1);
-      else if (key == T) atomicAdd(&ceq[c], 1);
-    }
-    __syncthreads();
-    // exclusive prefixes over chunks, 256 chunks per round
-    int sel_acc = 0, eq_acc = 0;
-    for (int base = 0; base < n_act; base += 256) {
-      const int c = base + threadIdx.x;
-      const bool in = c < n_act;
-      const int above_c = in ? above[c] : 0;
-      const int neq = in ? ceq[c] : 0;
-      int eq_sum, sel_sum;
-      const int eq_ex = eq_acc + block_excl_scan(neq, red[1], &eq_sum);
-      int take = (int)k - eq_ex;
-      take = take < 0 ? 0 : (take > neq ? neq : take);
-      const int nsel = in ? above_c + cgt[c] + take : 0;
-      const int sel_ex = sel_acc + block_excl_scan(nsel, red[2], &sel_sum);
-      if (in) {
-        a.chunk_sel[(int64_t)q * a.n_chunks + c] = sel_ex;
-        a.chunk_eq[(int64_t)q * a.n_chunks + c] = eq_ex;
-      }
-      sel_acc += sel_sum;
-      eq_acc += eq_sum;
-    }
-    if (threadIdx.x == 0) {
-      TopkState ns = st;
-      ns.T = T;
-      ns.k_eq = (int)k;
-      a.state[q] = ns;
-    }
-  }
-  // leave the first-digit histogram zeroed for the next call (nothing after
-  // the scoring kernel of this call reads it past collect)
-  uint32_t* gh = a.hist + (int64_t)q * kBins1;
-  for (int i = threadIdx.x; i < kBins1; i += 256) gh[i] = 0;
-}
 
 // Per chunk: keys above the first-digit bucket are counted, keys inside it go
 // to the chunk's own region of the query's candidate list (no global atomics).
@@ -527,17 +408,22 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   }
 }
 
-// Emit the selected indices of one chunk at their rank among all selected
-// indices (ascending index order), and the -1 padding.
-__global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
+// Selection, one workgroup per (chunk, query).  Every workgroup of a query
+// repeats the same small computation over the query's candidates (the keys in
+// the first-digit bucket, a few hundred in practice): radix-select the
+// k_rem-th largest of them (bits 19..10, then 9..0) to get the k-th largest
+// key T and how many keys equal to T are taken (lowest indices first), count
+// per chunk the candidates above and at T, and from those counts and the
+// chunks' counts above the bucket derive where this chunk's selection starts
+// in the output.  It then emits its selected indices in index order.  Up to
+// kLdsCand candidates are staged in LDS; more are re-read from the workspace.
+__global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   const int q = blockIdx.y;
   const int b = q / a.n_qb, r = q % a.n_qb;
-  const TopkState st = a.state[q];
-  int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
-  // this thread's 16 scores, requested together with the state (bounded by
-  // the capacity only, so the loads do not wait for the state)
+  // independent loads first: this thread's 16 scores (bounded by the
+  // capacity only), the state, and every chunk's counts
   const float* sc = a.scores + (int64_t)q * a.n_cap;
   const int64_t e0 = c0 + threadIdx.x * 16;
   float sv[16];
@@ -552,6 +438,26 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
       for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
     }
   }
+  const TopkState st = a.state[q];
+  constexpr int kCPT = kMaxChunks / 256;       // chunks per thread
+  int ccnt[kCPT], cabv[kCPT];
+  {
+    const int* cc = a.chunk_cand + (int64_t)q * a.n_chunks;
+    const int* ca = a.chunk_above + (int64_t)q * a.n_chunks;
+#pragma unroll
+    for (int j = 0; j < kCPT; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      ccnt[j] = c < a.n_chunks ? cc[c] : 0;
+      cabv[j] = c < a.n_chunks ? ca[c] : 0;
+    }
+  }
+  // leave the first-digit histogram zeroed for the next call (collect, its
+  // only reader, has finished)
+  {
+    uint32_t* gh = a.hist + (int64_t)q * kBins1;
+    for (int i = chunk * 256 + threadIdx.x; i < kBins1; i += a.n_chunks * 256) gh[i] = 0;
+  }
+  int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
   if (st.k_rem < 0) {
     // every visible entry, in order; chunk 0 also writes the padding
     for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
@@ -560,24 +466,125 @@ __global__ void __launch_bounds__(256) topk_write_kernel(IndexLaunch a) {
     return;
   }
   if (c0 >= st.n_vis) return;
-  const int sel_before = a.chunk_sel[(int64_t)q * a.n_chunks + chunk];
-  const int eq_before = a.chunk_eq[(int64_t)q * a.n_chunks + chunk];
+
+  __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
+  __shared__ int pref[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
+  __shared__ uint32_t lkey[kLdsCand];
+  __shared__ uint16_t lchunk[kLdsCand];
+  __shared__ uint32_t s_digit[2], s_kin[2];
+  __shared__ int red[4][4];
+  const int n_act = (st.n_vis + kChunk - 1) / kChunk;
+  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
+  for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
+  if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
+  // exclusive prefix of the per-chunk candidate counts
+  int n_cand = 0;
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    if (256 * j >= n_act) break;
+    const int c = threadIdx.x + 256 * j;
+    const int v = c < n_act ? ccnt[j] : 0;
+    int sum;
+    const int ex = n_cand + block_excl_scan(v, red[0], &sum);
+    if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
+    n_cand += sum;
+  }
+  __syncthreads();
+  const bool staged = n_cand <= kLdsCand;
+  if (staged) {
+    // eight independent loads in flight per thread
+    for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
+      uint32_t kv[8];
+      int cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = g0 + 256 * u;
+        cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
+        kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = g0 + 256 * u;
+        if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
+      }
+    }
+    __syncthreads();
+  }
+  auto cand = [&](int g, int* c_of) -> uint32_t {
+    if (staged) {
+      *c_of = lchunk[g];
+      return lkey[g];
+    }
+    const int c = chunk_of(pref, n_act, g);
+    *c_of = c;
+    return ck[(int64_t)c * kChunk + (g - pref[c])];
+  };
+  // radix select of the k_rem-th largest candidate: bits 19..10, then 9..0
+  uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
+  uint32_t k = (uint32_t)st.k_rem;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    for (int g = threadIdx.x; g < n_cand; g += 256) {
+      int c;
+      const uint32_t key = cand(g, &c);
+      if ((key & mask) == prefix) atomicAdd(&bins[pass][(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    uint32_t v[4];
+    my_buckets(bins[pass], v);
+    bucket_search(v, k, &s_digit[pass], &s_kin[pass]);
+    prefix |= s_digit[pass] << shift;
+    mask |= 1023u << shift;
+    k = s_kin[pass];
+  }
+  const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
+  for (int g = threadIdx.x; g < n_cand; g += 256) {
+    int c;
+    const uint32_t key = cand(g, &c);
+    if (key > T) atomicAdd(&cgt[c], 1);
+    else if (key == T) atomicAdd(&ceq[c], 1);
+  }
+  __syncthreads();
+  // this chunk's output start: the selection of every earlier chunk (above
+  // the bucket, above T, and its share of the keys equal to T)
+  int sel_before = 0, eq_before = 0;
+  {
+    int eq_acc = 0, sel_part = 0;
+#pragma unroll
+    for (int j = 0; j < kCPT; ++j) {
+      if (256 * j >= n_act) break;
+      const int c = threadIdx.x + 256 * j;
+      const bool in = c < n_act;
+      const int neq = in ? ceq[c] : 0;
+      int eq_sum;
+      const int eq_ex = eq_acc + block_excl_scan(neq, red[1], &eq_sum);
+      int take = (int)k - eq_ex;
+      take = take < 0 ? 0 : (take > neq ? neq : take);
+      if (c < chunk) sel_part += cabv[j] + cgt[c] + take;
+      if (c == chunk) eq_before = eq_ex;
+      eq_acc += eq_sum;
+    }
+    __shared__ int s_eqb;
+    if (chunk % 256 == threadIdx.x) s_eqb = eq_before;
+    sel_before = block_sum_int(sel_part, red[2]);
+    eq_before = s_eqb;
+  }
   uint32_t gtmask = 0, eqmask = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (e0 + j < st.n_vis) {
-      const uint32_t k = order_key(sv[j]);
-      gtmask |= (uint32_t)(k > st.T) << j;
-      eqmask |= (uint32_t)(k == st.T) << j;
+      const uint32_t key = order_key(sv[j]);
+      gtmask |= (uint32_t)(key > T) << j;
+      eqmask |= (uint32_t)(key == T) << j;
     }
   }
-  __shared__ int wsum[4];
-  const int eq_excl = eq_before + block_excl_scan(__popc(eqmask), wsum);
-  int can = st.k_eq - eq_excl;                // equal keys this thread may still take
+  const int eq_excl = eq_before + block_excl_scan(__popc(eqmask), red[3]);
+  int can = (int)k - eq_excl;                 // equal keys this thread may still take
   uint32_t selmask = gtmask;
   for (int j = 0; j < 16 && can > 0; ++j)
     if (eqmask >> j & 1u) { selmask |= 1u << j; --can; }
-  int pos = sel_before + block_excl_scan(__popc(selmask), wsum);
+  int pos = sel_before + block_excl_scan(__popc(selmask), red[0]);
   for (int j = 0; j < 16; ++j)
     if ((selmask >> j & 1u) && pos < a.top_k) out[pos++] = (int32_t)(e0 + j);
 }
@@ -610,8 +617,7 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   }
   dim3 g2(a.n_chunks, nq);
   topk_collect_kernel<<<g2, 256, 0, s>>>(a);
-  topk_refine_kernel<<<nq, 256, 0, s>>>(a);
-  topk_write_kernel<<<g2, 256, 0, s>>>(a);
+  topk_select_kernel<<<g2, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -29,9 +29,7 @@ struct TopkState {
   uint32_t b1;        // 12-bit bucket (key >> 20) holding the k-th largest key
   int32_t k_rem;      // how many to take inside bucket b1 (-1: every visible entry)
   int32_t n_vis;      // visible entries of the query
-  uint32_t T;         // the k-th largest order key
-  int32_t k_eq;       // keys equal to T to take, lowest index first
-  int32_t pad[3];
+  int32_t pad[5];
 };
 
 struct IndexLaunch {
@@ -54,9 +52,7 @@ struct IndexLaunch {
   TopkState* state;          // [B * n_qb]
   uint32_t* cand_key;        // [B * n_qb][n_cap]: chunk c's candidates at [c * 4096, ...)
   int32_t* chunk_cand;       // [B * n_qb][n_chunks] candidates per chunk
-  int32_t* chunk_above;      // [B * n_qb][n_chunks]
-  int32_t* chunk_sel;        // [B * n_qb][n_chunks] selected before the chunk
-  int32_t* chunk_eq;         // [B * n_qb][n_chunks] keys equal to T before the chunk
+  int32_t* chunk_above;      // [B * n_qb][n_chunks] scores above the first-digit bucket
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
