@@ -111,33 +111,23 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kDHalf = kD / 2;
+constexpr int kTileBytes = kTile * kRowBytes;             // one BF16 tile in LDS
 
-// Raw-row ring: tiles travel from HBM straight into LDS (global_load_lds,
-// 16 bytes per lane) kRing - 1 tiles ahead of the one in use, so several
-// tiles' worth of loads are in flight per workgroup without holding registers.
-constexpr int kRing = 4;                                  // raw tile slots
-constexpr int kRawRow = kDN + kDR * 2;                    // 576 bytes as stored
-constexpr int kSlotBytes = kTile * kRawRow;               // 18432 = 18 wave loads of 1 KiB
-constexpr int kTileLoads = kSlotBytes / 1024;             // 18: waves 0, 1 issue 3, the others 2
+// Row loads: thread t owns the sixteen-byte chunks t, t + 512, t + 1024 of a
+// tile (chunk c = row c / 36, part c % 36: parts 0..27 hold FP8 dims, 28..35
+// BF16 RoPE dims) and keeps kStages tiles of them in flight in registers.
+constexpr int kChunkSlots = (kChunksPerTile + kThreads - 1) / kThreads;   // 3
+constexpr int kStages = 3;
 constexpr int kAddrSlots = 8;                             // row-address ring (tiles)
 constexpr int kIdxMax = kAttendIdxMax;                    // selected indices staged per split
-
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void gbl_void;
-
-// Byte address inside LDS of a pointer to shared memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-constexpr int waitcnt_vm_lgkm0(int n) { return waitcnt_vm(n) & kWaitLgkm0; }
 
-// Workgroup barrier without the full memory fence of __syncthreads: the
-// caller states which counters to drain first, so ring loads stay in flight.
+// Workgroup barrier that waits for this wave's LDS traffic only: the row
+// loads in flight into registers stay in flight (a __syncthreads fence would
+// drain them).
 #define ATTEND_BARRIER(waitimm)                  \
   do {                                           \
     __builtin_amdgcn_s_waitcnt(waitimm);         \
@@ -147,14 +137,11 @@ constexpr int waitcnt_vm_lgkm0(int n) { return waitcnt_vm(n) & kWaitLgkm0; }
   } while (0)
 
 __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
-  // Separate LDS objects, so the compiler can tell reads of the BF16 tile
-  // from the ring's in-flight loads (it then leaves those loads in flight).
-  __shared__ __attribute__((aligned(16))) uint8_t raw[kRing * kSlotBytes];   // raw tile slots
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kRowBytes];   // BF16 rows
-  __shared__ __attribute__((aligned(16))) float xch[kWaves * 64 * 8];        // score halves
-  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                          // [slot][nope|rope][row]
-  __shared__ float rope_cs[64];                                              // cos, sin at t
-  __shared__ int lidx[kIdxMax];                                              // staged indices (CSA)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // BF16 rows, two buffers
+  __shared__ __attribute__((aligned(16))) float xch[kWaves * 64 * 8];    // score halves
+  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                      // [slot][nope|rope][row]
+  __shared__ float rope_cs[64];                                          // cos, sin at t
+  __shared__ int lidx[kIdxMax];                                          // staged indices (CSA)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,36 +203,64 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     }
   };
 #pragma unroll
-  for (int t = 0; t < kRing; ++t) tile_addrs(t);
+  for (int t = 0; t < kStages + 2; ++t) tile_addrs(t);
   __syncthreads();
 
-  // Loader: load i of wave w moves 1 KiB block j = w + 8i of the tile; lane
-  // `lane` carries sixteen-byte chunk c = 64j + lane (row c / 36, part c % 36:
-  // parts 0..27 are the FP8 bytes, 28..35 the BF16 RoPE dims) to byte 16c of
-  // the slot, so a slot holds the tile's rows back to back as stored.  Masked
-  // rows read harmless bytes (the query) and are zeroed at conversion.
-  const int n_loads = wave < kTileLoads - 2 * kWaves ? 3 : 2;   // waves 0, 1 carry blocks 16, 17
-  int ld_row[3], ld_off[3];
-  bool ld_rope[3];
+  // this thread's chunks of a tile
+  int ch_row[kChunkSlots], ch_src[kChunkSlots], ch_dst[kChunkSlots];
+  bool ch_ok[kChunkSlots], ch_rope[kChunkSlots];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int c = (wave + kWaves * i) * 64 + lane;
-    const int part = c % kChunksPerRow;
-    ld_row[i] = c < kChunksPerTile ? c / kChunksPerRow : 0;
-    ld_rope[i] = part >= 28;
-    ld_off[i] = part < 28 ? part * 16 : (part - 28) * 16;
+  for (int k = 0; k < kChunkSlots; ++k) {
+    const int c = tid + kThreads * k;
+    ch_ok[k] = c < kChunksPerTile;
+    const int cc = ch_ok[k] ? c : 0;
+    const int part = cc % kChunksPerRow;
+    ch_row[k] = cc / kChunksPerRow;
+    ch_rope[k] = part >= 28;
+    ch_src[k] = part < 28 ? part * 16 : (part - 28) * 16;
+    ch_dst[k] = ch_row[k] * kRowBytes + (part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16);
   }
+  // Request tile t's chunks into registers.  Every load is issued (a masked
+  // row or a missing chunk reads harmless bytes: the query) so the count of
+  // loads in flight is the same on every path; bit k of the result says
+  // whether chunk k is real data.
   const uint64_t dummy = (uint64_t)a.q;      // any readable bytes (q holds >= 16 KiB)
-  auto issue = [&](int t) {
+  auto fetch = [&](int t, i32x4 (&v)[kChunkSlots]) {
     const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
-    uint8_t* dst = raw + (t % kRing) * kSlotBytes;
+    int live = 0;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      if (i < n_loads) {
-        const uint64_t base = slot_a[(ld_rope[i] ? kTile : 0) + ld_row[i]];
-        const uint64_t src = (base ? base : dummy) + (uint64_t)ld_off[i];
-        __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + (wave + kWaves * i) * 1024),
-                                         16, 0, 0);
+    for (int k = 0; k < kChunkSlots; ++k) {
+      const uint64_t base = ch_ok[k] ? slot_a[(ch_rope[k] ? kTile : 0) + ch_row[k]] : 0;
+      live |= (base != 0) << k;
+      v[k] = *(gbl_i32x4*)((base ? base : dummy) + (uint64_t)ch_src[k]);
+    }
+    return live;
+  };
+  // Widen tile t's chunks to BF16 rows in buffer t % 2 (FP8 dims exactly;
+  // zeros for masked rows).
+  auto commit = [&](int t, const i32x4 (&vin)[kChunkSlots], int live) {
+    uint8_t* tile = tiles + (t & 1) * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < kChunkSlots; ++k) {
+      if (!ch_ok[k]) continue;
+      const i32x4 zero = {0, 0, 0, 0};
+      const i32x4 vk = (live >> k) & 1 ? vin[k] : zero;
+      const i32x4 v[1] = {vk};
+      uint8_t* dst = tile + ch_dst[k];
+      if (!ch_rope[k]) {
+        // two E4M3 bytes -> two BF16 per instruction (scale 1: exact)
+        i32x4 lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[0][j], 1.0f, false));
+          const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[0][j], 1.0f, true));
+          if (j < 2) { lo[2 * j] = w0; lo[2 * j + 1] = w1; }
+          else { hi[2 * (j - 2)] = w0; hi[2 * (j - 2) + 1] = w1; }
+        }
+        *(i32x4*)dst = lo;
+        *(i32x4*)(dst + 16) = hi;
+      } else {
+        *(i32x4*)dst = v[0];
       }
     }
   };
@@ -296,11 +311,6 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
       for (int j = 0; j < 8; ++j) qv[kb][j] = u16_as_bf16(f32_to_bf16(x[kb][j]));
   }
 
-  // first kRing - 1 tiles in flight (the q loads above have been consumed, so
-  // from here on the vector-memory counter tracks only the ring)
-#pragma unroll
-  for (int t = 0; t < kRing - 1; ++t) issue(t);
-
   f32x4 acc_o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -309,92 +319,50 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   float* xmine = xch + (wave * 64 + lane) * 8;
   const float* xpart = xch + ((wave ^ 4) * 64 + lane) * 8;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    // keep the ring full: tile t + 3 goes into the slot tile t - 1 used
-    // (always issued, so the count of loads in flight is the same every
-    // iteration; past the list the rows are masked and read harmless bytes)
-    issue(t + kRing - 1);
-    tile_addrs(t + kRing);
-    // this wave's loads of tile t are done once at most (kRing - 1) tiles' remain
-    if (n_loads == 3) ATTEND_BARRIER(waitcnt_vm_lgkm0((kRing - 1) * 3));
-    else ATTEND_BARRIER(waitcnt_vm_lgkm0((kRing - 1) * 2));
-
-    // widen tile t to BF16 rows (zeros for masked rows)
-    {
-      const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
-      // The slot is read with the wait written out: the loads that fill it
-      // are counted by hand above, and a plain LDS read here would make the
-      // compiler drain every load in flight, the other slots' included.
-      i32x4 vin[3];
-      {
-        const uint32_t base = lds_addr(raw) + (uint32_t)((t % kRing) * kSlotBytes);
-        uint32_t ad[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const int c = tid + kThreads * k;
-          ad[k] = base + (uint32_t)((c < kChunksPerTile ? c : 0) * 16);
-        }
-        __asm__ __volatile__(
-            "ds_read_b128 %0, %3\n\t"
-            "ds_read_b128 %1, %4\n\t"
-            "ds_read_b128 %2, %5\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(vin[0]), "=&v"(vin[1]), "=&v"(vin[2])
-            : "v"(ad[0]), "v"(ad[1]), "v"(ad[2])
-            : "memory");
-      }
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int c = tid + kThreads * k;
-        if (c < kChunksPerTile) {
-          const int row = c / kChunksPerRow, part = c % kChunksPerRow;
-          const bool live = slot_a[row] != 0;
-          const i32x4 v = vin[k];
-          uint8_t* dst = tile + row * kRowBytes;
-          if (part < 28) {
-            i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-            if (live) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[j], false);
-                const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[j], true);
-                const uint32_t w0 = pack_hi16(f01[0], f01[1]);
-                const uint32_t w1 = pack_hi16(f23[0], f23[1]);
-                if (j < 2) { lo[2 * j] = (int)w0; lo[2 * j + 1] = (int)w1; }
-                else { hi[2 * (j - 2)] = (int)w0; hi[2 * (j - 2) + 1] = (int)w1; }
-              }
-            }
-            *(i32x4*)(dst + part * 32) = lo;
-            *(i32x4*)(dst + part * 32 + 16) = hi;
-          } else {
-            *(i32x4*)(dst + kDN * 2 + (part - 28) * 16) = live ? v : (i32x4){0, 0, 0, 0};
-          }
-        }
-      }
-    }
+  // One tile of work.  Barriers:
+  //   A: tile t's BF16 rows are written (by every wave) and buffer (t+1) % 2
+  //      is free again;
+  //   B: the score halves are exchanged.
+  // Between A and B the scores of tile t are formed and tile t+1 (fetched
+  // kStages - 1 tiles ago) is widened into the other buffer; its register
+  // slot then fetches tile t + 1 + kStages.  After B: softmax and O += V P.
+  auto step = [&](int t, i32x4 (&cur)[kChunkSlots], int& cur_live, bool active) {
     ATTEND_BARRIER(kWaitLgkm0);
+    const uint8_t* tile = tiles + (t & 1) * kTileBytes;
     const uint64_t* vrow = rowa + (t % kAddrSlots) * 2 * kTile;   // masked rows have address 0
 
-    // partial S^T = K Q^T over this wave's 256 dims: two 16-entry blocks,
-    // each split over two accumulators
-    f32x4 s[2];
+    // partial S^T = K Q^T over this wave's 256 dims: every K fragment is
+    // requested first, then two 16-entry blocks over two accumulators each
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+      bf16x8 kf[2][8];
 #pragma unroll
-    for (int eb = 0; eb < 2; ++eb) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + kDHalf * 2 * dh + 16 * g;
+      for (int eb = 0; eb < 2; ++eb) {
+        const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + kDHalf * 2 * dh + 16 * g;
 #pragma unroll
-      for (int kb = 0; kb < 8; kb += 2) {
-        const bf16x8 k0 = *(const bf16x8*)(krow + 64 * kb);
-        const bf16x8 k1 = *(const bf16x8*)(krow + 64 * (kb + 1));
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qv[kb], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qv[kb + 1], s1, 0, 0, 0);
+        for (int kb = 0; kb < 8; ++kb) kf[eb][kb] = *(const bf16x8*)(krow + 64 * kb);
       }
-      s[eb] = s0 + s1;
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; kb += 2) {
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[eb][kb], qv[kb], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[eb][kb + 1], qv[kb + 1], s1, 0, 0, 0);
+        }
+        s[eb] = s0 + s1;
+      }
     }
     // swap halves with the partner wave (same heads, other dims)
     *(f32x4*)xmine = s[0];
     *(f32x4*)(xmine + 4) = s[1];
+    // widen tile t+1 while the matrix cores work, then reuse its registers
+    // (past the list the tiles are all masked and widen to zeros)
+    commit(t + 1, cur, cur_live);
+    tile_addrs(t + kStages + 2);
+    cur_live = fetch(t + 1 + kStages, cur);
     ATTEND_BARRIER(kWaitLgkm0);
+    if (!active) return;
     {
       const f32x4 o0 = *(const f32x4*)xpart, o1 = *(const f32x4*)(xpart + 4);
       // the same sum in both waves (a + b == b + a), so both run the same softmax
@@ -417,16 +385,17 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     // so the O rescale below is rare; probabilities stay below 2^slack
     const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // arguments are at most the slack (8), or -inf for masked rows
+    const float alpha = fast_exp2(m_run - m_use);
     bf16x8 pv;
     float psum = 0.f;
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[eb][i] - m_use);
+        const float p = fast_exp2(s[eb][i] - m_use);
         psum += p;
-        pv[eb * 4 + i] = u16_as_bf16(f32_to_bf16(p));
+        pv[eb * 4 + i] = (__bf16)p;          // round to nearest even
       }
     if (__any(alpha != 1.0f)) {
       l_part *= alpha;
@@ -436,23 +405,53 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     l_part += psum;
     m_run = m_new;
     // O^T += V^T P^T over this wave's dims; lane (g, col) supplies row
-    // 4g + col/4 (+16) at dims 256 dh + 16 db + 4 (col % 4)
+    // 4g + col/4 (+16) at dims 256 dh + 16 db + 4 (col % 4); the transposed
+    // reads go out eight blocks at a time ahead of their MFMAs
     const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + kDHalf * 2 * dh + 8 * (col & 3);
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * db));
-      const i16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRowBytes + 32 * db));
-      bf16x8 vt;
+    for (int d0 = 0; d0 < 16; d0 += 8) {
+      i16x4 lo[8], hi[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vt[j] = u16_as_bf16((uint16_t)lo[j]);
-        vt[4 + j] = u16_as_bf16((uint16_t)hi[j]);
+      for (int u = 0; u < 8; ++u) {
+        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * (d0 + u)));
+        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRowBytes + 32 * (d0 + u)));
       }
-      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[db], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        bf16x8 vt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vt[j] = u16_as_bf16((uint16_t)lo[u][j]);
+          vt[4 + j] = u16_as_bf16((uint16_t)hi[u][j]);
+        }
+        acc_o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[d0 + u], 0, 0, 0);
+      }
     }
+  };
+
+  // Prologue: tiles 0 .. kStages in flight, tile 0 widened into buffer 0.
+  // Register slot j carries tiles j, j + kStages, ... (the step loop is
+  // unrolled by kStages so every slot is a fixed set of registers).
+  i32x4 st0[kChunkSlots], st1[kChunkSlots], st2[kChunkSlots];
+  int lv0, lv1, lv2;
+  {
+    i32x4 first[kChunkSlots];
+    const int lf = fetch(0, first);
+    lv1 = fetch(1, st1);
+    lv2 = fetch(2, st2);
+    lv0 = fetch(3, st0);
+    commit(0, first, lf);
   }
-  // the ring's trailing loads (past the list) must land before the wave ends
+  // Whole rounds of kStages steps, so every path issues the same loads and
+  // the compiler's count of loads in flight stays exact; steps past the list
+  // only keep the barriers and the ring in step.
+  for (int t = 0; t < n_tiles; t += kStages) {
+    step(t, st1, lv1, true);               // widens t+1 (slot 1), then fetches t+4 into it
+    step(t + 1, st2, lv2, t + 1 < n_tiles);
+    step(t + 2, st0, lv0, t + 2 < n_tiles);
+  }
+
+  // the trailing fetches (past the list) must land before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // ---- epilogue: this wave's 256 dims of its 16 heads
@@ -490,10 +489,19 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
       a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
           l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   } else {
+    // partial output normalised by its own denominator, in fp16 (|o| is
+    // bounded by the largest |kv| element, far inside the fp16 range; the
+    // fp16 step is 4x finer than the BF16 output's)
     const int64_t ps = (unit * a.n_splits + split) * 64 + hq * 16 + col;
-    float* po = a.part_o + ps * kD + kDHalf * dh;
+    _Float16* po = a.part_o + ps * kD + kDHalf * dh;
+    const float inv_l = l_run > 0.f ? 1.0f / l_run : 0.f;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) *(f32x4*)(po + 16 * db + 4 * g) = acc_o[db];
+    for (int db = 0; db < 16; ++db) {
+      typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+      const f16x4 h = {(_Float16)(acc_o[db][0] * inv_l), (_Float16)(acc_o[db][1] * inv_l),
+                       (_Float16)(acc_o[db][2] * inv_l), (_Float16)(acc_o[db][3] * inv_l)};
+      *(f16x4*)(po + 16 * db + 4 * g) = h;
+    }
     if (g == 0 && dh == 0) {
       a.part_ml[ps * 2] = m_run;
       a.part_ml[ps * 2 + 1] = l_run;
@@ -537,10 +545,12 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
     const float wgt = exp2f(ms - top);
     den += ls * wgt;
     lsum += ls * exp2f(ms - mmax);
-    const float* po = a.part_o + (base + s * 64) * kD + d0;
-    const f32x4 v0 = *(const f32x4*)po, v1 = *(const f32x4*)(po + 4);
+    // the partial is normalised: its numerator is o * l
+    const float f = ls * wgt;
+    typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+    const f16x8 v = *(const f16x8*)(a.part_o + (base + s * 64) * kD + d0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { o[i] += v0[i] * wgt; o[4 + i] += v1[i] * wgt; }
+    for (int i = 0; i < 8; ++i) o[i] += (float)v[i] * f;
   }
   const float inv = 1.0f / den;
 #pragma unroll

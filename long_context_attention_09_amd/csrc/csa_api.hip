@@ -182,7 +182,7 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   }
   const int64_t units = (int64_t)a->B * a->n_q * ((a->H + 63) / 64);
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
-  int64_t s_max = (list + 63) / 64;               // at least two 32-entry tiles per split
+  int64_t s_max = (list + 191) / 192;             // at least six 32-entry tiles per split
   if (s > s_max) s = s_max;
   if (!dense) {                                   // a CSA split's indices fit the kernel's stage
     const int64_t s_min = (list + csa::kAttendIdxMax - 1) / csa::kAttendIdxMax;
@@ -198,7 +198,7 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   if (s > 1) {
     const size_t rows = (size_t)units * s * 64;
     p.off_o = 0;
-    p.off_ml = align_up(rows * 512 * 4);
+    p.off_ml = align_up(rows * 512 * 2);
     p.total = p.off_ml + align_up(rows * 2 * 4);
   } else {
     p.total = 0;
@@ -228,7 +228,7 @@ int run_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream, 
   L.win_pos0 = a->win_pos0; L.sink = a->sink; L.out = a->out; L.out_lse = a->out_lse;
   L.ev_start = (hipEvent_t)a->ev_start; L.ev_stop = (hipEvent_t)a->ev_stop;
   if (p.total > 0) {
-    L.part_o = (float*)((char*)ws + p.off_o);
+    L.part_o = (_Float16*)((char*)ws + p.off_o);
     L.part_ml = (float*)((char*)ws + p.off_ml);
   }
   if (csa::launch_attend(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;

@@ -79,7 +79,7 @@ struct AttendLaunch {
   const float* sink;
   void* out;
   float* out_lse;
-  float* part_o;             // [units][n_splits][64][d] partial numerators
+  _Float16* part_o;          // [units][n_splits][64][d] partial outputs (normalised)
   float* part_ml;            // [units][n_splits][64][2]  (running max, sum)
   hipEvent_t ev_start, ev_stop;  // recorded around the attention kernel (may be null)
 };
