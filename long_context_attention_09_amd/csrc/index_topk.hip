@@ -202,19 +202,25 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
       rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)(n_store * 4u) : 0, kBufferWord3);
     }
     const uint32_t off_c = (uint32_t)col * 64u + (uint32_t)g * 16u;
-    const uint32_t off_s = (uint32_t)col * 4u;
-    // lanes of row groups 1..3 hold copies of the head sum: their stores are
-    // sent past the end of the score buffer and dropped
-    const uint32_t off_o = g == 0 ? (uint32_t)col * 4u : 0x40000000u;
-    // ring of kRing tiles in flight: 16 B of codes + the scale word per lane
-    // and tile; tile t + kRing is requested as soon as tile t is scored
-    // (tiles past the wave's keys read as zeros without touching memory)
+    // Scales and scores move four tiles (64 keys) at a time, as one 256-byte
+    // access per wave: lane l loads the scale word of key 64 i + l, and the
+    // lane holding key (16 j + col) of tile j of the group is lane 16 j + col;
+    // lane (g, col) keeps the score of tile g of the group for the store.
+    const uint32_t off_s = (uint32_t)lane * 4u;
+    const uint32_t off_o = (uint32_t)lane * 4u;
+    // ring of kRing tiles in flight: 16 B of codes per lane and tile, plus a
+    // scale word per lane for every group of four; tile t + kRing is
+    // requested as soon as tile t is scored, and the scales of a group with
+    // its last tile, once every tile of the slot's previous group has used
+    // them (tiles past the wave's keys read as zeros without touching memory)
+    static_assert(kRing % 4 == 0, "tiles move in groups of four");
     i32x4 kbuf[kRing];
-    uint32_t kscw[kRing];
+    uint32_t kscw[kRing / 4];
     auto fetch = [&](int t, int u) {
       kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               rc, off_c + (uint32_t)t * 1024u, 0, 0));
-      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)t * 64u, 0, 0);
+      if (u % 4 == 3)
+        kscw[u / 4] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)(t - 3) * 64u, 0, 0);
     };
     // issue the first round in ring order (the loop consumes it in that order)
 #pragma unroll
@@ -225,12 +231,14 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     const int xor16 = (lane ^ 16) << 2, xor32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
     const int n_rounds = (int)((n_load + 16 * kRing - 1) / (16 * kRing));
     for (int t0 = 0; t0 < n_rounds * kRing; t0 += kRing) {
+      float keep[QT];
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;
-        const uint32_t kl = (uint32_t)(t * 16 + col);         // key - key_base
         const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
-        const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
+        // this tile's scale word for key col sits in lane 16 (u % 4) + col
+        const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (u % 4) + col) << 2, (int)kscw[u / 4]);
+        const int ksc = (int)((sw >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
           float part = 0.f;
@@ -245,10 +253,16 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
           }
           part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(part)));
           part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(part)));
-          const bool vis = (int64_t)kl < (int64_t)nvis[qi] - key_base;
-          const float sc = vis ? part : -INFINITY;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + (uint32_t)t * 64u, 0, 0);
-          if (g == 0 && vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
+          // every row group now holds the head sum; group g keeps tile g of the four
+          keep[qi] = (u % 4 == g) ? part : keep[qi];
+          if (u % 4 == 3) {
+            const int tg = t - 3;                         // first tile of the group
+            const uint32_t kl = (uint32_t)(tg * 16) + (uint32_t)lane;   // key - key_base
+            const bool vis = (int64_t)kl < (int64_t)nvis[qi] - key_base;
+            const float sc = vis ? keep[qi] : -INFINITY;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + (uint32_t)tg * 64u, 0, 0);
+            if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
+          }
         }
         fetch(t + kRing, u);
       }
@@ -330,18 +344,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total = nu
   return off + incl - v;
 }
 
-// Candidate g of a query, its chunk found by binary search over the
-// exclusive per-chunk prefix `pref` (n_act entries, in LDS).
-__device__ __forceinline__ int chunk_of(const int* pref, int n_act, int g) {
-  int lo = 0, hi = n_act - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= g) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-constexpr int kLdsCand = 8192;   // candidates the select kernel stages in LDS
 
 
 // Per chunk: keys above the first-digit bucket are counted, keys inside it go
@@ -415,15 +417,26 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
 // key T and how many keys equal to T are taken (lowest indices first), count
 // per chunk the candidates above and at T, and from those counts and the
 // chunks' counts above the bucket derive where this chunk's selection starts
-// in the output.  It then emits its selected indices in index order.  Up to
-// kLdsCand candidates are staged in LDS; more are re-read from the workspace.
+// in the output.  It then emits its selected indices in index order.
+//
+// The candidates are read in one round trip with everything else: the first
+// kSlots = 4096 / n_act slots of every chunk's region are loaded before the
+// counts are known (16 per thread) and masked by the counts afterwards;
+// only a chunk holding more candidates than that needs a second pass over
+// its region.
+constexpr int kOptSlots = 4096;                 // candidate slots loaded up front per workgroup
 __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   const int q = blockIdx.y;
   const int b = q / a.n_qb, r = q % a.n_qb;
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
-  // independent loads first: this thread's 16 scores (bounded by the
-  // capacity only), the state, and every chunk's counts
+  const int n_chunks_cap = a.n_chunks;          // chunks of the capacity (>= active chunks)
+  // slots per chunk of the up-front load (a power of two, 4 .. 4096)
+  int slots = kOptSlots;
+  while (slots > 4 && slots * n_chunks_cap > kOptSlots) slots >>= 1;
+  const int slot_shift = __builtin_ctz(slots);
+  // ---- one round trip: this thread's 16 scores, the state, every chunk's
+  // counts and the leading candidate slots
   const float* sc = a.scores + (int64_t)q * a.n_cap;
   const int64_t e0 = c0 + threadIdx.x * 16;
   float sv[16];
@@ -451,6 +464,15 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
       cabv[j] = c < a.n_chunks ? ca[c] : 0;
     }
   }
+  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
+  constexpr int kOptPT = kOptSlots / 256;       // up-front slots per thread
+  uint32_t okey[kOptPT];
+#pragma unroll
+  for (int j = 0; j < kOptPT; ++j) {
+    const int v = (int)threadIdx.x + 256 * j;   // virtual slot: chunk v >> shift, slot v & (slots-1)
+    const int64_t e = (int64_t)(v >> slot_shift) * kChunk + (v & (slots - 1));
+    okey[j] = e < a.n_cap ? ck[e] : 0u;          // (a chunk's candidates never pass the capacity)
+  }
   // leave the first-digit histogram zeroed for the next call (collect, its
   // only reader, has finished)
   {
@@ -468,56 +490,50 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   if (c0 >= st.n_vis) return;
 
   __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
-  __shared__ int pref[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
-  __shared__ uint32_t lkey[kLdsCand];
-  __shared__ uint16_t lchunk[kLdsCand];
+  __shared__ int lcnt[kMaxChunks], cgt[kMaxChunks], ceq[kMaxChunks];
   __shared__ uint32_t s_digit[2], s_kin[2];
+  __shared__ int s_over;
   __shared__ int red[4][4];
   const int n_act = (st.n_vis + kChunk - 1) / kChunk;
-  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
   for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
   if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
-  // exclusive prefix of the per-chunk candidate counts
-  int n_cand = 0;
+  if (threadIdx.x == 0) s_over = 0;
+  __syncthreads();
+  int over = 0;
 #pragma unroll
   for (int j = 0; j < kCPT; ++j) {
-    if (256 * j >= n_act) break;
     const int c = threadIdx.x + 256 * j;
-    const int v = c < n_act ? ccnt[j] : 0;
-    int sum;
-    const int ex = n_cand + block_excl_scan(v, red[0], &sum);
-    if (c < n_act) { pref[c] = ex; cgt[c] = 0; ceq[c] = 0; }
-    n_cand += sum;
+    if (c < kMaxChunks) {
+      const int n = c < n_act ? ccnt[j] : 0;
+      lcnt[c] = n;
+      cgt[c] = 0;
+      ceq[c] = 0;
+      over |= n > slots;
+    }
   }
+  if (over) s_over = 1;
   __syncthreads();
-  const bool staged = n_cand <= kLdsCand;
-  if (staged) {
-    // eight independent loads in flight per thread
-    for (int g0 = threadIdx.x; g0 < n_cand; g0 += 256 * 8) {
-      uint32_t kv[8];
-      int cv[8];
+  const bool overflow = s_over != 0;            // some chunk holds more than `slots` candidates
+  // candidate v of the up-front load is real when its slot is below its chunk's count
+  uint32_t valid = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int g = g0 + 256 * u;
-        cv[u] = g < n_cand ? chunk_of(pref, n_act, g) : 0;
-        kv[u] = g < n_cand ? ck[(int64_t)cv[u] * kChunk + (g - pref[cv[u]])] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int g = g0 + 256 * u;
-        if (g < n_cand) { lkey[g] = kv[u]; lchunk[g] = (uint16_t)cv[u]; }
-      }
-    }
-    __syncthreads();
+  for (int j = 0; j < kOptPT; ++j) {
+    const int v = (int)threadIdx.x + 256 * j;
+    const int c = v >> slot_shift;
+    valid |= (uint32_t)(c < n_act && (v & (slots - 1)) < lcnt[c < kMaxChunks ? c : 0]) << j;
   }
-  auto cand = [&](int g, int* c_of) -> uint32_t {
-    if (staged) {
-      *c_of = lchunk[g];
-      return lkey[g];
+  // every candidate goes through `visit(key, chunk)`: the up-front ones from
+  // registers, the rest of an over-full chunk from its region
+  auto for_each = [&](auto&& visit) {
+#pragma unroll
+    for (int j = 0; j < kOptPT; ++j)
+      if (valid >> j & 1u) visit(okey[j], ((int)threadIdx.x + 256 * j) >> slot_shift);
+    if (overflow) {
+      for (int c = 0; c < n_act; ++c) {
+        const int n = lcnt[c];
+        for (int i = slots + (int)threadIdx.x; i < n; i += 256) visit(ck[(int64_t)c * kChunk + i], c);
+      }
     }
-    const int c = chunk_of(pref, n_act, g);
-    *c_of = c;
-    return ck[(int64_t)c * kChunk + (g - pref[c])];
   };
   // radix select of the k_rem-th largest candidate: bits 19..10, then 9..0
   uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
@@ -525,11 +541,9 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
-    for (int g = threadIdx.x; g < n_cand; g += 256) {
-      int c;
-      const uint32_t key = cand(g, &c);
+    for_each([&](uint32_t key, int) {
       if ((key & mask) == prefix) atomicAdd(&bins[pass][(key >> shift) & 1023u], 1u);
-    }
+    });
     __syncthreads();
     uint32_t v[4];
     my_buckets(bins[pass], v);
@@ -539,12 +553,10 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
     k = s_kin[pass];
   }
   const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
-  for (int g = threadIdx.x; g < n_cand; g += 256) {
-    int c;
-    const uint32_t key = cand(g, &c);
+  for_each([&](uint32_t key, int c) {
     if (key > T) atomicAdd(&cgt[c], 1);
     else if (key == T) atomicAdd(&ceq[c], 1);
-  }
+  });
   __syncthreads();
   // this chunk's output start: the selection of every earlier chunk (above
   // the bucket, above T, and its share of the keys equal to T)
