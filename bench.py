@@ -47,12 +47,12 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "63e756be8b0e19b57c82025a841331d88c90776cb61c1176b9e22101e607e1a8",
-        "fetch_kib": 83316.9, "write_kib": 32896.0},
+        "sha256": "efc2a997d86bb01488fcb15de9ab2f1d91a05b9b33cd3b7eddb7307744caff13",
+        "fetch_kib": 83282.5, "write_kib": 16512.2},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "0c9eba2bf2312b55fb00aae374c275dad27d05ac2117b5aaf77649962b88de3f",
-        "fetch_kib": 69854.5, "write_kib": 8280.1},
+        "sha256": "010199161a7230f613b006dfe8881458656fbf6ca628216eee265ac2cdc24b54",
+        "fetch_kib": 69825.3, "write_kib": 8276.2},
 }
 
 
