@@ -9,23 +9,23 @@
 // joins every head's softmax denominator.
 //
 // FP8_BF16 kernel (gfx950 matrix cores).  A workgroup owns one query, 64
-// heads (16 per wavefront) and one contiguous split of the query's KV list.
-// KV rows stream through LDS in tiles of 32 entries: the loader threads fetch
-// the 576-byte rows (448 E4M3FN bytes + 64 BF16 values) with 16-byte loads
-// into registers while the previous tile is being used, then widen FP8 to
-// BF16 (exact) into a row-major LDS tile.  Each wavefront then computes
-//   S^T[32 entries x 16 heads] = K Q^T     (V_MFMA_F32_16X16X32_BF16, 32 per tile)
-// with its query heads held in registers as the B operand, runs the online
-// softmax in the log2 domain, and accumulates
-//   O^T[512 dims x 16 heads] += V^T P^T    (32 MFMAs per tile)
-// where the B operand P^T is the S^T accumulator itself (the summation order
-// over the 32 entries is permuted to match the accumulator layout) and the A
-// operand V^T comes from the LDS tile through ds_read_b64_tr_b16 transposing
-// reads.  The O^T accumulator keeps one head per lane, so rescaling is a
-// per-lane multiply, done only when a running maximum grows.
+// heads and one contiguous split of the query's KV list.  KV rows stream
+// through LDS in tiles of 32 entries: every thread fetches its share of the
+// 576-byte rows (448 E4M3FN bytes + 64 BF16 values) with 16-byte loads into
+// registers three tiles ahead, then widens FP8 to BF16 (exact, hardware
+// converter) into a row-major LDS tile whose 16-byte chunks are swizzled per
+// row.  Per tile the eight wavefronts first form the scores
+//   S^T[32 entries x 64 heads] = K Q^T       (V_MFMA_F32_32X32X16_BF16)
+// split as 2 head halves x 4 dim quarters, with the normalised, rotated
+// query held in registers as the B operand; the dim-quarter partials are
+// summed through LDS by the wave that runs the online softmax (log2 domain,
+// lazy rescale) of 8 heads, which leaves P in LDS as BF16.  Then
+//   O^T[512 dims x 64 heads] += V^T P^T
+// is split by dims only (64 per wave), with V^T read once through
+// ds_read_b64_tr_b16 transposing reads.
 //
 // A split that covers the whole list finalises in place (sink, normalisation,
-// inverse RoPE, BF16 store); otherwise (running max, sum, numerator) partials
+// inverse RoPE, BF16 store); otherwise (running max, sum, normalised output) partials
 // go to the workspace and combine_kernel merges them.
 #include <hip/hip_ext.h>
 
@@ -38,10 +38,8 @@ constexpr int kD = 512;
 constexpr int kDR = 64;
 constexpr int kDN = kD - kDR;         // 448
 constexpr int kTile = 32;             // entries per LDS tile
-constexpr int kRowBytes = kD * 2 + 16;  // bf16 row + 16 B pad (conflict-free 16-byte row reads)
 constexpr int kChunksPerRow = kDN / 16 + (kDR * 2) / 16;  // 28 + 8 = 36 sixteen-byte chunks
 constexpr int kChunksPerTile = kTile * kChunksPerRow;     // 1152
-constexpr int kLoadsPerThread = (kChunksPerTile + 255) / 256;  // 5 (the last one partial)
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -95,31 +93,49 @@ __device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, co
   return true;
 }
 
-__device__ __forceinline__ uint32_t pack_hi16(float f0, float f1) {
-  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-}
-
 typedef __attribute__((address_space(1))) const i32x4 gbl_i32x4;
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the true max
 
-// Workgroup of 8 wavefronts: wave w owns 16 heads (w & 3) and one half of the
-// 512 dims (w >> 2).  The two waves of a head group each form the scores over
-// their half of the dims and swap the partial sums through LDS, so both hold
-// the full scores, run the same online softmax, and accumulate the output for
-// their own 256 dims.  Two wavefronts per SIMD hide each other's LDS latency.
+// Workgroup of 8 wavefronts with two roles per 32-entry tile:
+//  * scores: wave w forms S^T = K Q^T for the 32 heads 32 (w >> 2) .. +31 over
+//    the 128 dims 128 (w & 3) .. +127 (V_MFMA_F32_32X32X16_BF16, 8 per tile);
+//    the four partial blocks of a head half meet in LDS, and wave w sums the
+//    8 heads 32 (w >> 2) + 8 (w & 3) .. +7 and runs their online softmax,
+//    leaving P (BF16) and each head's rescale factor in LDS;
+//  * output: wave w accumulates O^T += V^T P^T for the 64 dims 64 w .. +63 of
+//    all 64 heads, so every V element leaves LDS once per workgroup, through
+//    ds_read_b64_tr_b16 transposing reads.
+// The output product of tile t-1 runs in the same phase as the softmax of
+// tile t (matrix cores and vector ALUs overlap); three tile buffers keep
+// tile t-1 readable while tile t+1 is being widened.
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kDHalf = kD / 2;
-constexpr int kTileBytes = kTile * kRowBytes;             // one BF16 tile in LDS
+constexpr int kRowBytes = kD * 2 + 16;                    // BF16 row in LDS + 16-byte pad
+constexpr int kTileBytes = kTile * kRowBytes;             // 32.5 KiB
+constexpr int kTileBufs = 3;
+constexpr int kXsWave = 32 * 128;                         // one wave's partial scores (bytes)
+constexpr int kPRow = 80;                                 // bytes per head in P: 32 BF16 + pad
+constexpr int kPBytes = 64 * kPRow;
 
-// Row loads: thread t owns the sixteen-byte chunks t, t + 512, t + 1024 of a
-// tile (chunk c = row c / 36, part c % 36: parts 0..27 hold FP8 dims, 28..35
-// BF16 RoPE dims) and keeps kStages tiles of them in flight in registers.
+// Row loads: thread t owns the sixteen-byte chunks t, t + 512 (and threads
+// 128 .. 255 also t + 896) of a tile (chunk c = row c / 36, part c % 36:
+// parts 0..27 hold FP8 dims, 28..35 BF16 RoPE dims) and keeps kStages tiles of
+// them in flight in registers.
 constexpr int kChunkSlots = (kChunksPerTile + kThreads - 1) / kThreads;   // 3
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr int kAddrSlots = 8;                             // row-address ring (tiles)
 constexpr int kIdxMax = kAttendIdxMax;                    // selected indices staged per split
+
+// Entry slot k (0..31) of a tile lives in LDS row 16 (k / 16) + 2 h + u + 4 q,
+// where k % 16 = 8 h + 4 u + q.  Slot order is the order the matrix cores sum
+// over (the score MFMA's rows, P's columns, the output MFMA's K index); the
+// row placement makes each 32-lane half of a transposing read (4 rows x 64
+// bytes) and each 16-lane row read fall on distinct banks with rows padded
+// to 1040 bytes, so every fragment address is one register plus immediates.
+__device__ __forceinline__ int slot_row(int k) {
+  return 16 * (k >> 4) + 2 * ((k >> 3) & 1) + ((k >> 2) & 1) + 4 * (k & 3);
+}
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -136,23 +152,33 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
     __asm__ __volatile__("" ::: "memory");       \
   } while (0)
 
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+// Cross-lane move within rows of 16 lanes (DPP control CTRL: quad_perm or
+// row_half_mirror), no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * kTileBytes];  // BF16 rows, two buffers
-  __shared__ __attribute__((aligned(16))) float xch[kWaves * 64 * 8];    // score halves
-  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                      // [slot][nope|rope][row]
-  __shared__ float rope_cs[64];                                          // cos, sin at t
-  __shared__ int lidx[kIdxMax];                                          // staged indices (CSA)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs * kTileBytes];  // BF16 rows
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves * kXsWave];           // partial scores
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * kPBytes];              // P, two buffers
+  __shared__ float alpha_s[2 * 64];                                               // rescale factors
+  __shared__ float ml_s[2 * 64];                                                  // final (max, sum)
+  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                               // [slot][nope|rope][row]
+  __shared__ uint32_t rowmask[kAddrSlots];                                        // live rows per tile
+  __shared__ float rope_cs[64];                                                   // cos, sin at t
+  __shared__ int lidx[kIdxMax];                                                   // staged indices (CSA)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hq = wave & 3, dh = wave >> 2;
-  const int g = lane >> 4, col = lane & 15;
+  const int hh = wave >> 2, dq = wave & 3;
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
-  const int head = hg * 64 + hq * 16 + col;
-  const bool head_ok = head < a.H;
   const ListInfo L = list_info(a, b, r);
   const int list_len = L.n_comp + L.n_w;
   const int p0 = split * a.split_len;
@@ -174,6 +200,58 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     for (int i = tid; i < n_sel; i += kThreads) lidx[i] = src[p0 + i];
   }
   __syncthreads();
+
+  // ---- query operand of the score role: head 32 hh + (lane % 32), dims
+  //      128 dq + 16 s + 8 (lane / 32) + j; RMSNorm over all 512 dims (the four
+  //      dim quarters add their sums of squares through LDS), RoPE at t, BF16
+  bf16x8 qv[8];
+  {
+    const int head_q = hg * 64 + 32 * hh + (lane & 31);
+    const bool ok = head_q < a.H;
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (ok ? head_q : 0)) * kD +
+                           128 * dq + 8 * (lane >> 5);
+    float x[8][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      i32x4 v = *(gbl_i32x4*)(qrow + 16 * s);
+      if (!ok) v = (i32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[s][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
+        x[s][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
+        ss += x[s][2 * j] * x[s][2 * j] + x[s][2 * j + 1] * x[s][2 * j + 1];
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    float* ssx = (float*)xs;                 // [hh][dq][32], before the tile loop uses xs
+    if (lane < 32) ssx[(hh * 4 + dq) * 32 + lane] = ss;
+    __syncthreads();
+    ss = ((ssx[(hh * 4 + 0) * 32 + (lane & 31)] + ssx[(hh * 4 + 1) * 32 + (lane & 31)]) +
+          ssx[(hh * 4 + 2) * 32 + (lane & 31)]) + ssx[(hh * 4 + 3) * 32 + (lane & 31)];
+    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[s][j] *= rs;
+    if (dq == 3) {                           // dims 448 .. 511 carry RoPE
+#pragma unroll
+      for (int s = 4; s < 8; ++s) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int u = (128 * 3 + 16 * s + 8 * (lane >> 5) + j - kDN) >> 1;
+          const float cs = rope_cs[u], sn = rope_cs[32 + u];
+          const float xe = x[s][j], xo = x[s][j + 1];
+          x[s][j] = xe * cs - xo * sn;
+          x[s][j + 1] = xe * sn + xo * cs;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[s][j] = u16_as_bf16(f32_to_bf16(x[s][j]));
+  }
 
   // Row addresses of tile t (list positions p0 + 32t ...): 0 marks a masked row.
   auto tile_addrs = [&](int t) {
@@ -197,9 +275,12 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
           }
         }
       }
+      // list position p0 + 32 t + tid fills entry slot tid, i.e. LDS row slot_row(tid)
       uint64_t* slot = rowa + (t % kAddrSlots) * 2 * kTile;
-      slot[tid] = an;
-      slot[kTile + tid] = ar;
+      slot[slot_row(tid)] = an;
+      slot[kTile + slot_row(tid)] = ar;
+      const uint64_t live = __ballot(an != 0);      // bit k: entry slot k is a real row
+      if (tid == 0) rowmask[t % kAddrSlots] = (uint32_t)live;
     }
   };
 #pragma unroll
@@ -207,18 +288,21 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   __syncthreads();
 
   // this thread's chunks of a tile
-  int ch_row[kChunkSlots], ch_src[kChunkSlots], ch_dst[kChunkSlots];
+  int ch_slot[kChunkSlots], ch_src[kChunkSlots], ch_dst[kChunkSlots];
   bool ch_ok[kChunkSlots], ch_rope[kChunkSlots];
 #pragma unroll
   for (int k = 0; k < kChunkSlots; ++k) {
-    const int c = tid + kThreads * k;
-    ch_ok[k] = c < kChunksPerTile;
+    // chunks 0 .. 1023 to every thread twice, 1024 .. 1151 to waves 2 and 3
+    // (wave 0 also builds the row addresses)
+    const int c = k < 2 ? tid + kThreads * k : 2 * kThreads + tid - 128;
+    ch_ok[k] = k < 2 || (tid >= 128 && tid < 128 + kChunksPerTile - 2 * kThreads);
     const int cc = ch_ok[k] ? c : 0;
     const int part = cc % kChunksPerRow;
-    ch_row[k] = cc / kChunksPerRow;
+    const int row = cc / kChunksPerRow;
     ch_rope[k] = part >= 28;
+    ch_slot[k] = (ch_rope[k] ? kTile : 0) + row;
     ch_src[k] = part < 28 ? part * 16 : (part - 28) * 16;
-    ch_dst[k] = ch_row[k] * kRowBytes + (part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16);
+    ch_dst[k] = row * kRowBytes + (part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16);
   }
   // Request tile t's chunks into registers.  Every load is issued (a masked
   // row or a missing chunk reads harmless bytes: the query) so the count of
@@ -227,26 +311,28 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   const uint64_t dummy = (uint64_t)a.q;      // any readable bytes (q holds >= 16 KiB)
   auto fetch = [&](int t, i32x4 (&v)[kChunkSlots]) {
     const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
+    uint64_t base[kChunkSlots];
+#pragma unroll
+    for (int k = 0; k < kChunkSlots; ++k) base[k] = slot_a[ch_slot[k]];   // all requested at once
     int live = 0;
 #pragma unroll
     for (int k = 0; k < kChunkSlots; ++k) {
-      const uint64_t base = ch_ok[k] ? slot_a[(ch_rope[k] ? kTile : 0) + ch_row[k]] : 0;
-      live |= (base != 0) << k;
-      v[k] = *(gbl_i32x4*)((base ? base : dummy) + (uint64_t)ch_src[k]);
+      const uint64_t bk = ch_ok[k] ? base[k] : 0;
+      live |= (bk != 0) << k;
+      v[k] = *(gbl_i32x4*)((bk ? bk : dummy) + (uint64_t)ch_src[k]);
     }
     return live;
   };
-  // Widen tile t's chunks to BF16 rows in buffer t % 2 (FP8 dims exactly;
+  // Widen tile t's chunks to BF16 rows in buffer t % 3 (FP8 dims exactly;
   // zeros for masked rows).
   auto commit = [&](int t, const i32x4 (&vin)[kChunkSlots], int live) {
-    uint8_t* tile = tiles + (t & 1) * kTileBytes;
+    uint8_t* tile = tiles + (t % kTileBufs) * kTileBytes;
 #pragma unroll
     for (int k = 0; k < kChunkSlots; ++k) {
       if (!ch_ok[k]) continue;
       const i32x4 zero = {0, 0, 0, 0};
       const i32x4 vk = (live >> k) & 1 ? vin[k] : zero;
       const i32x4 v[1] = {vk};
-      uint8_t* dst = tile + ch_dst[k];
       if (!ch_rope[k]) {
         // two E4M3 bytes -> two BF16 per instruction (scale 1: exact)
         i32x4 lo, hi;
@@ -257,254 +343,281 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
           if (j < 2) { lo[2 * j] = w0; lo[2 * j + 1] = w1; }
           else { hi[2 * (j - 2)] = w0; hi[2 * (j - 2) + 1] = w1; }
         }
-        *(i32x4*)dst = lo;
-        *(i32x4*)(dst + 16) = hi;
+        *(i32x4*)(tile + ch_dst[k]) = lo;
+        *(i32x4*)(tile + ch_dst[k] + 16) = hi;
       } else {
-        *(i32x4*)dst = v[0];
+        *(i32x4*)(tile + ch_dst[k]) = v[0];
       }
     }
   };
 
-  // ---- query operand: head `head`, dims 256 dh + 32 kb + 8 g + j, RMSNorm, RoPE at t, BF16
-  bf16x8 qv[8];
-  {
-    const int hq_ = head_ok ? head : 0;
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + hq_) * kD;
-    float x[8][8];
-    float ss = 0.f;
+  // ---- score role: partial S^T of tile t over this wave's dims, into xs
+  struct KIn {
+    bf16x8 kf[8];
+  };
+  auto scores_load = [&](int t) {
+    KIn in;
+    const uint8_t* tile = tiles + (t % kTileBufs) * kTileBytes;
+    const uint8_t* krow = tile + slot_row(lane & 31) * kRowBytes + 2 * (128 * dq + 8 * (lane >> 5));
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const i32x4 v = *(gbl_i32x4*)(qrow + kDHalf * dh + 32 * kb + 8 * g);
-      const i32x4 o = *(gbl_i32x4*)(qrow + kDHalf * (1 - dh) + 32 * kb + 8 * g);
+    for (int s = 0; s < 8; ++s) in.kf[s] = *(const bf16x8*)(krow + 32 * s);
+    return in;
+  };
+  auto scores_mma = [&](const KIn& in) {
+    f32x16 s0 = {};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[kb][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
-        x[kb][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
-        const float y0 = __uint_as_float(((uint32_t)o[j]) << 16);
-        const float y1 = __uint_as_float(((uint32_t)o[j]) & 0xffff0000u);
-        ss += x[kb][2 * j] * x[kb][2 * j] + x[kb][2 * j + 1] * x[kb][2 * j + 1] + y0 * y0 + y1 * y1;
-      }
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
+    for (int s = 0; s < 8; ++s) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in.kf[s], qv[s], s0, 0, 0, 0);
+    // lane holds head (lane % 32), entry slots 8 jb + 4 (lane / 32) + i, i.e.
+    // the 16-byte group k = 2 jb + lane / 32 of that head's 32 scores
+    uint8_t* xw = xs + wave * kXsWave + (lane & 31) * 128;
+    const int sw = ((lane & 31) >> 1) & 7;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[kb][j] *= rs;
-    if (dh == 1) {
-#pragma unroll
-      for (int kb = 6; kb < 8; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int u = (kDHalf + 32 * kb + 8 * g + j - kDN) >> 1;
-          const float cs = rope_cs[u], sn = rope_cs[32 + u];
-          const float xe = x[kb][j], xo = x[kb][j + 1];
-          x[kb][j] = xe * cs - xo * sn;
-          x[kb][j + 1] = xe * sn + xo * cs;
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[kb][j] = u16_as_bf16(f32_to_bf16(x[kb][j]));
-  }
+    for (int jb = 0; jb < 4; ++jb)
+      *(f32x4*)(xw + 16 * ((2 * jb + (lane >> 5)) ^ sw)) =
+          (f32x4){s0[4 * jb], s0[4 * jb + 1], s0[4 * jb + 2], s0[4 * jb + 3]};
+  };
 
-  f32x4 acc_o[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc_o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;     // log2-domain reference max of head `col` (lags the true max by < 8)
+  // ---- softmax role: head sm_head of the group, entries 4 sm_k .. +3
+  const int sm_hloc = 8 * dq + (lane >> 3);                 // head within the head half
+  const int sm_head = 32 * hh + sm_hloc;                    // head within the group
+  const int sm_k = lane & 7;
+  float m_run = -INFINITY;     // log2-domain reference max (lags the true max by < the slack)
   float l_part = 0.f;          // this lane's share of the running denominator
-  float* xmine = xch + (wave * 64 + lane) * 8;
-  const float* xpart = xch + ((wave ^ 4) * 64 + lane) * 8;
-
-  // One tile of work.  Barriers:
-  //   A: tile t's BF16 rows are written (by every wave) and buffer (t+1) % 2
-  //      is free again;
-  //   B: the score halves are exchanged.
-  // Between A and B the scores of tile t are formed and tile t+1 (fetched
-  // kStages - 1 tiles ago) is widened into the other buffer; its register
-  // slot then fetches tile t + 1 + kStages.  After B: softmax and O += V P.
-  auto step = [&](int t, i32x4 (&cur)[kChunkSlots], int& cur_live, bool active) {
-    ATTEND_BARRIER(kWaitLgkm0);
-    const uint8_t* tile = tiles + (t & 1) * kTileBytes;
-    const uint64_t* vrow = rowa + (t % kAddrSlots) * 2 * kTile;   // masked rows have address 0
-
-    // partial S^T = K Q^T over this wave's 256 dims: every K fragment is
-    // requested first, then two 16-entry blocks over two accumulators each
-    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (active) {
-      bf16x8 kf[2][8];
+  // part 1: the four partial score blocks of the head and the live-row mask
+  struct SmIn {
+    f32x4 x[4];
+    uint32_t live;
+  };
+  auto sm_load = [&](int t) {
+    SmIn in;
+    const int swr = (sm_hloc >> 1) & 7;
 #pragma unroll
-      for (int eb = 0; eb < 2; ++eb) {
-        const uint8_t* krow = tile + (eb * 16 + col) * kRowBytes + kDHalf * 2 * dh + 16 * g;
+    for (int src = 0; src < 4; ++src)
+      in.x[src] = *(const f32x4*)(xs + (hh * 4 + src) * kXsWave + sm_hloc * 128 + 16 * (sm_k ^ swr));
+    in.live = rowmask[t % kAddrSlots];
+    return in;
+  };
+  // part 2: online softmax, P and the rescale factor to LDS
+  auto sm_compute = [&](int t, const SmIn& in) {
+    const f32x4 sc = ((in.x[0] + in.x[1]) + in.x[2]) + in.x[3];
+    float v[4];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) kf[eb][kb] = *(const bf16x8*)(krow + 64 * kb);
+    for (int i = 0; i < 4; ++i) {
+      v[i] = (in.live >> (4 * sm_k + i)) & 1 ? sc[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, v[i]);
+    }
+    mx = fmaxf(mx, dpp_f32<0xB1>(mx));     // lane ^ 1
+    mx = fmaxf(mx, dpp_f32<0x4E>(mx));     // lane ^ 2
+    mx = fmaxf(mx, dpp_f32<0x141>(mx));    // lane 7 - i of each 8: the other quad
+    // the reference max moves only when the tile max overtakes it by the slack,
+    // so O rescales are rare; probabilities stay below 2^slack
+    const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);   // argument <= 0, or -inf
+    float p[4], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(v[i] - m_use);
+      psum += p[i];
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    const bf16x4 pk = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};   // nearest even
+    *(bf16x4*)(pbuf + (t & 1) * kPBytes + sm_head * kPRow + 8 * sm_k) = pk;
+    if (sm_k == 0) alpha_s[(t & 1) * 64 + sm_head] = alpha;
+  };
+
+  // ---- output role: O^T (dims 64 wave + 32 db + ..., heads 32 hb + ...) += V^T P^T
+  f32x16 acc_o[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) acc_o[db][hb] = (f32x16){};
+  struct PvIn {
+    i16x4 vlo[2][2], vhi[2][2];   // [rs][db]
+    bf16x8 pf[2][2];              // [rs][hb]
+    float al0, al1;
+  };
+  // part 1: V^T fragments (transposing reads), P^T fragments, rescale factors
+  auto pv_load = [&](int tbuf, int pidx) {
+    PvIn in;
+    const uint8_t* tile = tiles + tbuf * kTileBytes;
+    const uint8_t* pb = pbuf + pidx * kPBytes;
+    // transposing reads: lane j of 16-lane group G supplies entry slot
+    // 16 rs + 8 (G / 2) + 4 u + j / 4 (u = 0, 1 for the two reads) at the 4
+    // dims 64 wave + 32 db + 16 (G % 2) + 4 (j % 4) ..; lane j of the group
+    // receives dim j's values of the four slots
+    const int G = lane >> 4, j = lane & 15;
+    const uint8_t* vb = tile + slot_row(8 * (G >> 1) + (j >> 2)) * kRowBytes +
+                        2 * (64 * wave + 16 * (G & 1) + 4 * (j & 3));
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const uint8_t* v0 = vb + 16 * rs * kRowBytes + 64 * db;
+        in.vlo[rs][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)v0);
+        in.vhi[rs][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + kRowBytes));   // u = 1: next row
       }
+    // P^T: lane supplies head 32 hb + lane % 32, entries 16 rs + 8 (lane / 32) .. +7
 #pragma unroll
-      for (int eb = 0; eb < 2; ++eb) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    for (int rs = 0; rs < 2; ++rs)
 #pragma unroll
-        for (int kb = 0; kb < 8; kb += 2) {
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[eb][kb], qv[kb], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[eb][kb + 1], qv[kb + 1], s1, 0, 0, 0);
-        }
-        s[eb] = s0 + s1;
+      for (int hb = 0; hb < 2; ++hb)
+        in.pf[rs][hb] = *(const bf16x8*)(pb + (32 * hb + (lane & 31)) * kPRow + 2 * (16 * rs + 8 * (lane >> 5)));
+    in.al0 = alpha_s[pidx * 64 + (lane & 31)];
+    in.al1 = alpha_s[pidx * 64 + 32 + (lane & 31)];
+    return in;
+  };
+  // part 2: rescale when a running max moved, then 8 MFMAs
+  auto pv_mma = [&](const PvIn& in) {
+    if (__any(in.al0 != 1.0f || in.al1 != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        acc_o[db][0] *= in.al0;
+        acc_o[db][1] *= in.al1;
       }
     }
-    // swap halves with the partner wave (same heads, other dims)
-    *(f32x4*)xmine = s[0];
-    *(f32x4*)(xmine + 4) = s[1];
-    // widen tile t+1 while the matrix cores work, then reuse its registers
-    // (past the list the tiles are all masked and widen to zeros)
+#pragma unroll
+    for (int rs = 0; rs < 2; ++rs)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        bf16x8 vt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vt[i] = u16_as_bf16((uint16_t)in.vlo[rs][db][i]);
+          vt[4 + i] = u16_as_bf16((uint16_t)in.vhi[rs][db][i]);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          acc_o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, in.pf[rs][hb], acc_o[db][hb], 0, 0, 0);
+      }
+  };
+
+  // One pipeline step.  Phase 1: every LDS read of the step's matrix work
+  // goes out at once (K of tile t; V, P and the rescale factors of tile t-1,
+  // whose P was written in the previous step), then O += V P for tile t-1 and
+  // the scores of tile t run on the matrix cores while tile t+1 (fetched
+  // kStages steps ago) is widened into its buffer and tile t + 1 + kStages is
+  // requested into the freed registers.  Barrier.  Phase 2: the softmax of
+  // tile t.  Barrier.  The body is the same on every step: tile -1 is an
+  // all-zero tile with P = 0 and rescale factors 1, and tiles past the list
+  // are masked (scores -inf: P = 0, the running max and sum unchanged).
+  auto step = [&](int t, i32x4 (&cur)[kChunkSlots], int& cur_live) {
+    const PvIn pin = pv_load((t + 2) % kTileBufs, (t + 1) & 1);   // tile t - 1
+    const KIn kin = scores_load(t);
+    pv_mma(pin);
+    scores_mma(kin);
     commit(t + 1, cur, cur_live);
     tile_addrs(t + kStages + 2);
     cur_live = fetch(t + 1 + kStages, cur);
     ATTEND_BARRIER(kWaitLgkm0);
-    if (!active) return;
-    {
-      const f32x4 o0 = *(const f32x4*)xpart, o1 = *(const f32x4*)(xpart + 4);
-      // the same sum in both waves (a + b == b + a), so both run the same softmax
-      s[0] = dh == 0 ? s[0] + o0 : o0 + s[0];
-      s[1] = dh == 0 ? s[1] + o1 : o1 + s[1];
-    }
-    // online softmax (log2 domain); lane holds entries eb*16 + 4g + i of head `col`
-    float mx = -INFINITY;
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = vrow[eb * 16 + 4 * g + i] ? s[eb][i] * a.scale_log2 : -INFINITY;
-        s[eb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // the reference max moves only when the tile max overtakes it by the slack,
-    // so the O rescale below is rare; probabilities stay below 2^slack
-    const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    // arguments are at most the slack (8), or -inf for masked rows
-    const float alpha = fast_exp2(m_run - m_use);
-    bf16x8 pv;
-    float psum = 0.f;
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[eb][i] - m_use);
-        psum += p;
-        pv[eb * 4 + i] = (__bf16)p;          // round to nearest even
-      }
-    if (__any(alpha != 1.0f)) {
-      l_part *= alpha;
-#pragma unroll
-      for (int db = 0; db < 16; ++db) acc_o[db] *= alpha;
-    }
-    l_part += psum;
-    m_run = m_new;
-    // O^T += V^T P^T over this wave's dims; lane (g, col) supplies row
-    // 4g + col/4 (+16) at dims 256 dh + 16 db + 4 (col % 4); the transposed
-    // reads go out eight blocks at a time ahead of their MFMAs
-    const uint8_t* vbase = tile + (4 * g + (col >> 2)) * kRowBytes + kDHalf * 2 * dh + 8 * (col & 3);
-#pragma unroll
-    for (int d0 = 0; d0 < 16; d0 += 8) {
-      i16x4 lo[8], hi[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        lo[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 32 * (d0 + u)));
-        hi[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + 16 * kRowBytes + 32 * (d0 + u)));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        bf16x8 vt;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vt[j] = u16_as_bf16((uint16_t)lo[u][j]);
-          vt[4 + j] = u16_as_bf16((uint16_t)hi[u][j]);
-        }
-        acc_o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pv, acc_o[d0 + u], 0, 0, 0);
-      }
-    }
+    sm_compute(t, sm_load(t));
+    ATTEND_BARRIER(kWaitLgkm0);
   };
 
   // Prologue: tiles 0 .. kStages in flight, tile 0 widened into buffer 0.
   // Register slot j carries tiles j, j + kStages, ... (the step loop is
   // unrolled by kStages so every slot is a fixed set of registers).
-  i32x4 st0[kChunkSlots], st1[kChunkSlots], st2[kChunkSlots];
-  int lv0, lv1, lv2;
+  static_assert(kStages == 2, "the step loop below is unrolled for two register stages");
+  i32x4 st0[kChunkSlots], st1[kChunkSlots];
+  int lv0, lv1;
   {
     i32x4 first[kChunkSlots];
     const int lf = fetch(0, first);
     lv1 = fetch(1, st1);
-    lv2 = fetch(2, st2);
-    lv0 = fetch(3, st0);
+    lv0 = fetch(2, st0);
     commit(0, first, lf);
   }
-  // Whole rounds of kStages steps, so every path issues the same loads and
-  // the compiler's count of loads in flight stays exact; steps past the list
-  // only keep the barriers and the ring in step.
-  for (int t = 0; t < n_tiles; t += kStages) {
-    step(t, st1, lv1, true);               // widens t+1 (slot 1), then fetches t+4 into it
-    step(t + 1, st2, lv2, t + 1 < n_tiles);
-    step(t + 2, st0, lv0, t + 2 < n_tiles);
+  // tile -1 of the first step's output product: zero rows, P = 0, factors 1
+  for (int i = tid; i < kTileBytes / 16; i += kThreads)
+    *(i32x4*)(tiles + 2 * kTileBytes + 16 * i) = (i32x4){0, 0, 0, 0};
+  for (int i = tid; i < kPBytes / 16; i += kThreads) *(i32x4*)(pbuf + kPBytes + 16 * i) = (i32x4){0, 0, 0, 0};
+  if (tid < 64) alpha_s[64 + tid] = 1.0f;
+  ATTEND_BARRIER(kWaitLgkm0);
+  // Whole rounds of kStages steps (n_tiles + 1 steps are needed: the last one
+  // only accumulates the final tile), so every path issues the same loads and
+  // the compiler's count of loads in flight stays exact.
+  for (int t = 0; t <= n_tiles; t += kStages) {
+    step(t, st1, lv1);               // widens t+1 (slot 1), then fetches t+3 into it
+    step(t + 1, st0, lv0);
   }
 
   // the trailing fetches (past the list) must land before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue: this wave's 256 dims of its 16 heads
-  float l_run = l_part + __shfl_xor(l_part, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (!head_ok) return;
+  // ---- epilogue: the softmax role publishes each head's (max, sum)
+  {
+    float l_run = l_part;
+    l_run += __shfl_xor(l_run, 1, 64);
+    l_run += __shfl_xor(l_run, 2, 64);
+    l_run += __shfl_xor(l_run, 4, 64);
+    if (sm_k == 0) {
+      ml_s[2 * sm_head] = m_run;
+      ml_s[2 * sm_head + 1] = l_run;
+    }
+  }
+  __syncthreads();
   const int64_t unit = (int64_t)br * gridDim.y + hg;
-  if (a.n_splits == 1) {
-    const float z2 = a.sink[head] * kLog2e;
-    const float top = fmaxf(m_run, z2);
-    const float den = l_run * exp2f(m_run - top) + exp2f(z2 - top);
-    const float inv = exp2f(m_run - top) / den;      // 0 when no row was seen
-    uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD + kDHalf * dh;
-    const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
+  const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      float o[4];
+  for (int hb = 0; hb < 2; ++hb) {
+    const int hl = 32 * hb + (lane & 31);
+    const int head = hg * 64 + hl;
+    if (head >= a.H) continue;
+    const float m_h = ml_s[2 * hl], l_h = ml_s[2 * hl + 1];
+    if (a.n_splits == 1) {
+      const float z2 = a.sink[head] * kLog2e;
+      const float top = fmaxf(m_h, z2);
+      const float den = l_h * exp2f(m_h - top) + exp2f(z2 - top);
+      const float inv = exp2f(m_h - top) / den;      // 0 when no row was seen
+      uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = acc_o[db][i] * inv;
-      if (dh == 1 && db >= 12 && inv_rope) {
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const int u = (kDHalf + 16 * db + 4 * g + i - kDN) >> 1;
-          const float cs = rope_cs[u], sn = -rope_cs[32 + u];   // rotation by -t
-          const float xe = o[i], xo = o[i + 1];
-          o[i] = xe * cs - xo * sn;
-          o[i + 1] = xe * sn + xo * cs;
+        for (int jb = 0; jb < 4; ++jb) {
+          const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = acc_o[db][hb][4 * jb + i] * inv;
+          if (d0 >= kDN && inv_rope) {
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const int u = (d0 + i - kDN) >> 1;
+              const float cs = rope_cs[u], sn = -rope_cs[32 + u];   // rotation by -t
+              const float xe = o[i], xo = o[i + 1];
+              o[i] = xe * cs - xo * sn;
+              o[i + 1] = xe * sn + xo * cs;
+            }
+          }
+          const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+          *(i32x2*)(orow + d0) = (i32x2){(int)w0, (int)w1};
         }
-      }
-      const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-      *(i32x2*)(orow + 16 * db + 4 * g) = (i32x2){(int)w0, (int)w1};
-    }
-    if (a.out_lse && g == 0 && dh == 0)
-      a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
-          l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
-  } else {
-    // partial output normalised by its own denominator, in fp16 (|o| is
-    // bounded by the largest |kv| element, far inside the fp16 range; the
-    // fp16 step is 4x finer than the BF16 output's)
-    const int64_t ps = (unit * a.n_splits + split) * 64 + hq * 16 + col;
-    _Float16* po = a.part_o + ps * kD + kDHalf * dh;
-    const float inv_l = l_run > 0.f ? 1.0f / l_run : 0.f;
+      if (a.out_lse && wave == 0 && lane < 32)
+        a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
+            l_h > 0.f ? (m_h + log2f(l_h)) * 0.6931471805599453f : -INFINITY;
+    } else {
+      // partial output normalised by its own denominator, in fp16 (|o| is
+      // bounded by the largest |kv| element, far inside the fp16 range; the
+      // fp16 step is 4x finer than the BF16 output's)
+      const int64_t ps = (unit * a.n_splits + split) * 64 + hl;
+      _Float16* po = a.part_o + ps * kD;
+      const float inv_l = l_h > 0.f ? 1.0f / l_h : 0.f;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-      const f16x4 h = {(_Float16)(acc_o[db][0] * inv_l), (_Float16)(acc_o[db][1] * inv_l),
-                       (_Float16)(acc_o[db][2] * inv_l), (_Float16)(acc_o[db][3] * inv_l)};
-      *(f16x4*)(po + 16 * db + 4 * g) = h;
-    }
-    if (g == 0 && dh == 0) {
-      a.part_ml[ps * 2] = m_run;
-      a.part_ml[ps * 2 + 1] = l_run;
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+          const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
+          const f16x4 h = {(_Float16)(acc_o[db][hb][4 * jb] * inv_l), (_Float16)(acc_o[db][hb][4 * jb + 1] * inv_l),
+                           (_Float16)(acc_o[db][hb][4 * jb + 2] * inv_l), (_Float16)(acc_o[db][hb][4 * jb + 3] * inv_l)};
+          *(f16x4*)(po + d0) = h;
+        }
+      if (wave == 0 && lane < 32) {
+        a.part_ml[ps * 2] = m_h;
+        a.part_ml[ps * 2 + 1] = l_h;
+      }
     }
   }
 }

@@ -57,7 +57,7 @@ struct IndexLaunch {
 };
 
 // Longest split of a CSA selection list the FP8 attention kernel stages in LDS.
-constexpr int kAttendIdxMax = 4096;
+constexpr int kAttendIdxMax = 2048;
 
 struct AttendLaunch {
   int32_t B, n_q, H, d, d_rope, m, fmt, flags;
