@@ -304,6 +304,24 @@ int csa_compress(const CsaCompressArgs* args, void* stream);
  * status is that of the first invalid job, else of the launches.  Jobs must
  * not write to overlapping outputs. */
 int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void* stream);
+
+/* The same batch with a workspace, so that long blocks (m >= 16, the HCA
+ * compression) are pooled over many workgroups instead of one per entry: the
+ * candidates of an entry are folded in groups of 16 by separate workgroups
+ * into per-channel partial (max, sum, weighted sum) states, which a second
+ * launch merges before the norm, rotation and storage of the entry.  The
+ * result equals csa_compress_batch's up to the order of the fp32 sums.
+ *
+ * csa_compress_workspace_bytes: device bytes the batch needs (0 when no job
+ * has long blocks with a complete entry; (size_t)-1 when a job is invalid).
+ * Workspace: at least that many bytes, 256-byte aligned, caller-owned, no
+ * initial contents required; its contents after the call are unspecified.
+ * Returns CSA_EWORKSPACE when it is too small or misaligned (nothing is
+ * launched), otherwise as csa_compress_batch.  Calls that share a workspace
+ * must be ordered on one stream. */
+size_t csa_compress_workspace_bytes(const CsaCompressArgs* jobs, int n_jobs);
+int csa_compress_batch_ws(const CsaCompressArgs* jobs, int n_jobs, void* workspace, size_t workspace_bytes,
+                          void* stream);
 int csa_index_topk(const CsaIndexArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 int csa_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 int hca_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);

@@ -79,10 +79,14 @@ def load(path: str = LIB_PATH):
     lib.csa_workspace_bytes.argtypes = [C.c_int, _vp]
     lib.csa_compress.argtypes = [C.POINTER(CompressArgs), _vp]
     lib.csa_compress_batch.argtypes = [C.POINTER(CompressArgs), C.c_int, _vp]
+    lib.csa_compress_workspace_bytes.restype = C.c_size_t
+    lib.csa_compress_workspace_bytes.argtypes = [C.POINTER(CompressArgs), C.c_int]
+    lib.csa_compress_batch_ws.argtypes = [C.POINTER(CompressArgs), C.c_int, _vp, C.c_size_t, _vp]
     lib.csa_index_topk.argtypes = [C.POINTER(IndexArgs), _vp, C.c_size_t, _vp]
     lib.csa_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
     lib.hca_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
-    for fn in ("csa_compress", "csa_compress_batch", "csa_index_topk", "csa_attend", "hca_attend"):
+    for fn in ("csa_compress", "csa_compress_batch", "csa_compress_batch_ws", "csa_index_topk", "csa_attend",
+               "hca_attend"):
         getattr(lib, fn).restype = C.c_int
     if lib.csa_abi_version() != ABI_VERSION:
         raise RuntimeError("libcsa.so ABI version mismatch")
@@ -178,10 +182,33 @@ def compress(kv_a, **kw):
     _check(load().csa_compress(C.byref(a), _stream()), "csa_compress")
 
 
-def compress_batch(jobs):
-    """csa_compress_batch over a list of CompressArgs."""
+def compress_batch(jobs, workspace=True):
+    """Compress a list of CompressArgs in one call: csa_compress_batch_ws with a
+    workspace of csa_compress_workspace_bytes (workspace=True: a fresh torch
+    buffer; a uint8 CUDA tensor: that buffer), or csa_compress_batch
+    (workspace=None: every long block pooled by one workgroup)."""
     arr = (CompressArgs * len(jobs))(*jobs)
-    _check(load().csa_compress_batch(arr, len(jobs), _stream()), "csa_compress_batch")
+    lib = load()
+    if workspace is None:
+        _check(lib.csa_compress_batch(arr, len(jobs), _stream()), "csa_compress_batch")
+        return
+    n = lib.csa_compress_workspace_bytes(arr, len(jobs))
+    if n == C.c_size_t(-1).value:
+        raise ValueError("csa_compress_workspace_bytes: invalid job")
+    if workspace is True:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda") if n else None
+    else:
+        ws = workspace
+        if n and (ws.numel() < n or ws.device.type != "cuda"):
+            raise ValueError(f"compress workspace needs {n} device bytes")
+    _check(lib.csa_compress_batch_ws(arr, len(jobs), _ptr(ws), n if ws is None else ws.numel(), _stream()),
+           "csa_compress_batch_ws")
+
+
+def compress_workspace_bytes(jobs):
+    """csa_compress_workspace_bytes of a list of CompressArgs."""
+    arr = (CompressArgs * len(jobs))(*jobs)
+    return load().csa_compress_workspace_bytes(arr, len(jobs))
 
 
 # ---------------------------------------------------------------- index + top-k

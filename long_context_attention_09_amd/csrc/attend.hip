@@ -154,12 +154,6 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-// Cross-lane move within rows of 16 lanes (DPP control CTRL: quad_perm or
-// row_half_mirror), no LDS round trip.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
 
 __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs * kTileBytes];  // BF16 rows
@@ -642,29 +636,55 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
   __syncthreads();
   if (head >= a.H) return;
   const int64_t base = (int64_t)unit * a.n_splits * 64 + hl;
+  // Splits are merged eight at a time, every load of a group in flight
+  // together, against a running maximum: M over the sink logit and the
+  // splits' maxima (output and denominator), Mx over the splits only (LSE).
+  typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+  constexpr int kGroup = 8;
   const float z2 = a.sink[head] * kLog2e;
-  float top = z2, mmax = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ms = a.part_ml[(base + s * 64) * 2];
-    top = fmaxf(top, ms);
-    mmax = fmaxf(mmax, ms);
-  }
-  float den = exp2f(z2 - top), lsum = 0.f;
+  float M = z2, den = 1.0f;                 // den = exp2(z2 - M) + sum l_s exp2(m_s - M)
+  float Mx = -INFINITY, lsum = 0.f;         // lsum = sum l_s exp2(m_s - Mx)
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ms = a.part_ml[(base + s * 64) * 2];
-    if (ms == -INFINITY) continue;
-    const float ls = a.part_ml[(base + s * 64) * 2 + 1];
-    const float wgt = exp2f(ms - top);
-    den += ls * wgt;
-    lsum += ls * exp2f(ms - mmax);
-    // the partial is normalised: its numerator is o * l
-    const float f = ls * wgt;
-    typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-    const f16x8 v = *(const f16x8*)(a.part_o + (base + s * 64) * kD + d0);
+  for (int s0 = 0; s0 < a.n_splits; s0 += kGroup) {
+    float ms[kGroup], ls[kGroup];
+    f16x8 v[kGroup];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] += (float)v[i] * f;
+    for (int j = 0; j < kGroup; ++j) {
+      const int sj = s0 + j < a.n_splits ? s0 + j : s0;
+      const int64_t rj = base + (int64_t)sj * 64;
+      ms[j] = a.part_ml[rj * 2];
+      ls[j] = a.part_ml[rj * 2 + 1];
+      v[j] = *(const f16x8*)(a.part_o + rj * kD + d0);
+    }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (s0 + j >= a.n_splits) ms[j] = -INFINITY;
+      cm = fmaxf(cm, ms[j]);
+    }
+    if (cm == -INFINITY) continue;          // no split of the group saw a row
+    const float nM = fmaxf(M, cm);
+    const float sc = exp2f(M - nM);
+    const float nMx = fmaxf(Mx, cm);
+    const float scx = Mx == -INFINITY ? 0.f : exp2f(Mx - nMx);
+    den *= sc;
+    lsum *= scx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= sc;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (ms[j] == -INFINITY) continue;
+      // the partial is normalised: its numerator is o * l
+      const float f = ls[j] * exp2f(ms[j] - nM);
+      den += f;
+      lsum += ls[j] * exp2f(ms[j] - nMx);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] += (float)v[j][i] * f;
+    }
+    M = nM;
+    Mx = nMx;
   }
+  const float mmax = Mx;
   const float inv = 1.0f / den;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] *= inv;

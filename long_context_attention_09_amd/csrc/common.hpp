@@ -121,6 +121,28 @@ __device__ __forceinline__ void rope_cos_sin(double pos, int u, int d_rope, doub
 
 // ------------------------------------------------------------------ wave helpers
 
+// Cross-lane move within rows of 16 lanes (DPP control CTRL: quad_perm,
+// row_half_mirror or row_mirror), no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes, the same value in every lane: DPP within each row of
+// 16 (lane ^ 1, lane ^ 2, mirrored half rows, mirrored rows), then the four
+// row sums through readlane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -62,20 +62,111 @@ __device__ __forceinline__ void load_row(const T* row, int c0, int d, float* v) 
   }
 }
 
+// Raw 32-bit words of a lane's slice (the VEC case of load_row, split in two so
+// a batch of candidates can have all its loads in flight before any is used).
+template <int KW>
+__device__ __forceinline__ void raw_words(const char* src, uint32_t (&w)[KW]) {
+  if constexpr (KW % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < KW; k += 4) {
+      const u32x4 x = *(const u32x4*)(src + 4 * k);
+      w[k] = x[0]; w[k + 1] = x[1]; w[k + 2] = x[2]; w[k + 3] = x[3];
+    }
+  } else if constexpr (KW == 2) {
+    const u32x2 x = *(const u32x2*)src;
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int k = 0; k < KW; ++k) w[k] = ((const uint32_t*)src)[k];
+  }
+}
+
+template <typename T, int CPT, int KW>
+__device__ __forceinline__ void unpack_words(const uint32_t (&w)[KW], bool in, float* v) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    float x;
+    if constexpr (sizeof(T) == 2) x = bf16_to_f32((uint16_t)((w[k >> 1] >> (16 * (k & 1))) & 0xffffu));
+    else x = __uint_as_float(w[k]);
+    v[k] = in ? x : 0.0f;
+  }
+}
+
 // WIDE: one 512-thread workgroup per entry, its eight wavefronts fold
 // interleaved candidates and merge their running (max, sum, weighted sum)
 // through LDS (the 128-token HCA blocks); otherwise one wavefront per entry.
 // blockIdx.z selects one of up to kMaxJobs independent jobs of one launch.
-template <typename T, int CPT, bool WIDE, bool VEC>
-__global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatch batch) {
-  const CompressLaunch& a = batch.job[blockIdx.z];
-  constexpr int kWaves = WIDE ? 8 : 4;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
-  const int b = blockIdx.y;
-  if (b >= a.B || entry_local >= a.n_entries) return;
-  const int64_t i = a.i_first + entry_local;           // absolute entry index
+// Merge another running (max, sum, weighted sum) state into this one, channel
+// by channel, without branches: where both maxima are -inf the scale factors
+// are exp2(-inf) = 0 and the state stays empty.
+template <int CPT>
+__device__ __forceinline__ void merge_state(float (&mx)[CPT], float (&sm)[CPT], float (&acc)[CPT],
+                                            const float* om, const float* os, const float* oa) {
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const float nm = fmaxf(mx[k], om[k]);
+    const float base = nm == -INFINITY ? 0.f : nm;
+    const float r0 = fast_exp2(mx[k] - base), r1 = fast_exp2(om[k] - base);
+    sm[k] = sm[k] * r0 + os[k] * r1;
+    acc[k] = acc[k] * r0 + oa[k] * r1;
+    mx[k] = nm;
+  }
+}
+
+// Cross-wave state exchange through LDS: wave w > 0 stores its state at slot
+// w - 1 of red ([slots][3][64 * CPT], 16-byte aligned) with 16-byte stores.
+template <int CPT>
+__device__ __forceinline__ void put_state(float* red, int slot, int c0, const float* mx, const float* sm,
+                                          const float* acc) {
+  float* r = red + slot * 3 * 64 * CPT + c0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { r[k] = mx[k]; r[64 * CPT + k] = sm[k]; r[128 * CPT + k] = acc[k]; }
+}
+
+template <int CPT>
+__device__ __forceinline__ void get_state(const float* red, int slot, int c0, float* om, float* os, float* oa) {
+  const float* r = red + slot * 3 * 64 * CPT + c0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { om[k] = r[k]; os[k] = r[64 * CPT + k]; oa[k] = r[128 * CPT + k]; }
+}
+
+// This lane's CPT channels of a pooled candidate group [3][d] (max, sum,
+// weighted sum): 16-byte loads when the lane's slice lies inside the row.
+template <int CPT>
+__device__ __forceinline__ void part_state(const float* q, int c0, int d, float* pm, float* ps, float* pa) {
+  if constexpr (CPT % 4 == 0) {
+    if (c0 + CPT <= d) {
+      uint32_t wm[CPT], ws[CPT], wa[CPT];
+      raw_words<CPT>((const char*)(q + c0), wm);
+      raw_words<CPT>((const char*)(q + d + c0), ws);
+      raw_words<CPT>((const char*)(q + 2 * d + c0), wa);
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        pm[k] = __uint_as_float(wm[k]);
+        ps[k] = __uint_as_float(ws[k]);
+        pa[k] = __uint_as_float(wa[k]);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const bool ok = c0 + k < d;
+    pm[k] = ok ? q[c0 + k] : -INFINITY;
+    ps[k] = ok ? q[d + c0 + k] : 0.f;
+    pa[k] = ok ? q[2 * d + c0 + k] : 0.f;
+  }
+}
+
+// Fold candidates c_first, c_first + c_step, ... (below c_end) of entry i of
+// sequence b into the running per-channel (max, sum, weighted sum) of this
+// lane's CPT channels; softmax in base 2.  Candidate c < m is token m*i + c of
+// the a-branch (bias row c); m <= c < 2m is token m*(i-1) + c - m of the
+// b-branch (bias row c - m).
+template <typename T, int CPT, bool VEC, int kBatch>
+__device__ __forceinline__ void fold_candidates(const CompressLaunch& a, int b, int64_t i, int lane, int c_first,
+                                                int c_step, int c_end, float (&mx)[CPT], float (&sm)[CPT],
+                                                float (&acc)[CPT]) {
   const int c0 = lane * CPT;
   const int d = a.d;
   const int m = a.m;
@@ -83,25 +174,82 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
   const char* base_ga = a.gate_a ? (const char*)a.gate_a + (int64_t)b * a.in_seq_stride : nullptr;
   const char* base_kb = a.kv_b ? (const char*)a.kv_b + (int64_t)b * a.in_seq_stride : nullptr;
   const char* base_gb = a.gate_b ? (const char*)a.gate_b + (int64_t)b * a.in_seq_stride : nullptr;
-  // candidates: c < m is token m*i + c of the a-branch (bias row c); m <= c < 2m
-  // is token m*(i-1) + c - m of the b-branch (bias row c - m); entry 0 has no b-branch
-  const int n_cand = (base_kb && i >= 1) ? 2 * m : m;
-
-  float mx[CPT], sm[CPT], acc[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) { mx[k] = -INFINITY; sm[k] = 0.f; acc[k] = 0.f; }
-
-  const int c_first = WIDE ? wave : 0;
-  const int c_step = WIDE ? kWaves : 1;
-  constexpr int kBatch = CPT >= 16 ? 4 : 8;   // candidates whose loads are in flight together
+  const float* bias_a = a.bias_a;
+  const float* bias_b = a.bias_b;
   // Branch-free batches: a dead slot re-reads candidate 0 and gets logit -inf.
-  for (int cb = c_first; cb < n_cand; cb += kBatch * c_step) {
+  for (int cb = c_first; cb < c_end; cb += kBatch * c_step) {
+    constexpr bool kSplitLoads = VEC && CPT * (int)sizeof(T) >= 4 && CPT <= 8;
+    if constexpr (kSplitLoads) {
+      // Every load of the batch is issued before any is used (kv rows, then
+      // under uniform branches the gate and bias rows); the fold below then
+      // reads each channel straight from the raw words.
+      constexpr int KW = CPT * (int)sizeof(T) / 4, KWB = CPT;
+      const bool in = c0 < d;
+      const int coff = in ? c0 : 0;
+      uint32_t wk[kBatch][KW], wg[kBatch][KW], wb[kBatch][KWB];
+      bool live[kBatch], g_ok[kBatch], b_ok[kBatch];
+      const char* gp[kBatch];
+      const float* bp[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        int c = cb + u * c_step;
+        live[u] = c < c_end;
+        c = live[u] ? c : 0;
+        const bool a_side = c < m;
+        const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
+        const char* kp = (a_side ? base_ka : base_kb) + row * a.in_row_stride + (int64_t)coff * (int64_t)sizeof(T);
+        const char* g = a_side ? base_ga : base_gb;
+        g_ok[u] = in && g != nullptr;
+        gp[u] = g ? g + row * a.in_row_stride + (int64_t)coff * (int64_t)sizeof(T) : kp;
+        const float* bb = a_side ? bias_a : bias_b;
+        b_ok[u] = in && bb != nullptr;
+        bp[u] = bb ? bb + (int64_t)(a_side ? c : c - m) * d + coff : bias_a + coff;
+        raw_words<KW>(kp, wk[u]);
+      }
+      if (base_ga) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) raw_words<KW>(gp[u], wg[u]);
+      }
+      if (bias_a) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) raw_words<KWB>((const char*)bp[u], wb[u]);
+      }
+      auto word_f = [&](const uint32_t* w, int k) -> float {
+        if constexpr (sizeof(T) == 2) return bf16_to_f32((uint16_t)((w[k >> 1] >> (16 * (k & 1))) & 0xffffu));
+        else return __uint_as_float(w[k]);
+      };
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float lg[kBatch];
+        float bm = mx[k];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float zz = (base_ga && g_ok[u]) ? word_f(wg[u], k) : 0.f;
+          const float bz = (bias_a && b_ok[u]) ? __uint_as_float(wb[u][k]) : 0.f;
+          lg[u] = live[u] ? (zz + bz) * kLog2e : -INFINITY;
+          bm = fmaxf(bm, lg[u]);
+        }
+        const float base = bm == -INFINITY ? 0.f : bm;
+        const float r = fast_exp2(mx[k] - base);       // 0 while nothing was folded
+        float sum = sm[k] * r, num = acc[k] * r;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float e = fast_exp2(lg[u] - base);
+          const float vv = in ? word_f(wk[u], k) : 0.f;
+          sum += e;
+          num = fmaf(e, vv, num);
+        }
+        sm[k] = sum;
+        acc[k] = num;
+        mx[k] = bm;
+      }
+    } else {
     float v[kBatch][CPT], z[kBatch][CPT], bias[kBatch][CPT];
     bool live[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       int c = cb + u * c_step;
-      live[u] = c < n_cand;
+      live[u] = c < c_end;
       c = live[u] ? c : 0;
       const bool a_side = c < m;
       const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
@@ -149,31 +297,62 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
       acc[k] = num;
       mx[k] = bm;
     }
+    }
+  }
+}
+
+template <typename T, int CPT, bool WIDE, bool VEC>
+__global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kernel(CompressBatch batch) {
+  const CompressLaunch& a = batch.job[blockIdx.z];
+  constexpr int kWaves = WIDE ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
+  const int b = blockIdx.y;
+  if (b >= a.B || entry_local >= a.n_entries) return;
+  const int64_t i = a.i_first + entry_local;           // absolute entry index
+  const int c0 = lane * CPT;
+  const int d = a.d;
+  const int m = a.m;
+  // entry 0 has no b-branch
+  const int n_cand = (a.kv_b && i >= 1) ? 2 * m : m;
+
+  float mx[CPT], sm[CPT], acc[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { mx[k] = -INFINITY; sm[k] = 0.f; acc[k] = 0.f; }
+
+  if (a.part) {
+    // candidates pooled in n_parts groups by compress_part_kernel: wave w
+    // merges the groups' (max, sum, weighted sum) states w, w + kWaves, ...
+    const float* pp = a.part + ((int64_t)b * a.n_entries + entry_local) * a.n_parts * 3 * d;
+    const int g_first = WIDE ? wave : 0, g_step = WIDE ? kWaves : 1;
+    for (int g = g_first; g < a.n_parts; g += g_step) {
+      const float* q = pp + (int64_t)g * 3 * d;
+      float pm[CPT], ps[CPT], pa[CPT];
+      part_state<CPT>(q, c0, d, pm, ps, pa);
+      merge_state<CPT>(mx, sm, acc, pm, ps, pa);
+    }
+  } else {
+    constexpr int kBatch = CPT >= 16 ? 4 : 8;   // candidates whose loads are in flight together
+    fold_candidates<T, CPT, VEC, kBatch>(a, b, i, lane, WIDE ? wave : 0, WIDE ? kWaves : 1, n_cand, mx, sm, acc);
   }
   if constexpr (WIDE) {
-    __shared__ float red[kWaves - 1][3][64 * CPT];  // waves 1..: max, sum, weighted sum
-    if (wave > 0) {
+    // tree merge, 8 -> 4 -> 2 -> 1 waves; each level has its own LDS slots
+    // (4 + 2 + 1), so one barrier per level
+    __shared__ __attribute__((aligned(16))) float red[(kWaves - 1) * 3 * 64 * CPT];
+    int slot0 = 0;
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        red[wave - 1][0][c0 + k] = mx[k];
-        red[wave - 1][1][c0 + k] = sm[k];
-        red[wave - 1][2][c0 + k] = acc[k];
+    for (int half = kWaves / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half) put_state<CPT>(red, slot0 + wave - half, c0, mx, sm, acc);
+      __syncthreads();
+      if (wave < half) {
+        float om[CPT], os[CPT], oa[CPT];
+        get_state<CPT>(red, slot0 + wave, c0, om, os, oa);
+        merge_state<CPT>(mx, sm, acc, om, os, oa);
       }
+      slot0 += half;
     }
-    __syncthreads();
     if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < kWaves - 1; ++w)
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const float om = red[w][0][c0 + k];
-        const float nm = fmaxf(mx[k], om);
-        if (nm == -INFINITY) continue;
-        const float r0 = fast_exp2(mx[k] - nm), r1 = fast_exp2(om - nm);
-        sm[k] = sm[k] * r0 + red[w][1][c0 + k] * r1;
-        acc[k] = acc[k] * r0 + red[w][2][c0 + k] * r1;
-        mx[k] = nm;
-      }
   }
   float x[CPT];
 #pragma unroll
@@ -183,7 +362,7 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
     float ss = 0.f;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) ss += x[k] * x[k];
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     const float r = 1.0f / sqrtf(ss / (float)d + a.rms_eps);
 #pragma unroll
     for (int k = 0; k < CPT; ++k) x[k] *= r;
@@ -244,6 +423,24 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
   } else if (a.out_fmt == CSA_FMT_FP8_BF16) {
     uint8_t* on = (uint8_t*)a.out0 + (int64_t)b * a.out0_seq_stride + (i - a.out_row0) * a.out0_stride;
     uint16_t* orr = (uint16_t*)((char*)a.out1 + (int64_t)b * a.out1_seq_stride + (i - a.out_row0) * a.out1_stride);
+    if constexpr (CPT == 8) {
+      // a lane's 8 channels are all FP8 or all BF16 when d - d_rope is a
+      // multiple of 8: one 8-byte or 16-byte store where aligned
+      if (c0 + CPT <= d0 && ((uintptr_t)(on + c0) & 7) == 0) {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) w[k >> 2] |= f32_to_e4m3(x[k]) << (8 * (k & 3));
+        *(u32x2*)(on + c0) = (u32x2){w[0], w[1]};
+        return;
+      }
+      if (c0 >= d0 && c0 + CPT <= d && ((uintptr_t)(orr + (c0 - d0)) & 15) == 0) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (uint32_t)f32_to_bf16(x[2 * k]) | ((uint32_t)f32_to_bf16(x[2 * k + 1]) << 16);
+        *(u32x4*)(orr + (c0 - d0)) = w;
+        return;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int c = c0 + k;
@@ -270,8 +467,67 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256) compress_kernel(CompressBatc
   }
 }
 
+// Long blocks (m >= 16) over many workgroups: workgroup (entry, group) folds
+// the kPartCands candidates kPartCands*group .. of one entry over its four
+// wavefronts, merges them through LDS and writes the group's per-channel
+// (max, sum, weighted sum) to a.part; compress_kernel then merges the groups
+// and finishes the entry.  Jobs without a.part are skipped.
+template <typename T, int CPT, bool VEC>
+__global__ void __launch_bounds__(256, 2) compress_part_kernel(CompressBatch batch) {
+  const CompressLaunch& a = batch.job[blockIdx.z];
+  if (!a.part) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.x / a.n_parts, g = blockIdx.x % a.n_parts;
+  const int b = blockIdx.y;
+  if (b >= a.B || e >= a.n_entries) return;
+  const int64_t i = a.i_first + e;
+  const int n_cand = (a.kv_b && i >= 1) ? 2 * a.m : a.m;
+  const int c_lo = g * kPartCands;
+  const int c_end = c_lo + kPartCands < n_cand ? c_lo + kPartCands : n_cand;
+  float mx[CPT], sm[CPT], acc[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) { mx[k] = -INFINITY; sm[k] = 0.f; acc[k] = 0.f; }
+  fold_candidates<T, CPT, VEC, kPartCands / 4>(a, b, i, lane, c_lo + wave, 4, c_end, mx, sm, acc);
+  __shared__ __attribute__((aligned(16))) float red[3 * 3 * 64 * CPT];   // waves 1..3
+  const int c0 = lane * CPT;
+  if (wave > 0) put_state<CPT>(red, wave - 1, c0, mx, sm, acc);
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    float om[CPT], os[CPT], oa[CPT];
+    get_state<CPT>(red, w, c0, om, os, oa);
+    merge_state<CPT>(mx, sm, acc, om, os, oa);
+  }
+  const int d = a.d;
+  float* q = a.part + (((int64_t)b * a.n_entries + e) * a.n_parts + g) * 3 * d;
+  if (CPT % 4 == 0 && c0 + CPT <= d) {
+#pragma unroll
+    for (int k = 0; k < CPT; k += 4) {
+      *(f32x4*)(q + c0 + k) = (f32x4){mx[k], mx[k + 1], mx[k + 2], mx[k + 3]};
+      *(f32x4*)(q + d + c0 + k) = (f32x4){sm[k], sm[k + 1], sm[k + 2], sm[k + 3]};
+      *(f32x4*)(q + 2 * d + c0 + k) = (f32x4){acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (c0 + k < d) {
+        q[c0 + k] = mx[k];
+        q[d + c0 + k] = sm[k];
+        q[2 * d + c0 + k] = acc[k];
+      }
+    }
+  }
+}
+
 template <typename T, int CPT, bool VEC>
 static void launch_cpt(const CompressBatch& bt, int B, int n_entries, bool wide, hipStream_t s) {
+  int n_part_wg = 0;
+  for (int j = 0; j < bt.n_jobs; ++j)
+    if (bt.job[j].part && bt.job[j].n_entries * bt.job[j].n_parts > n_part_wg)
+      n_part_wg = bt.job[j].n_entries * bt.job[j].n_parts;
+  if (n_part_wg > 0) compress_part_kernel<T, CPT, VEC><<<dim3(n_part_wg, B, bt.n_jobs), 256, 0, s>>>(bt);
   if (wide) {
     compress_kernel<T, CPT, true, VEC><<<dim3(n_entries, B, bt.n_jobs), 512, 0, s>>>(bt);
   } else {

@@ -313,20 +313,50 @@ int check_compress_entries(const CsaCompressArgs* a) {
 
 }  // namespace
 
-CSA_EXPORT int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void* stream) {
+namespace {
+
+// Candidate groups per entry when a job's long blocks (m >= 16) are pooled
+// over several workgroups; 0 for short blocks.
+int compress_parts(const CsaCompressArgs* a) {
+  if (a->m < 16) return 0;
+  const int n_cand = a->overlap ? 2 * a->m : a->m;
+  return (n_cand + csa::kPartCands - 1) / csa::kPartCands;
+}
+
+size_t compress_part_bytes(const CsaCompressArgs* a) {
+  const int P = compress_parts(a);
+  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
+  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  if (P == 0 || end <= first) return 0;
+  return align_up((size_t)a->B * (size_t)(end - first) * (size_t)P * 3 * (size_t)a->d * sizeof(float));
+}
+
+int check_compress_jobs(const CsaCompressArgs* jobs, int n_jobs) {
   if (!jobs || n_jobs < 0) return CSA_EINVAL;
   for (int j = 0; j < n_jobs; ++j) {
     int st = check_compress(&jobs[j]);
     if (!st) st = check_compress_entries(&jobs[j]);
     if (st) return st;
   }
-  // one launch per run of up to kMaxJobs jobs of the same input dtype
+  return CSA_OK;
+}
+
+// One launch (two with grouped long blocks) per run of up to kMaxJobs jobs of
+// the same input dtype; ws NULL keeps every block in one workgroup.
+int run_compress_batch(const CsaCompressArgs* jobs, int n_jobs, char* ws, void* stream) {
+  size_t off = 0;
   for (int dt = CSA_DT_F32; dt <= CSA_DT_BF16; ++dt) {
     csa::CompressBatch bt{};
     for (int j = 0; j < n_jobs; ++j) {
       if (jobs[j].in_dtype != dt) continue;
-      if (compress_job(&jobs[j], &bt.job[bt.n_jobs])) ++bt.n_jobs;
-      if (bt.n_jobs == csa::kMaxJobs) {
+      if (!compress_job(&jobs[j], &bt.job[bt.n_jobs])) continue;
+      const size_t pb = ws ? compress_part_bytes(&jobs[j]) : 0;
+      if (pb > 0) {
+        bt.job[bt.n_jobs].part = (float*)(ws + off);
+        bt.job[bt.n_jobs].n_parts = compress_parts(&jobs[j]);
+        off += pb;
+      }
+      if (++bt.n_jobs == csa::kMaxJobs) {
         if (csa::launch_compress(bt, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
         bt.n_jobs = 0;
       }
@@ -334,6 +364,31 @@ CSA_EXPORT int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void*
     if (bt.n_jobs > 0 && csa::launch_compress(bt, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
   }
   return CSA_OK;
+}
+
+}  // namespace
+
+CSA_EXPORT int csa_compress_batch(const CsaCompressArgs* jobs, int n_jobs, void* stream) {
+  const int st = check_compress_jobs(jobs, n_jobs);
+  if (st) return st;
+  return run_compress_batch(jobs, n_jobs, nullptr, stream);
+}
+
+CSA_EXPORT size_t csa_compress_workspace_bytes(const CsaCompressArgs* jobs, int n_jobs) {
+  if (check_compress_jobs(jobs, n_jobs)) return (size_t)-1;
+  size_t total = 0;
+  for (int j = 0; j < n_jobs; ++j) total += compress_part_bytes(&jobs[j]);
+  return total;
+}
+
+CSA_EXPORT int csa_compress_batch_ws(const CsaCompressArgs* jobs, int n_jobs, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  const int st = check_compress_jobs(jobs, n_jobs);
+  if (st) return st;
+  size_t need = 0;
+  for (int j = 0; j < n_jobs; ++j) need += compress_part_bytes(&jobs[j]);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, kAlign))) return CSA_EWORKSPACE;
+  return run_compress_batch(jobs, n_jobs, need > 0 ? (char*)ws : nullptr, stream);
 }
 
 CSA_EXPORT int csa_compress(const CsaCompressArgs* a, void* stream) {

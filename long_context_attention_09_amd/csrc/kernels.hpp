@@ -22,7 +22,12 @@ struct CompressLaunch {
   void* out0;
   void* out1;
   int64_t out0_stride, out0_seq_stride, out1_stride, out1_seq_stride;
+  float* part;               // NULL, or [B][n_entries][n_parts][3][d] pooled candidate groups
+  int32_t n_parts;           // candidate groups of kPartCands per entry (with part)
 };
+
+// Candidates per workgroup when long blocks are pooled in groups.
+constexpr int kPartCands = 16;
 
 // Per-query top-k state kept in the workspace.
 struct TopkState {

@@ -121,14 +121,18 @@ class LayerStep:
     def store_window(self):
         K.compress_batch([self._window_job()])
 
-    def compress_all(self, c=0):
-        """Every store of the step in one batched call: the newest entry (and,
-        for CSA, the newest indexer key) and the raw window rows."""
+    def _all_jobs(self, c=0):
         jobs = [self._main_job(c)]
         if self.s.csa:
             jobs.append(self._index_job(c))
         jobs.append(self._window_job())
-        K.compress_batch(jobs)
+        return jobs
+
+    def compress_all(self, c=0):
+        """Every store of the step in one batched call: the newest entry (and,
+        for CSA, the newest indexer key) and the raw window rows; long blocks
+        are pooled over many workgroups through the step's workspace."""
+        K.compress_batch(self._all_jobs(c), workspace=self.ws_compress)
 
     def index(self, c=0, events=(None, None)):
         """csa_index_topk; `events` = optional HIP event handles recorded around
@@ -159,6 +163,8 @@ class LayerStep:
     def _alloc_workspaces(self):
         s = self.s
         dev = self.out.device
+        n = K.compress_workspace_bytes(self._all_jobs(0))
+        self.ws_compress = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         if s.csa:
             kc, ks = self.keys[0]
             a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,

@@ -130,3 +130,34 @@ def test_attend_validation_and_workspace(K):
     c = _attend_args(K, idx=None, top_k=1024)
     assert lib.csa_attend(C.byref(c), FAKE, 1 << 30, None) == K.CSA_EINVAL   # CSA needs idx
     assert lib.hca_attend(C.byref(a), None, 0, None) == K.CSA_EWORKSPACE
+
+
+def test_compress_workspace_rules(K):
+    """Long blocks (m >= 16) need a workspace for the grouped path; short ones
+    none; a missing or small workspace is refused before anything launches."""
+    import torch
+    lib = K.load()
+
+    def job(m, n_rows, overlap=False, B=2, d=512):
+        a = K.CompressArgs(B=B, n_rows=n_rows, pos0=0, m=m, overlap=1 if overlap else 0, d=d, d_rope=64,
+                           in_dtype=K.DT_BF16, out_fmt=K.FMT_FP8_BF16, do_norm=1, rms_eps=1e-6,
+                           rope_theta=1e4, kv_a=1 << 20, kv_b=(1 << 20) if overlap else None,
+                           in_row_stride=d * 2, in_seq_stride=n_rows * d * 2, out0=1 << 21, out1=1 << 22,
+                           out0_stride=576, out0_seq_stride=576 * 64, out1_stride=576,
+                           out1_seq_stride=576 * 64)
+        return a
+
+    arr = (K.CompressArgs * 1)(job(128, 3 * 128))
+    n = lib.csa_compress_workspace_bytes(arr, 1)
+    # 3 entries x 8 groups of 16 candidates x (max, sum, weighted sum) x 512 channels, fp32, per sequence
+    assert n == 2 * 3 * 8 * 3 * 512 * 4
+    arr = (K.CompressArgs * 2)(job(4, 64, overlap=True), job(1, 5))
+    assert lib.csa_compress_workspace_bytes(arr, 2) == 0
+    bad = job(128, 128)
+    bad.d = 12                       # d % 8 != 0
+    arr = (K.CompressArgs * 1)(bad)
+    assert lib.csa_compress_workspace_bytes(arr, 1) == C.c_size_t(-1).value
+    arr = (K.CompressArgs * 1)(job(128, 128))
+    assert lib.csa_compress_batch_ws(arr, 1, None, 0, None) == K.CSA_EWORKSPACE
+    assert lib.csa_compress_batch_ws(arr, 1, C.c_void_p(1 << 20), 16, None) == K.CSA_EWORKSPACE
+    assert lib.csa_compress_batch_ws(arr, 1, C.c_void_p((1 << 20) + 8), 1 << 20, None) == K.CSA_EWORKSPACE
