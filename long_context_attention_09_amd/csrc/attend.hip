@@ -180,7 +180,22 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   p1 = p1 < list_len ? p1 : list_len;
   const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
 
-  // RoPE table at the query position (fp64 angle), one pair per thread
+  // Prologue, ordered so the query's and the first tiles' loads are in flight
+  // while the RoPE table, the row addresses and the query's norm are formed.
+  // The query operand of the score role: head 32 hh + (lane % 32), dims
+  // 128 dq + 16 s + 8 (lane / 32) + j; RMSNorm over all 512 dims (the four
+  // dim quarters add their sums of squares through LDS), RoPE at t, BF16.
+  const int head_q = hg * 64 + 32 * hh + (lane & 31);
+  const bool q_ok = head_q < a.H;
+  i32x4 qraw[8];
+  bf16x8 qv[8];                              // formed once the row fetches are issued
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok ? head_q : 0)) * kD +
+                           128 * dq + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qraw[s] = *(gbl_i32x4*)(qrow + 16 * s);
+  }
+  // RoPE table at the query position, one pair per thread
   if (tid < kDR / 2) {
     float cs, sn;
     rope_cos_sin((double)L.t, tid, kDR, a.log_theta, &cs, &sn);
@@ -193,59 +208,7 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     const int n_sel = (p1 < L.n_comp ? p1 : L.n_comp) - p0;
     for (int i = tid; i < n_sel; i += kThreads) lidx[i] = src[p0 + i];
   }
-  __syncthreads();
-
-  // ---- query operand of the score role: head 32 hh + (lane % 32), dims
-  //      128 dq + 16 s + 8 (lane / 32) + j; RMSNorm over all 512 dims (the four
-  //      dim quarters add their sums of squares through LDS), RoPE at t, BF16
-  bf16x8 qv[8];
-  {
-    const int head_q = hg * 64 + 32 * hh + (lane & 31);
-    const bool ok = head_q < a.H;
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (ok ? head_q : 0)) * kD +
-                           128 * dq + 8 * (lane >> 5);
-    float x[8][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      i32x4 v = *(gbl_i32x4*)(qrow + 16 * s);
-      if (!ok) v = (i32x4){0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[s][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
-        x[s][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
-        ss += x[s][2 * j] * x[s][2 * j] + x[s][2 * j + 1] * x[s][2 * j + 1];
-      }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    float* ssx = (float*)xs;                 // [hh][dq][32], before the tile loop uses xs
-    if (lane < 32) ssx[(hh * 4 + dq) * 32 + lane] = ss;
-    __syncthreads();
-    ss = ((ssx[(hh * 4 + 0) * 32 + (lane & 31)] + ssx[(hh * 4 + 1) * 32 + (lane & 31)]) +
-          ssx[(hh * 4 + 2) * 32 + (lane & 31)]) + ssx[(hh * 4 + 3) * 32 + (lane & 31)];
-    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[s][j] *= rs;
-    if (dq == 3) {                           // dims 448 .. 511 carry RoPE
-#pragma unroll
-      for (int s = 4; s < 8; ++s) {
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int u = (128 * 3 + 16 * s + 8 * (lane >> 5) + j - kDN) >> 1;
-          const float cs = rope_cs[u], sn = rope_cs[32 + u];
-          const float xe = x[s][j], xo = x[s][j + 1];
-          x[s][j] = xe * cs - xo * sn;
-          x[s][j + 1] = xe * sn + xo * cs;
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[s][j] = u16_as_bf16(f32_to_bf16(x[s][j]));
-  }
+  ATTEND_BARRIER(kWaitLgkm0);
 
   // Row addresses of tile t (list positions p0 + 32t ...): 0 marks a masked row.
   auto tile_addrs = [&](int t) {
@@ -279,7 +242,7 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   };
 #pragma unroll
   for (int t = 0; t < kStages + 2; ++t) tile_addrs(t);
-  __syncthreads();
+  ATTEND_BARRIER(kWaitLgkm0);
 
   // this thread's chunks of a tile
   int ch_slot[kChunkSlots], ch_src[kChunkSlots], ch_dst[kChunkSlots];
@@ -510,19 +473,62 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     ATTEND_BARRIER(kWaitLgkm0);
   };
 
-  // Prologue: tiles 0 .. kStages in flight, tile 0 widened into buffer 0.
-  // Register slot j carries tiles j, j + kStages, ... (the step loop is
-  // unrolled by kStages so every slot is a fixed set of registers).
+  // Prologue (continued): tiles 0 .. kStages requested, the query operand
+  // formed meanwhile, tile 0 widened into buffer 0.  Register slot j carries
+  // tiles j, j + kStages, ... (the step loop is unrolled by kStages so every
+  // slot is a fixed set of registers).
   static_assert(kStages == 2, "the step loop below is unrolled for two register stages");
   i32x4 st0[kChunkSlots], st1[kChunkSlots];
   int lv0, lv1;
+  i32x4 first[kChunkSlots];
+  const int lf = fetch(0, first);
+  lv1 = fetch(1, st1);
+  lv0 = fetch(2, st0);
   {
-    i32x4 first[kChunkSlots];
-    const int lf = fetch(0, first);
-    lv1 = fetch(1, st1);
-    lv0 = fetch(2, st0);
-    commit(0, first, lf);
+    float x[8][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      i32x4 v = qraw[s];
+      if (!q_ok) v = (i32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[s][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
+        x[s][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
+        ss += x[s][2 * j] * x[s][2 * j] + x[s][2 * j + 1] * x[s][2 * j + 1];
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    float* ssx = (float*)xs;                 // [hh][dq][32], before the tile loop uses xs
+    if (lane < 32) ssx[(hh * 4 + dq) * 32 + lane] = ss;
+    ATTEND_BARRIER(kWaitLgkm0);
+    ss = ((ssx[(hh * 4 + 0) * 32 + (lane & 31)] + ssx[(hh * 4 + 1) * 32 + (lane & 31)]) +
+          ssx[(hh * 4 + 2) * 32 + (lane & 31)]) + ssx[(hh * 4 + 3) * 32 + (lane & 31)];
+    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[s][j] *= rs;
+    if (dq == 3) {                           // dims 448 .. 511 carry RoPE
+#pragma unroll
+      for (int s = 4; s < 8; ++s) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int u = (128 * 3 + 16 * s + 8 * (lane >> 5) + j - kDN) >> 1;
+          const float cs = rope_cs[u], sn = rope_cs[32 + u];
+          const float xe = x[s][j], xo = x[s][j + 1];
+          x[s][j] = xe * cs - xo * sn;
+          x[s][j + 1] = xe * sn + xo * cs;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[s][j] = u16_as_bf16(f32_to_bf16(x[s][j]));
   }
+  ATTEND_BARRIER(kWaitLgkm0);               // every wave has read the sums before xs is reused
+  commit(0, first, lf);
   // tile -1 of the first step's output product: zero rows, P = 0, factors 1
   for (int i = tid; i < kTileBytes / 16; i += kThreads)
     *(i32x4*)(tiles + 2 * kTileBytes + 16 * i) = (i32x4){0, 0, 0, 0};
@@ -554,26 +560,36 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   __syncthreads();
   const int64_t unit = (int64_t)br * gridDim.y + hg;
   const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
+  const bool single = a.n_splits == 1;
+  // The normalised output (BF16 with the sink and inverse RoPE when the split
+  // covers the whole list, else the fp16 partial) is staged in LDS as
+  // [64 heads][512 dims] rows of 1040 bytes (the tile buffers are free now),
+  // so the global stores are contiguous 16-byte chunks.
+  uint8_t* stage = tiles;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int hl = 32 * hb + (lane & 31);
     const int head = hg * 64 + hl;
-    if (head >= a.H) continue;
     const float m_h = ml_s[2 * hl], l_h = ml_s[2 * hl + 1];
-    if (a.n_splits == 1) {
-      const float z2 = a.sink[head] * kLog2e;
+    float scale;
+    if (single) {
+      const float z2 = head < a.H ? a.sink[head] * kLog2e : 0.f;
       const float top = fmaxf(m_h, z2);
       const float den = l_h * exp2f(m_h - top) + exp2f(z2 - top);
-      const float inv = exp2f(m_h - top) / den;      // 0 when no row was seen
-      uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
+      scale = exp2f(m_h - top) / den;                 // 0 when no row was seen
+    } else {
+      scale = l_h > 0.f ? 1.0f / l_h : 0.f;
+    }
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
-          float o[4];
+      for (int jb = 0; jb < 4; ++jb) {
+        const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
+        float o[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = acc_o[db][hb][4 * jb + i] * inv;
+        for (int i = 0; i < 4; ++i) o[i] = acc_o[db][hb][4 * jb + i] * scale;
+        uint32_t w0, w1;
+        if (single) {
           if (d0 >= kDN && inv_rope) {
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
@@ -584,34 +600,43 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
               o[i + 1] = xe * sn + xo * cs;
             }
           }
-          const uint32_t w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-          *(i32x2*)(orow + d0) = (i32x2){(int)w0, (int)w1};
+          w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+          w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        } else {
+          typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+          w0 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[0], (_Float16)o[1]});
+          w1 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[2], (_Float16)o[3]});
         }
-      if (a.out_lse && wave == 0 && lane < 32)
-        a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
-            l_h > 0.f ? (m_h + log2f(l_h)) * 0.6931471805599453f : -INFINITY;
-    } else {
-      // partial output normalised by its own denominator, in fp16 (|o| is
-      // bounded by the largest |kv| element, far inside the fp16 range; the
-      // fp16 step is 4x finer than the BF16 output's)
-      const int64_t ps = (unit * a.n_splits + split) * 64 + hl;
-      _Float16* po = a.part_o + ps * kD;
-      const float inv_l = l_h > 0.f ? 1.0f / l_h : 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-          const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
-          const f16x4 h = {(_Float16)(acc_o[db][hb][4 * jb] * inv_l), (_Float16)(acc_o[db][hb][4 * jb + 1] * inv_l),
-                           (_Float16)(acc_o[db][hb][4 * jb + 2] * inv_l), (_Float16)(acc_o[db][hb][4 * jb + 3] * inv_l)};
-          *(f16x4*)(po + d0) = h;
-        }
-      if (wave == 0 && lane < 32) {
+        *(u32x2*)(stage + hl * kRowBytes + 2 * d0) = (u32x2){w0, w1};
+      }
+    if (dq == 0 && (lane >> 5) == 0 && hh == 0 && head < a.H) {   // wave 0, one lane per head
+      if (single) {
+        if (a.out_lse)
+          a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
+              l_h > 0.f ? (m_h + log2f(l_h)) * 0.6931471805599453f : -INFINITY;
+      } else {
+        const int64_t ps = (unit * a.n_splits + split) * 64 + hl;
         a.part_ml[ps * 2] = m_h;
         a.part_ml[ps * 2 + 1] = l_h;
       }
+    }
+  }
+  ATTEND_BARRIER(kWaitLgkm0);
+  // 64 rows x 64 chunks of 16 bytes, 8 per thread, consecutive threads on
+  // consecutive chunks of a row
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = tid + kThreads * k;
+    const int hl = c >> 6, ch = c & 63;
+    const int head = hg * 64 + hl;
+    if (head >= a.H) continue;
+    const i32x4 v = *(const i32x4*)(stage + hl * kRowBytes + 16 * ch);
+    if (single) {
+      uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
+      *(i32x4*)(orow + 8 * ch) = v;
+    } else {
+      _Float16* po = a.part_o + ((unit * a.n_splits + split) * 64 + hl) * kD;
+      *(i32x4*)(po + 8 * ch) = v;
     }
   }
 }

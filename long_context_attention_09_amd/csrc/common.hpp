@@ -105,18 +105,16 @@ __device__ __forceinline__ uint32_t e2m1_code(float x) {
 
 // ------------------------------------------------------------------ RoPE
 
-// cos / sin of pos * theta^(-2u/d_rope), with the angle formed and reduced in
-// fp64: at positions near 2^20 an fp32 angle would be off by ~0.06 rad.
+// cos / sin of pos * theta^(-2u/d_rope): the angle is formed and reduced to
+// one turn in fp64 (at positions near 2^20 an fp32 angle would be off by
+// ~0.06 rad); sin and cos of the reduced angle are taken in fp32.
 __device__ __forceinline__ void rope_cos_sin(double pos, int u, int d_rope, double log_theta,
                                              float* c, float* s) {
   const double inv_freq = exp(-2.0 * (double)u / (double)d_rope * log_theta);
   double ang = pos * inv_freq;
   const double two_pi = 6.283185307179586476925286766559;
-  ang = ang - two_pi * floor(ang / two_pi);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  ang = ang - two_pi * floor(ang * (1.0 / two_pi));
+  sincosf((float)ang, s, c);
 }
 
 // ------------------------------------------------------------------ wave helpers

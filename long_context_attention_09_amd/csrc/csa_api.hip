@@ -182,7 +182,7 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   }
   const int64_t units = (int64_t)a->B * a->n_q * ((a->H + 63) / 64);
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
-  int64_t s_max = (list + 191) / 192;             // at least six 32-entry tiles per split
+  int64_t s_max = (list + 95) / 96;               // at least three 32-entry tiles per split
   if (s > s_max) s = s_max;
   if (!dense) {                                   // a CSA split's indices fit the kernel's stage
     const int64_t s_min = (list + csa::kAttendIdxMax - 1) / csa::kAttendIdxMax;
