@@ -214,14 +214,17 @@ def main():
     n = args.warmup + args.steps
     marks = [[ev.create() for _ in range(8)] for _ in range(n)]
 
+    st = C.c_void_p(stream.cuda_stream)
+    record = ev.h.hipEventRecord
+
     def step(k, m):
         c = k % COPIES
         # op-level marks on the same stream, kernel-level marks through the library hook
-        ev.h.hipEventRecord(C.c_void_p(m[0]), C.c_void_p(stream.cuda_stream))
-        csa.run(c, events={"index": (m[2], m[3])})
-        ev.h.hipEventRecord(C.c_void_p(m[1]), C.c_void_p(stream.cuda_stream))
-        hca.run(c, events={"attend": (m[5], m[6])})
-        ev.h.hipEventRecord(C.c_void_p(m[4]), C.c_void_p(stream.cuda_stream))
+        record(C.c_void_p(m[0]), st)
+        csa.run(c, events={"index": (m[2], m[3])}, stream=st)
+        record(C.c_void_p(m[1]), st)
+        hca.run(c, events={"attend": (m[5], m[6])}, stream=st)
+        record(C.c_void_p(m[4]), st)
 
     ev.h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
     print("[bench] warmup", file=sys.stderr, flush=True)

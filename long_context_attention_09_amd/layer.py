@@ -72,6 +72,7 @@ class LayerStep:
         self.idx = torch.empty(B, s.n_q, max(s.top_k, 1), dtype=torch.int32, device=dev)
         self.ws_index = None
         self.ws_attend = None
+        self._prep = {}
         self._alloc_workspaces()
 
     # ------------------------------------------------------------ pieces
@@ -128,37 +129,52 @@ class LayerStep:
         jobs.append(self._window_job())
         return jobs
 
-    def compress_all(self, c=0):
+    def _prepared(self, c):
+        """The argument structs of copy c's step, built once: every pointer
+        they hold stays valid while this object holds the tensors."""
+        p = self._prep.get(c)
+        if p is None:
+            s = self.s
+            jobs = self._all_jobs(c)
+            arr = (K.CompressArgs * len(jobs))(*jobs)
+            p = {"jobs": arr, "n_jobs": len(jobs)}
+            if s.csa:
+                kc, ks = self.keys[c]
+                p["index"] = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
+                                          top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
+                                          fmt=K.FMT_MXFP4)
+            nope, rope = K.split_main(self.caches[c])
+            wn, wr = K.split_main(self.win)
+            p["attend"] = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0,
+                                        self.inp["sink"], self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
+                                        idx=self.idx if s.csa else None, out_lse=self.lse, d_rope=s.d_r,
+                                        rope_theta=s.theta, fmt=K.FMT_FP8_BF16)
+            self._prep[c] = p
+        return p
+
+    def compress_all(self, c=0, stream=None):
         """Every store of the step in one batched call: the newest entry (and,
         for CSA, the newest indexer key) and the raw window rows; long blocks
         are pooled over many workgroups through the step's workspace."""
-        K.compress_batch(self._all_jobs(c), workspace=self.ws_compress)
+        p = self._prepared(c)
+        st = K._stream() if stream is None else stream
+        K._check(self._fn_compress(p["jobs"], p["n_jobs"], self._ws_c[0], self._ws_c[1], st),
+                 "csa_compress_batch_ws")
 
-    def index(self, c=0, events=(None, None)):
+    def index(self, c=0, events=(None, None), stream=None):
         """csa_index_topk; `events` = optional HIP event handles recorded around
         the scoring kernel."""
-        s = self.s
-        kc, ks = self.keys[c]
-        a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
-                         top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
-                         fmt=K.FMT_MXFP4)
+        a = self._prepared(c)["index"]
         a.ev_start, a.ev_stop = events
-        ws, n = self.ws_index
-        K._check(K.load().csa_index_topk(C.byref(a), K._ptr(ws), n, K._stream()), "csa_index_topk")
+        st = K._stream() if stream is None else stream
+        K._check(self._fn_index(C.byref(a), self._ws_i[0], self._ws_i[1], st), "csa_index_topk")
 
-    def attend(self, c=0, events=(None, None)):
+    def attend(self, c=0, events=(None, None), stream=None):
         """csa_attend / hca_attend; `events` as for index()."""
-        s = self.s
-        nope, rope = K.split_main(self.caches[c])
-        wn, wr = K.split_main(self.win)
-        a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0,
-                          self.inp["sink"], self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
-                          idx=self.idx if s.csa else None, out_lse=self.lse, d_rope=s.d_r,
-                          rope_theta=s.theta, fmt=K.FMT_FP8_BF16)
+        a = self._prepared(c)["attend"]
         a.ev_start, a.ev_stop = events
-        ws, n = self.ws_attend
-        fn = K.load().csa_attend if s.csa else K.load().hca_attend
-        K._check(fn(C.byref(a), K._ptr(ws), n, K._stream()), "attend")
+        st = K._stream() if stream is None else stream
+        K._check(self._fn_attend(C.byref(a), self._ws_a[0], self._ws_a[1], st), "attend")
 
     def _alloc_workspaces(self):
         s = self.s
@@ -180,15 +196,25 @@ class LayerStep:
                           fmt=K.FMT_FP8_BF16)
         n = K.workspace_bytes(K.OP_ATTEND if s.csa else K.OP_HCA_ATTEND, a)
         self.ws_attend = (torch.zeros(max(n, 256), dtype=torch.uint8, device=dev) if n else None, n)
+        # the library entry points and workspace (pointer, bytes) pairs, bound once
+        lib = K.load()
+        self._fn_compress = lib.csa_compress_batch_ws
+        self._fn_index = lib.csa_index_topk
+        self._fn_attend = lib.csa_attend if s.csa else lib.hca_attend
+        self._ws_c = (K._ptr(self.ws_compress), self.ws_compress.numel())
+        self._ws_i = (K._ptr(self.ws_index[0]), self.ws_index[1]) if self.ws_index else (None, 0)
+        self._ws_a = (K._ptr(self.ws_attend[0]), self.ws_attend[1])
 
     # ------------------------------------------------------------ whole step
 
-    def run(self, c=0, events=None):
-        """One full step on the current stream (no synchronisation).  `events`
-        optionally maps 'index' / 'attend' to (start, stop) HIP event handles
-        recorded around the scoring and attention kernels."""
+    def run(self, c=0, events=None, stream=None):
+        """One full step on the current stream (or `stream`, a HIP stream
+        handle), no synchronisation.  `events` optionally maps 'index' /
+        'attend' to (start, stop) HIP event handles recorded around the scoring
+        and attention kernels."""
         ev = events or {}
-        self.compress_all(c)
+        st = K._stream() if stream is None else stream
+        self.compress_all(c, stream=st)
         if self.s.csa:
-            self.index(c, events=ev.get("index", (None, None)))
-        self.attend(c, events=ev.get("attend", (None, None)))
+            self.index(c, events=ev.get("index", (None, None)), stream=st)
+        self.attend(c, events=ev.get("attend", (None, None)), stream=st)
