@@ -47,8 +47,8 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "efc2a997d86bb01488fcb15de9ab2f1d91a05b9b33cd3b7eddb7307744caff13",
-        "fetch_kib": 83282.5, "write_kib": 16512.2},
+        "sha256": "60a846a5d1fe570aebb119dbedc589db114945b7ddbcffb817deca186239b1b8",
+        "fetch_kib": 83314.9, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
         "sha256": "010199161a7230f613b006dfe8881458656fbf6ca628216eee265ac2cdc24b54",
