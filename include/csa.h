@@ -239,7 +239,8 @@ typedef struct CsaIndexArgs {
  *   idx          int32 [B][n_q][top_k] (csa_attend); must be NULL for hca_attend.
  *   sink         fp32 [H].
  *   out_lse      optional fp32 [B][n_q][H].
- * Constraints: FP8_BF16 needs d == 512, d_rope == 64 and H % 16 == 0;
+ * Constraints: FP8_BF16 needs d == 512, d_rope == 64, H % 16 == 0 and row
+ * strides (kv_stride, win_stride) below 2^31 bytes (CSA_EUNSUPPORTED otherwise);
  * F32 needs d <= 512 and H <= 128.  1 <= n_win, win_len >= 0.
  * Workspace: csa_workspace_bytes(CSA_OP_ATTEND / CSA_OP_HCA_ATTEND, &args).
  * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call

@@ -21,11 +21,11 @@ LIB = os.path.join(PKG, "libcsa.so")
 
 SOURCES = ["csa_api.hip", "compress.hip", "index_topk.hip", "attend.hip"]
 
-# Per-source extra flags: MFMA accumulators stay in ordinary VGPRs, so the
-# indexer's ReLU / head-weight epilogue and the attention's softmax rescale
-# work on them in place (no AGPR round trips).
-EXTRA_FLAGS = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags: the indexer's MFMA accumulators stay in ordinary
+# VGPRs, so its ReLU / head-weight epilogue works on them in place (no AGPR
+# round trips).  The attention keeps its output accumulators in AGPRs (one
+# wavefront per SIMD with the full register file).
+EXTRA_FLAGS = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

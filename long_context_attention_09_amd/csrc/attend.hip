@@ -94,48 +94,48 @@ __device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, co
 }
 
 typedef __attribute__((address_space(1))) const i32x4 gbl_i32x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the true max
 
-// Workgroup of 8 wavefronts with two roles per 32-entry tile:
-//  * scores: wave w forms S^T = K Q^T for the 32 heads 32 (w >> 2) .. +31 over
-//    the 128 dims 128 (w & 3) .. +127 (V_MFMA_F32_32X32X16_BF16, 8 per tile);
-//    the four partial blocks of a head half meet in LDS, and wave w sums the
-//    8 heads 32 (w >> 2) + 8 (w & 3) .. +7 and runs their online softmax,
-//    leaving P (BF16) and each head's rescale factor in LDS;
-//  * output: wave w accumulates O^T += V^T P^T for the 64 dims 64 w .. +63 of
-//    all 64 heads, so every V element leaves LDS once per workgroup, through
-//    ds_read_b64_tr_b16 transposing reads.
-// The output product of tile t-1 runs in the same phase as the softmax of
-// tile t (matrix cores and vector ALUs overlap); three tile buffers keep
-// tile t-1 readable while tile t+1 is being widened.
-constexpr int kWaves = 8;
+// Workgroup of 4 wavefronts, one per SIMD, each with the full register file.
+// Wave w owns a quarter of the 512 dims: FP8 dims 128 w .. +127 for w < 3,
+// and FP8 dims 384 .. 447 plus the 64 BF16 RoPE dims for w = 3.  Per
+// 32-entry tile:
+//  * scores: every lane loads 16-byte pieces of one entry row straight from
+//    HBM into registers (three tiles ahead); they are widened FP8 -> BF16 in
+//    registers and used as the A operand of
+//      S^T[32 entries x 64 heads] (partial over the wave's dims) = K Q^T
+//    (V_MFMA_F32_32X32X16_BF16, 16 per tile) with the normalised, rotated,
+//    pre-scaled query as the B operand; the same raw bytes go to the wave's
+//    own slice of an LDS tile, where the output product reads them back
+//    transposed;
+//  * softmax: the four partial score blocks meet in LDS; wave w runs the
+//    online softmax (log2 domain, lazy rescale) of heads 16 w .. +15, four
+//    lanes per head, and leaves P (BF16) and the rescale factors in LDS;
+//  * output: O^T[wave's 128 dims x 64 heads] += V^T P^T (16 MFMAs per tile),
+//    V^T read from the wave's slice by ds_read_b64_tr_b8 (FP8, widened in
+//    registers) or ds_read_b64_tr_b16 (RoPE dims).
+// The score product of tile t runs before the first barrier of a step and
+// the output product of tile t-1 after it, beside the softmax of tile t, so
+// both phases have matrix work.
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowBytes = kD * 2 + 16;                    // BF16 row in LDS + 16-byte pad
-constexpr int kTileBytes = kTile * kRowBytes;             // 32.5 KiB
-constexpr int kTileBufs = 3;
-constexpr int kXsWave = 32 * 128;                         // one wave's partial scores (bytes)
-constexpr int kPRow = 80;                                 // bytes per head in P: 32 BF16 + pad
+constexpr int kVRow = 208;                      // bytes per entry in a wave's slice (192 used)
+constexpr int kVWave = kTile * kVRow;           // one wave's slice of a tile
+constexpr int kVBuf = kWaves * kVWave;          // one tile
+constexpr int kXsRow = 144;                     // one head's 32 partial scores (fp32) + pad
+constexpr int kXsWave = 64 * kXsRow;            // a wave's partial scores
+constexpr int kPRow = 80;                       // bytes per head in P: 32 BF16 + pad
 constexpr int kPBytes = 64 * kPRow;
-
-// Row loads: thread t owns the sixteen-byte chunks t, t + 512 (and threads
-// 128 .. 255 also t + 896) of a tile (chunk c = row c / 36, part c % 36:
-// parts 0..27 hold FP8 dims, 28..35 BF16 RoPE dims) and keeps kStages tiles of
-// them in flight in registers.
-constexpr int kChunkSlots = (kChunksPerTile + kThreads - 1) / kThreads;   // 3
-constexpr int kStages = 2;
-constexpr int kAddrSlots = 8;                             // row-address ring (tiles)
-constexpr int kIdxMax = kAttendIdxMax;                    // selected indices staged per split
-
-// Entry slot k (0..31) of a tile lives in LDS row 16 (k / 16) + 2 h + u + 4 q,
-// where k % 16 = 8 h + 4 u + q.  Slot order is the order the matrix cores sum
-// over (the score MFMA's rows, P's columns, the output MFMA's K index); the
-// row placement makes each 32-lane half of a transposing read (4 rows x 64
-// bytes) and each 16-lane row read fall on distinct banks with rows padded
-// to 1040 bytes, so every fragment address is one register plus immediates.
-__device__ __forceinline__ int slot_row(int k) {
-  return 16 * (k >> 4) + 2 * ((k >> 3) & 1) + ((k >> 2) & 1) + 4 * (k & 3);
-}
+constexpr int kStageRow = kD * 2 + 16;          // output staging: one head's row
+constexpr int kStages = 3;                      // tiles in flight in registers
+constexpr int kXsBuf = kWaves * kXsWave;        // one tile's partial scores
+constexpr int kOffXs = 2 * kVBuf;               // slices, partial scores and P are double-buffered
+constexpr int kOffP = kOffXs + 2 * kXsBuf;
+constexpr int kSmemBytes = kOffP + 2 * kPBytes;
+static_assert(64 * kStageRow <= kOffP, "output staging reuses the tile and score regions");
+constexpr int kIdxMax = kAttendIdxMax;          // selected indices staged per split
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + [15:14], expcnt[6:4], lgkmcnt[11:8])
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -152,24 +152,73 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
     __asm__ __volatile__("" ::: "memory");       \
   } while (0)
 
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+// eight E4M3FN bytes (two dwords, low byte first) -> eight BF16 (exact)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const i32x4 w = {__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                   __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true))};
+  return __builtin_bit_cast(bf16x8, w);
+}
 
+struct AttendShared {
+  uint8_t* sm;       // [2 tiles][4 waves][32 entries][kVRow] | xs[2] | P[2]
+  float* alpha;      // [2][64] rescale factors per head
+  float* ml;         // [64][2] final (max, sum)
+  float* rope;       // cos, sin at the query position
+  float* ssx;        // [4 waves][64 heads] query sums of squares
+  int* lidx;         // staged selected indices (CSA)
+};
 
-__global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kTileBufs * kTileBytes];  // BF16 rows
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves * kXsWave];           // partial scores
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * kPBytes];              // P, two buffers
-  __shared__ float alpha_s[2 * 64];                                               // rescale factors
-  __shared__ float ml_s[2 * 64];                                                  // final (max, sum)
-  __shared__ uint64_t rowa[kAddrSlots * 2 * kTile];                               // [slot][nope|rope][row]
-  __shared__ uint32_t rowmask[kAddrSlots];                                        // live rows per tile
-  __shared__ float rope_cs[64];                                                   // cos, sin at t
-  __shared__ int lidx[kIdxMax];                                                   // staged indices (CSA)
+// Where a lane's entry rows come from (one query, one split).  Addresses are
+// formed without branches: a base, a row and a stride are selected per lane
+// (row strides are below 2^31 bytes, checked on the host).
+struct RowSource {
+  uint64_t kvb0, kvb1, wb0, wb1, dummy;   // entry / window bases of the sequence
+  uint32_t kvs, wns;                      // row strides
+  int p1, n_comp, n_vis, n_w;             // list end, list layout
+  bool gather;                            // entries through staged indices (CSA)
+};
+struct RowPtrs {
+  uint64_t pn, pr;                        // FP8 bytes, RoPE bytes of the row
+  uint32_t live;                          // the tile's live-entry mask
+};
 
+// Row pointers of list position p (sel: its staged index when gathering).
+template <bool kRope>
+__device__ __forceinline__ RowPtrs row_ptrs(const RowSource rs, int p, int sel) {
+  const bool in = p < rs.p1;
+  const bool comp = p < rs.n_comp;
+  const int e = rs.gather ? sel : p;
+  const int w = p - rs.n_comp;
+  const bool ok_c = in && comp && e >= 0 && e < rs.n_vis;
+  const bool ok_w = in && !comp && w < rs.n_w;
+  const uint32_t row = ok_c ? (uint32_t)e : ok_w ? (uint32_t)w : 0u;
+  const uint32_t stride = ok_c ? rs.kvs : rs.wns;
+  const uint64_t off = (uint64_t)row * stride;
+  RowPtrs r;
+  r.pn = (ok_c ? rs.kvb0 : ok_w ? rs.wb0 : rs.dummy) + off;
+  r.pr = kRope ? (ok_c ? rs.kvb1 : ok_w ? rs.wb1 : rs.dummy) + off : 0;
+  r.live = (uint32_t)__ballot(ok_c || ok_w);
+  return r;
+}
+
+// Chunk c of a lane's row pieces: FP8 bytes wdim + 32 c + 16 g (the RoPE
+// wave: chunks 0, 1 at 384 + ..., chunks 2..5 the RoPE bytes 32 (c - 2) + 16 g).
+template <bool kRope>
+__device__ __forceinline__ i32x4 load_chunk(int c, const RowPtrs rp, int wdim, int g) {
+  if (kRope && c >= 2) return *(gbl_i32x4*)(rp.pr + 32 * (c - 2) + 16 * g);
+  return *(gbl_i32x4*)(rp.pn + wdim + 32 * c + 16 * g);
+}
+
+template <bool kRopeWave>
+__device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendShared S, const int wave) {
+  constexpr int NL = kRopeWave ? 6 : 4;     // 16-byte row pieces per lane per tile
+  constexpr int NDT8 = kRopeWave ? 2 : 4;   // 32-dim output tiles read as FP8
+  uint8_t* const sm = S.sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = wave >> 2, dq = wave & 3;
+  const int g = lane >> 5, r32 = lane & 31;
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
@@ -179,382 +228,370 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   int p1 = p0 + a.split_len;
   p1 = p1 < list_len ? p1 : list_len;
   const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
+  const int wdim = 128 * wave;              // first output dim of the wave (wave 3: 384)
 
-  // Prologue, ordered so the query's and the first tiles' loads are in flight
-  // while the RoPE table, the row addresses and the query's norm are formed.
-  // The query operand of the score role: head 32 hh + (lane % 32), dims
-  // 128 dq + 16 s + 8 (lane / 32) + j; RMSNorm over all 512 dims (the four
-  // dim quarters add their sums of squares through LDS), RoPE at t, BF16.
-  const int head_q = hg * 64 + 32 * hh + (lane & 31);
-  const bool q_ok = head_q < a.H;
-  i32x4 qraw[8];
-  bf16x8 qv[8];                              // formed once the row fetches are issued
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok ? head_q : 0)) * kD +
-                           128 * dq + 8 * (lane >> 5);
+  // The 8 dims of k-step s held by lane half g (A and B operands alike).
+  auto kdim = [&](int s) {
+    return (kRopeWave && s >= 4) ? kDN + 16 * (s - 4) + 8 * g : wdim + 32 * (s >> 1) + 16 * g + 8 * (s & 1);
+  };
+
+  // Row pieces of tile t for this lane's entry (list position p0 + 32 t +
+  // lane % 32).  Every load is issued (a masked entry reads harmless bytes:
+  // the query) so the count of loads in flight is the same on every path.
+  RowSource rsrc;
+  rsrc.dummy = (uint64_t)a.q;                // >= 1 KiB of readable bytes
+  rsrc.kvb0 = (uint64_t)a.kv0 + (uint64_t)((int64_t)b * a.kv_seq_stride);
+  rsrc.kvb1 = (uint64_t)a.kv1 + (uint64_t)((int64_t)b * a.kv_seq_stride);
+  rsrc.wb0 = (uint64_t)a.win0 + (uint64_t)((int64_t)b * a.win_seq_stride + (int64_t)L.win_lo * a.win_stride);
+  rsrc.wb1 = (uint64_t)a.win1 + (uint64_t)((int64_t)b * a.win_seq_stride + (int64_t)L.win_lo * a.win_stride);
+  rsrc.kvs = (uint32_t)a.kv_stride;
+  rsrc.wns = (uint32_t)a.win_stride;
+  rsrc.p1 = p1;
+  rsrc.n_comp = L.n_comp;
+  rsrc.n_vis = L.n_vis;
+  rsrc.n_w = L.n_w;
+  rsrc.gather = a.idx != nullptr;
+  // index of tile t's entry for this lane (staged indices; a harmless read
+  // for HCA)
+#define ATTEND_SEL(t) S.lidx[(t) * kTile + r32 < kIdxMax ? (t) * kTile + r32 : kIdxMax - 1]
+  i32x4 kst[kStages][NL];
+  uint32_t kmask[kStages];
+
+  // Prologue: the first tiles' row loads (HCA: at once; CSA: once the
+  // selected indices are staged), query loads, RoPE table, the zero tiles.
+  if (!rsrc.gather) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qraw[s] = *(gbl_i32x4*)(qrow + 16 * s);
+    for (int u = 0; u < kStages; ++u) {
+      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, ATTEND_SEL(u));
+      kmask[u] = rp.live;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
+    }
   }
-  // RoPE table at the query position, one pair per thread
+  i32x4 qraw[2][8];
+  bool q_ok[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head_q = hg * 64 + 32 * ht + r32;
+    q_ok[ht] = head_q < a.H;
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok[ht] ? head_q : 0)) * kD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qraw[ht][s] = *(gbl_i32x4*)(qrow + kdim(s));
+  }
   if (tid < kDR / 2) {
     float cs, sn;
     rope_cos_sin((double)L.t, tid, kDR, a.log_theta, &cs, &sn);
-    rope_cs[tid] = cs;
-    rope_cs[32 + tid] = sn;
+    S.rope[tid] = cs;
+    S.rope[32 + tid] = sn;
   }
-  // the split's selected indices (CSA), staged once
   if (a.idx) {
     const int* src = a.idx + ((int64_t)b * a.n_q + r) * a.top_k;
     const int n_sel = (p1 < L.n_comp ? p1 : L.n_comp) - p0;
-    for (int i = tid; i < n_sel; i += kThreads) lidx[i] = src[p0 + i];
+    for (int i = tid; i < n_sel; i += kThreads) S.lidx[i] = src[p0 + i];
   }
+  // tile -1's slices (buffer 1) and tile -2's P (buffer 0) are zero, its factors 1
+  for (int i = tid; i < kVBuf / 16; i += kThreads) *(i32x4*)(sm + kVBuf + 16 * i) = (i32x4){0, 0, 0, 0};
+  for (int i = tid; i < kPBytes / 16; i += kThreads) *(i32x4*)(sm + kOffP + 16 * i) = (i32x4){0, 0, 0, 0};
+  if (tid < 64) S.alpha[tid] = 1.0f;
   ATTEND_BARRIER(kWaitLgkm0);
-
-  // Row addresses of tile t (list positions p0 + 32t ...): 0 marks a masked row.
-  auto tile_addrs = [&](int t) {
-    if (tid < kTile) {
-      const int p = p0 + t * kTile + tid;
-      uint64_t an = 0, ar = 0;
-      if (p < p1) {
-        if (p < L.n_comp) {
-          const int e = a.idx ? lidx[p - p0] : p;
-          if (!a.idx || (e >= 0 && e < L.n_vis)) {
-            const int64_t off = (int64_t)b * a.kv_seq_stride + (int64_t)e * a.kv_stride;
-            an = (uint64_t)((const uint8_t*)a.kv0 + off);
-            ar = (uint64_t)((const uint8_t*)a.kv1 + off);
-          }
-        } else {
-          const int w = p - L.n_comp;
-          if (w < L.n_w) {
-            const int64_t off = (int64_t)b * a.win_seq_stride + (int64_t)(L.win_lo + w) * a.win_stride;
-            an = (uint64_t)((const uint8_t*)a.win0 + off);
-            ar = (uint64_t)((const uint8_t*)a.win1 + off);
-          }
-        }
-      }
-      // list position p0 + 32 t + tid fills entry slot tid, i.e. LDS row slot_row(tid)
-      uint64_t* slot = rowa + (t % kAddrSlots) * 2 * kTile;
-      slot[slot_row(tid)] = an;
-      slot[kTile + slot_row(tid)] = ar;
-      const uint64_t live = __ballot(an != 0);      // bit k: entry slot k is a real row
-      if (tid == 0) rowmask[t % kAddrSlots] = (uint32_t)live;
+  if (rsrc.gather) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
+      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, ATTEND_SEL(u));
+      kmask[u] = rp.live;
+#pragma unroll
+      for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
     }
-  };
-#pragma unroll
-  for (int t = 0; t < kStages + 2; ++t) tile_addrs(t);
-  ATTEND_BARRIER(kWaitLgkm0);
-
-  // this thread's chunks of a tile
-  int ch_slot[kChunkSlots], ch_src[kChunkSlots], ch_dst[kChunkSlots];
-  bool ch_ok[kChunkSlots], ch_rope[kChunkSlots];
-#pragma unroll
-  for (int k = 0; k < kChunkSlots; ++k) {
-    // chunks 0 .. 1023 to every thread twice, 1024 .. 1151 to waves 2 and 3
-    // (wave 0 also builds the row addresses)
-    const int c = k < 2 ? tid + kThreads * k : 2 * kThreads + tid - 128;
-    ch_ok[k] = k < 2 || (tid >= 128 && tid < 128 + kChunksPerTile - 2 * kThreads);
-    const int cc = ch_ok[k] ? c : 0;
-    const int part = cc % kChunksPerRow;
-    const int row = cc / kChunksPerRow;
-    ch_rope[k] = part >= 28;
-    ch_slot[k] = (ch_rope[k] ? kTile : 0) + row;
-    ch_src[k] = part < 28 ? part * 16 : (part - 28) * 16;
-    ch_dst[k] = row * kRowBytes + (part < 28 ? part * 32 : kDN * 2 + (part - 28) * 16);
   }
-  // Request tile t's chunks into registers.  Every load is issued (a masked
-  // row or a missing chunk reads harmless bytes: the query) so the count of
-  // loads in flight is the same on every path; bit k of the result says
-  // whether chunk k is real data.
-  const uint64_t dummy = (uint64_t)a.q;      // any readable bytes (q holds >= 16 KiB)
-  auto fetch = [&](int t, i32x4 (&v)[kChunkSlots]) {
-    const uint64_t* slot_a = rowa + (t % kAddrSlots) * 2 * kTile;
-    uint64_t base[kChunkSlots];
+
+  // The query operand: head 32 ht + lane % 32, dims kdim(s) .. +7; RMSNorm
+  // over all 512 dims (the four waves add their sums of squares through
+  // LDS), the softmax scale (log2 units), RoPE at the query position, BF16.
+  bf16x8 qv[2][8];
+  {
+    float ss[2];
 #pragma unroll
-    for (int k = 0; k < kChunkSlots; ++k) base[k] = slot_a[ch_slot[k]];   // all requested at once
-    int live = 0;
+    for (int ht = 0; ht < 2; ++ht) {
+      ss[ht] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kChunkSlots; ++k) {
-      const uint64_t bk = ch_ok[k] ? base[k] : 0;
-      live |= (bk != 0) << k;
-      v[k] = *(gbl_i32x4*)((bk ? bk : dummy) + (uint64_t)ch_src[k]);
-    }
-    return live;
-  };
-  // Widen tile t's chunks to BF16 rows in buffer t % 3 (FP8 dims exactly;
-  // zeros for masked rows).
-  auto commit = [&](int t, const i32x4 (&vin)[kChunkSlots], int live) {
-    uint8_t* tile = tiles + (t % kTileBufs) * kTileBytes;
-#pragma unroll
-    for (int k = 0; k < kChunkSlots; ++k) {
-      if (!ch_ok[k]) continue;
-      const i32x4 zero = {0, 0, 0, 0};
-      const i32x4 vk = (live >> k) & 1 ? vin[k] : zero;
-      const i32x4 v[1] = {vk};
-      if (!ch_rope[k]) {
-        // two E4M3 bytes -> two BF16 per instruction (scale 1: exact)
-        i32x4 lo, hi;
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int w0 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[0][j], 1.0f, false));
-          const int w1 = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[0][j], 1.0f, true));
-          if (j < 2) { lo[2 * j] = w0; lo[2 * j + 1] = w1; }
-          else { hi[2 * (j - 2)] = w0; hi[2 * (j - 2) + 1] = w1; }
+          const uint32_t w = q_ok[ht] ? (uint32_t)qraw[ht][s][j] : 0u;
+          const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+          ss[ht] += lo * lo + hi * hi;
         }
-        *(i32x4*)(tile + ch_dst[k]) = lo;
-        *(i32x4*)(tile + ch_dst[k] + 16) = hi;
+      ss[ht] += __shfl_xor(ss[ht], 32, 64);
+    }
+    if (g == 0) {
+      S.ssx[wave * 64 + r32] = ss[0];
+      S.ssx[wave * 64 + 32 + r32] = ss[1];
+    }
+    ATTEND_BARRIER(kWaitLgkm0);
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int h = 32 * ht + r32;
+      const float tot = ((S.ssx[h] + S.ssx[64 + h]) + S.ssx[128 + h]) + S.ssx[192 + h];
+      // RMSNorm and the softmax scale (log2 units) in one factor; RoPE is linear
+      const float rs = ((a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(tot / (float)kD + 1e-6f) : 1.0f) * a.scale_log2;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = q_ok[ht] ? (uint32_t)qraw[ht][s][j] : 0u;
+          x[2 * j] = __uint_as_float(w << 16) * rs;
+          x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
+        }
+        if (kRopeWave && s >= 4) {              // dims 448 .. 511 carry RoPE
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const int u = (16 * (s - 4) + 8 * g + j) >> 1;
+            const float cs = S.rope[u], sn = S.rope[32 + u];
+            const float xe = x[j], xo = x[j + 1];
+            x[j] = xe * cs - xo * sn;
+            x[j + 1] = xe * sn + xo * cs;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[ht][s][j] = (__bf16)x[j];   // nearest even
+      }
+    }
+  }
+
+  f32x16 acc_o[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) acc_o[dt][ht] = (f32x16){};
+  // softmax head of the lane (a quad per head; the four heads of a 16-lane
+  // row are 0, 1, 8, 9 apart so their score rows fall on distinct banks)
+  const int hs = 16 * wave + 2 * (lane >> 4) + ((lane >> 2) & 1) + 8 * ((lane >> 3) & 1);
+  const int qq = lane & 3;                  // its entries 8 qq .. +7
+  float m_run = -INFINITY;   // log2-domain reference max (lags the true max by < the slack)
+  float l_part = 0.f;        // this lane's share of the running denominator
+  const int G = lane >> 4, j16 = lane & 15;
+  // V^T operands of the tile whose output product runs next (zero for tile -2)
+  i32x2 vt8[NDT8][2];
+  i16x4 vt16[2][2][2];
+#pragma unroll
+  for (int dt = 0; dt < NDT8; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vt8[dt][ks] = (i32x2){0, 0};
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) vt16[dt][ks][u] = (i16x4){0, 0, 0, 0};
+  uint32_t live_prev = 0;    // live-entry mask of tile t-1 (tile -1: none)
+
+  // Software pipeline, one barrier per step: step t forms the scores of
+  // tile t, the online softmax of tile t-1 and the output product of tile
+  // t-2, so the matrix cores have work on both sides of the softmax.  Slices,
+  // partial scores, P and the rescale factors are double-buffered (tile t in
+  // buffer t % 2); row pieces sit in register stage t % 3.  Tiles -2 and -1
+  // are empty (zero V, P = 0, factors 1); tiles past the list are masked
+  // (scores -inf: P = 0, the running max and sum unchanged).  n_tiles + 2
+  // steps, in rounds of three.
+  for (int t0 = 0; t0 <= n_tiles + 1; t0 += kStages) {
+#pragma unroll
+    for (int buf = 0; buf < kStages; ++buf) {
+      const int t = t0 + buf;
+      const int par = t & 1;
+      i32x4 (&kr)[NL] = kst[buf];
+      uint32_t& km = kmask[buf];
+      // masked entries of tile t read zeros (rare: a list's last tile, unused selections)
+      const uint32_t live_t = km;
+      if (__builtin_expect(live_t != 0xffffffffu, 0)) {
+        const bool mine = (live_t >> r32) & 1;
+#pragma unroll
+        for (int c = 0; c < NL; ++c) kr[c] = mine ? kr[c] : (i32x4){0, 0, 0, 0};
+      }
+      // LDS reads of the step: P^T and the rescale factors of tile t-2, the
+      // partial scores of tile t-1 (head hs, entries 8 qq .. +7), the staged
+      // index of tile t+3's entry
+      const uint8_t* pb = sm + kOffP + par * kPBytes;
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          pf[ks][ht] = *(const bf16x8*)(pb + (32 * ht + r32) * kPRow + 16 * (2 * ks + g));
+      const float al0 = S.alpha[par * 64 + r32], al1 = S.alpha[par * 64 + 32 + r32];
+      const uint8_t* xr = sm + kOffXs + (par ^ 1) * kXsBuf + hs * kXsRow + 32 * qq;
+      f32x4 x[4][2];
+#pragma unroll
+      for (int src = 0; src < 4; ++src)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) x[src][u] = *(const f32x4*)(xr + src * kXsWave + 16 * u);
+      const int sel = ATTEND_SEL(t + kStages);
+
+      // tile t's raw bytes into the wave's slice
+      uint8_t* vs = sm + par * kVBuf + wave * kVWave + r32 * kVRow;
+      if constexpr (!kRopeWave) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *(i32x4*)(vs + 32 * c + 16 * g) = kr[c];
       } else {
-        *(i32x4*)(tile + ch_dst[k]) = v[0];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) *(i32x4*)(vs + 32 * c + 16 * g) = kr[c];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *(i32x4*)(vs + 64 + 32 * c + 16 * g) = kr[2 + c];
       }
-    }
-  };
-
-  // ---- score role: partial S^T of tile t over this wave's dims, into xs
-  struct KIn {
-    bf16x8 kf[8];
-  };
-  auto scores_load = [&](int t) {
-    KIn in;
-    const uint8_t* tile = tiles + (t % kTileBufs) * kTileBytes;
-    const uint8_t* krow = tile + slot_row(lane & 31) * kRowBytes + 2 * (128 * dq + 8 * (lane >> 5));
+      // partial scores of tile t; each chunk's registers take tile t+3's chunk
+      // once its k-steps are issued
+      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + (t + kStages) * kTile + r32, sel);
+      km = rp.live;
+      f32x16 sc0 = {}, sc1 = {};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) in.kf[s] = *(const bf16x8*)(krow + 32 * s);
-    return in;
-  };
-  auto scores_mma = [&](const KIn& in) {
-    f32x16 s0 = {};
+      for (int c = 0; c < NL; ++c) {
+        if (kRopeWave && c >= 2) {
+          const bf16x8 kop = __builtin_bit_cast(bf16x8, kr[c]);
+          sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[0][c + 2], sc0, 0, 0, 0);
+          sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[1][c + 2], sc1, 0, 0, 0);
+        } else {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in.kf[s], qv[s], s0, 0, 0, 0);
-    // lane holds head (lane % 32), entry slots 8 jb + 4 (lane / 32) + i, i.e.
-    // the 16-byte group k = 2 jb + lane / 32 of that head's 32 scores
-    uint8_t* xw = xs + wave * kXsWave + (lane & 31) * 128;
-    const int sw = ((lane & 31) >> 1) & 7;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-      *(f32x4*)(xw + 16 * ((2 * jb + (lane >> 5)) ^ sw)) =
-          (f32x4){s0[4 * jb], s0[4 * jb + 1], s0[4 * jb + 2], s0[4 * jb + 3]};
-  };
-
-  // ---- softmax role: head sm_head of the group, entries 4 sm_k .. +3
-  const int sm_hloc = 8 * dq + (lane >> 3);                 // head within the head half
-  const int sm_head = 32 * hh + sm_hloc;                    // head within the group
-  const int sm_k = lane & 7;
-  float m_run = -INFINITY;     // log2-domain reference max (lags the true max by < the slack)
-  float l_part = 0.f;          // this lane's share of the running denominator
-  // part 1: the four partial score blocks of the head and the live-row mask
-  struct SmIn {
-    f32x4 x[4];
-    uint32_t live;
-  };
-  auto sm_load = [&](int t) {
-    SmIn in;
-    const int swr = (sm_hloc >> 1) & 7;
-#pragma unroll
-    for (int src = 0; src < 4; ++src)
-      in.x[src] = *(const f32x4*)(xs + (hh * 4 + src) * kXsWave + sm_hloc * 128 + 16 * (sm_k ^ swr));
-    in.live = rowmask[t % kAddrSlots];
-    return in;
-  };
-  // part 2: online softmax, P and the rescale factor to LDS
-  auto sm_compute = [&](int t, const SmIn& in) {
-    const f32x4 sc = ((in.x[0] + in.x[1]) + in.x[2]) + in.x[3];
-    float v[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (in.live >> (4 * sm_k + i)) & 1 ? sc[i] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, v[i]);
-    }
-    mx = fmaxf(mx, dpp_f32<0xB1>(mx));     // lane ^ 1
-    mx = fmaxf(mx, dpp_f32<0x4E>(mx));     // lane ^ 2
-    mx = fmaxf(mx, dpp_f32<0x141>(mx));    // lane 7 - i of each 8: the other quad
-    // the reference max moves only when the tile max overtakes it by the slack,
-    // so O rescales are rare; probabilities stay below 2^slack
-    const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);   // argument <= 0, or -inf
-    float p[4], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(v[i] - m_use);
-      psum += p[i];
-    }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-    const bf16x4 pk = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};   // nearest even
-    *(bf16x4*)(pbuf + (t & 1) * kPBytes + sm_head * kPRow + 8 * sm_k) = pk;
-    if (sm_k == 0) alpha_s[(t & 1) * 64 + sm_head] = alpha;
-  };
-
-  // ---- output role: O^T (dims 64 wave + 32 db + ..., heads 32 hb + ...) += V^T P^T
-  f32x16 acc_o[2][2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) acc_o[db][hb] = (f32x16){};
-  struct PvIn {
-    i16x4 vlo[2][2], vhi[2][2];   // [rs][db]
-    bf16x8 pf[2][2];              // [rs][hb]
-    float al0, al1;
-  };
-  // part 1: V^T fragments (transposing reads), P^T fragments, rescale factors
-  auto pv_load = [&](int tbuf, int pidx) {
-    PvIn in;
-    const uint8_t* tile = tiles + tbuf * kTileBytes;
-    const uint8_t* pb = pbuf + pidx * kPBytes;
-    // transposing reads: lane j of 16-lane group G supplies entry slot
-    // 16 rs + 8 (G / 2) + 4 u + j / 4 (u = 0, 1 for the two reads) at the 4
-    // dims 64 wave + 32 db + 16 (G % 2) + 4 (j % 4) ..; lane j of the group
-    // receives dim j's values of the four slots
-    const int G = lane >> 4, j = lane & 15;
-    const uint8_t* vb = tile + slot_row(8 * (G >> 1) + (j >> 2)) * kRowBytes +
-                        2 * (64 * wave + 16 * (G & 1) + 4 * (j & 3));
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const uint8_t* v0 = vb + 16 * rs * kRowBytes + 64 * db;
-        in.vlo[rs][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)v0);
-        in.vhi[rs][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + kRowBytes));   // u = 1: next row
-      }
-    // P^T: lane supplies head 32 hb + lane % 32, entries 16 rs + 8 (lane / 32) .. +7
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        in.pf[rs][hb] = *(const bf16x8*)(pb + (32 * hb + (lane & 31)) * kPRow + 2 * (16 * rs + 8 * (lane >> 5)));
-    in.al0 = alpha_s[pidx * 64 + (lane & 31)];
-    in.al1 = alpha_s[pidx * 64 + 32 + (lane & 31)];
-    return in;
-  };
-  // part 2: rescale when a running max moved, then 8 MFMAs
-  auto pv_mma = [&](const PvIn& in) {
-    if (__any(in.al0 != 1.0f || in.al1 != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        acc_o[db][0] *= in.al0;
-        acc_o[db][1] *= in.al1;
-      }
-    }
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        bf16x8 vt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vt[i] = u16_as_bf16((uint16_t)in.vlo[rs][db][i]);
-          vt[4 + i] = u16_as_bf16((uint16_t)in.vhi[rs][db][i]);
+          for (int h = 0; h < 2; ++h) {
+            const bf16x8 kop = fp8x8_to_bf16((uint32_t)kr[c][2 * h], (uint32_t)kr[c][2 * h + 1]);
+            sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[0][2 * c + h], sc0, 0, 0, 0);
+            sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[1][2 * c + h], sc1, 0, 0, 0);
+          }
         }
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          acc_o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, in.pf[rs][hb], acc_o[db][hb], 0, 0, 0);
+        kr[c] = load_chunk<kRopeWave>(c, rp, wdim, g);
       }
-  };
 
-  // One pipeline step.  Phase 1: every LDS read of the step's matrix work
-  // goes out at once (K of tile t; V, P and the rescale factors of tile t-1,
-  // whose P was written in the previous step), then O += V P for tile t-1 and
-  // the scores of tile t run on the matrix cores while tile t+1 (fetched
-  // kStages steps ago) is widened into its buffer and tile t + 1 + kStages is
-  // requested into the freed registers.  Barrier.  Phase 2: the softmax of
-  // tile t.  Barrier.  The body is the same on every step: tile -1 is an
-  // all-zero tile with P = 0 and rescale factors 1, and tiles past the list
-  // are masked (scores -inf: P = 0, the running max and sum unchanged).
-  auto step = [&](int t, i32x4 (&cur)[kChunkSlots], int& cur_live) {
-    const PvIn pin = pv_load((t + 2) % kTileBufs, (t + 1) & 1);   // tile t - 1
-    const KIn kin = scores_load(t);
-    pv_mma(pin);
-    scores_mma(kin);
-    commit(t + 1, cur, cur_live);
-    tile_addrs(t + kStages + 2);
-    cur_live = fetch(t + 1 + kStages, cur);
-    ATTEND_BARRIER(kWaitLgkm0);
-    sm_compute(t, sm_load(t));
-    ATTEND_BARRIER(kWaitLgkm0);
-  };
-
-  // Prologue (continued): tiles 0 .. kStages requested, the query operand
-  // formed meanwhile, tile 0 widened into buffer 0.  Register slot j carries
-  // tiles j, j + kStages, ... (the step loop is unrolled by kStages so every
-  // slot is a fixed set of registers).
-  static_assert(kStages == 2, "the step loop below is unrolled for two register stages");
-  i32x4 st0[kChunkSlots], st1[kChunkSlots];
-  int lv0, lv1;
-  i32x4 first[kChunkSlots];
-  const int lf = fetch(0, first);
-  lv1 = fetch(1, st1);
-  lv0 = fetch(2, st0);
-  {
-    float x[8][8];
-    float ss = 0.f;
+      // O rescaled before tile t-2 joins it, when a running max moved (in
+      // place in the accumulation registers)
+      if (__any(al0 != 1.0f || al1 != 1.0f)) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      i32x4 v = qraw[s];
-      if (!q_ok) v = (i32x4){0, 0, 0, 0};
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[s][2 * j] = __uint_as_float(((uint32_t)v[j]) << 16);
-        x[s][2 * j + 1] = __uint_as_float(((uint32_t)v[j]) & 0xffff0000u);
-        ss += x[s][2 * j] * x[s][2 * j] + x[s][2 * j + 1] * x[s][2 * j + 1];
+          for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float e = acc_o[dt][ht][i], tmp;
+              __asm__ __volatile__(
+                  "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                  : "+a"(e), "=&v"(tmp)
+                  : "v"(ht ? al1 : al0));
+              acc_o[dt][ht][i] = e;
+            }
+        __asm__ __volatile__("s_nop 4");      // vector writes before the next matrix read
       }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    float* ssx = (float*)xs;                 // [hh][dq][32], before the tile loop uses xs
-    if (lane < 32) ssx[(hh * 4 + dq) * 32 + lane] = ss;
-    ATTEND_BARRIER(kWaitLgkm0);
-    ss = ((ssx[(hh * 4 + 0) * 32 + (lane & 31)] + ssx[(hh * 4 + 1) * 32 + (lane & 31)]) +
-          ssx[(hh * 4 + 2) * 32 + (lane & 31)]) + ssx[(hh * 4 + 3) * 32 + (lane & 31)];
-    const float rs = (a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(ss / (float)kD + 1e-6f) : 1.0f;
+
+      // tile t's partial scores: lane holds head 32 ht + lane % 32, entries
+      // 8 jb + 4 (lane / 32) + i, i.e. the 16-byte group 2 jb + lane / 32
+      uint8_t* xw = sm + kOffXs + par * kXsBuf + wave * kXsWave;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+      for (int ht = 0; ht < 2; ++ht) {
+        const int head = 32 * ht + r32;
+        const f32x16& sc = ht ? sc1 : sc0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[s][j] *= rs;
-    if (dq == 3) {                           // dims 448 .. 511 carry RoPE
+        for (int jb = 0; jb < 4; ++jb)
+          *(f32x4*)(xw + head * kXsRow + 16 * (2 * jb + g)) =
+              (f32x4){sc[4 * jb], sc[4 * jb + 1], sc[4 * jb + 2], sc[4 * jb + 3]};
+      }
+
+      // O^T += V^T P^T for tile t-2
 #pragma unroll
-      for (int s = 4; s < 8; ++s) {
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int u = (128 * 3 + 16 * s + 8 * (lane >> 5) + j - kDN) >> 1;
-          const float cs = rope_cs[u], sn = rope_cs[32 + u];
-          const float xe = x[s][j], xo = x[s][j + 1];
-          x[s][j] = xe * cs - xo * sn;
-          x[s][j + 1] = xe * sn + xo * cs;
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 vop;
+          if (dt < NDT8) {
+            const int d8 = dt < NDT8 ? dt : 0;
+            vop = fp8x8_to_bf16((uint32_t)vt8[d8][ks][0], (uint32_t)vt8[d8][ks][1]);
+          } else {
+            const int d2 = dt - NDT8 < 0 ? 0 : dt - NDT8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              vop[i] = u16_as_bf16((uint16_t)vt16[d2][ks][0][i]);
+              vop[4 + i] = u16_as_bf16((uint16_t)vt16[d2][ks][1][i]);
+            }
+          }
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht)
+            acc_o[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[ks][ht], acc_o[dt][ht], 0, 0, 0);
         }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[s][j] = u16_as_bf16(f32_to_bf16(x[s][j]));
-  }
-  ATTEND_BARRIER(kWaitLgkm0);               // every wave has read the sums before xs is reused
-  commit(0, first, lf);
-  // tile -1 of the first step's output product: zero rows, P = 0, factors 1
-  for (int i = tid; i < kTileBytes / 16; i += kThreads)
-    *(i32x4*)(tiles + 2 * kTileBytes + 16 * i) = (i32x4){0, 0, 0, 0};
-  for (int i = tid; i < kPBytes / 16; i += kThreads) *(i32x4*)(pbuf + kPBytes + 16 * i) = (i32x4){0, 0, 0, 0};
-  if (tid < 64) alpha_s[64 + tid] = 1.0f;
-  ATTEND_BARRIER(kWaitLgkm0);
-  // Whole rounds of kStages steps (n_tiles + 1 steps are needed: the last one
-  // only accumulates the final tile), so every path issues the same loads and
-  // the compiler's count of loads in flight stays exact.
-  for (int t = 0; t <= n_tiles; t += kStages) {
-    step(t, st1, lv1);               // widens t+1 (slot 1), then fetches t+3 into it
-    step(t + 1, st0, lv0);
-  }
 
+      // online softmax of tile t-1 for head hs
+      {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 s4 = ((x[0][u] + x[1][u]) + x[2][u]) + x[3][u];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * u + i] = s4[i];
+        }
+        if (__builtin_expect(live_prev != 0xffffffffu, 0)) {   // masked entries: -inf
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = (live_prev >> (8 * qq + i)) & 1 ? v[i] : -INFINITY;
+        }
+        float mx = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, v[i]);
+        mx = fmaxf(mx, dpp_f32<0xB1>(mx));     // lane ^ 1
+        mx = fmaxf(mx, dpp_f32<0x4E>(mx));     // lane ^ 2
+        // the reference max moves only when the tile max overtakes it by the
+        // slack, so O rescales are rare; probabilities stay below 2^slack
+        const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);   // argument <= 0, or -inf
+        float psum = 0.f;
+        bf16x8 pk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p = fast_exp2(v[i] - m_use);
+          psum += p;
+          pk[i] = (__bf16)p;                   // nearest even
+        }
+        l_part = l_part * alpha + psum;
+        m_run = m_new;
+        *(bf16x8*)(sm + kOffP + (par ^ 1) * kPBytes + hs * kPRow + 16 * qq) = pk;
+        if (qq == 0) S.alpha[(par ^ 1) * 64 + hs] = alpha;
+      }
+      live_prev = live_t;
+
+      // V^T of tile t-1 from the wave's slice, for the next step's output product
+      const uint8_t* vw = sm + (par ^ 1) * kVBuf + wave * kVWave;
+#pragma unroll
+      for (int dt = 0; dt < NDT8; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          // lanes 2i, 2i+1 of a 16-lane group supply entry 16 ks + 8 (G / 2) + i,
+          // bytes 32 dt + 16 (G % 2) + 8 (j % 2); lane j receives byte j of the 8 entries
+          const int row = 16 * ks + 8 * (G >> 1) + (j16 >> 1);
+          vt8[dt][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)(vw + row * kVRow + 32 * dt + 16 * (G & 1) + 8 * (j16 & 1)));
+        }
+      if constexpr (kRopeWave) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              // lane j supplies entry 16 ks + 8 (G / 2) + 4 u + j / 4 at the 4 RoPE
+              // dims 32 dt + 16 (G % 2) + 4 (j % 4); receives dim j's 4 entries
+              const int row = 16 * ks + 8 * (G >> 1) + 4 * u + (j16 >> 2);
+              vt16[dt][ks][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)(vw + row * kVRow + 64 + 2 * (32 * dt + 16 * (G & 1) + 4 * (j16 & 3))));
+            }
+      }
+      ATTEND_BARRIER(kWaitLgkm0);
+    }
+  }
   // the trailing fetches (past the list) must land before the wave ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  // ---- epilogue: the softmax role publishes each head's (max, sum)
+  // ---- epilogue: each head's (max, sum) from its softmax lanes
   {
     float l_run = l_part;
-    l_run += __shfl_xor(l_run, 1, 64);
-    l_run += __shfl_xor(l_run, 2, 64);
-    l_run += __shfl_xor(l_run, 4, 64);
-    if (sm_k == 0) {
-      ml_s[2 * sm_head] = m_run;
-      ml_s[2 * sm_head + 1] = l_run;
+    l_run += dpp_f32<0xB1>(l_run);
+    l_run += dpp_f32<0x4E>(l_run);
+    if (qq == 0) {
+      S.ml[2 * hs] = m_run;
+      S.ml[2 * hs + 1] = l_run;
     }
   }
   __syncthreads();
@@ -563,14 +600,13 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   const bool single = a.n_splits == 1;
   // The normalised output (BF16 with the sink and inverse RoPE when the split
   // covers the whole list, else the fp16 partial) is staged in LDS as
-  // [64 heads][512 dims] rows of 1040 bytes (the tile buffers are free now),
-  // so the global stores are contiguous 16-byte chunks.
-  uint8_t* stage = tiles;
+  // [64 heads][512 dims] rows, so the global stores are contiguous 16-byte chunks.
+  uint8_t* stage = sm;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int hl = 32 * hb + (lane & 31);
+  for (int ht = 0; ht < 2; ++ht) {
+    const int hl = 32 * ht + r32;
     const int head = hg * 64 + hl;
-    const float m_h = ml_s[2 * hl], l_h = ml_s[2 * hl + 1];
+    const float m_h = S.ml[2 * hl], l_h = S.ml[2 * hl + 1];
     float scale;
     if (single) {
       const float z2 = head < a.H ? a.sink[head] * kLog2e : 0.f;
@@ -581,20 +617,20 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
       scale = l_h > 0.f ? 1.0f / l_h : 0.f;
     }
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
-        const int d0 = 64 * wave + 32 * db + 8 * jb + 4 * (lane >> 5);
+        const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc_o[db][hb][4 * jb + i] * scale;
+        for (int i = 0; i < 4; ++i) o[i] = acc_o[dt][ht][4 * jb + i] * scale;
         uint32_t w0, w1;
         if (single) {
-          if (d0 >= kDN && inv_rope) {
+          if (kRopeWave && dt >= NDT8 && inv_rope) {
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
               const int u = (d0 + i - kDN) >> 1;
-              const float cs = rope_cs[u], sn = -rope_cs[32 + u];   // rotation by -t
+              const float cs = S.rope[u], sn = -S.rope[32 + u];   // rotation by -t
               const float xe = o[i], xo = o[i + 1];
               o[i] = xe * cs - xo * sn;
               o[i + 1] = xe * sn + xo * cs;
@@ -607,9 +643,9 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
           w0 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[0], (_Float16)o[1]});
           w1 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[2], (_Float16)o[3]});
         }
-        *(u32x2*)(stage + hl * kRowBytes + 2 * d0) = (u32x2){w0, w1};
+        *(u32x2*)(stage + hl * kStageRow + 2 * d0) = (u32x2){w0, w1};
       }
-    if (dq == 0 && (lane >> 5) == 0 && hh == 0 && head < a.H) {   // wave 0, one lane per head
+    if (wave == 0 && g == 0 && head < a.H) {        // one lane per head
       if (single) {
         if (a.out_lse)
           a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
@@ -622,15 +658,15 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
     }
   }
   ATTEND_BARRIER(kWaitLgkm0);
-  // 64 rows x 64 chunks of 16 bytes, 8 per thread, consecutive threads on
+  // 64 rows x 64 chunks of 16 bytes, 16 per thread, consecutive threads on
   // consecutive chunks of a row
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 16; ++k) {
     const int c = tid + kThreads * k;
     const int hl = c >> 6, ch = c & 63;
     const int head = hg * 64 + hl;
     if (head >= a.H) continue;
-    const i32x4 v = *(const i32x4*)(stage + hl * kRowBytes + 16 * ch);
+    const i32x4 v = *(const i32x4*)(stage + hl * kStageRow + 16 * ch);
     if (single) {
       uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
       *(i32x4*)(orow + 8 * ch) = v;
@@ -641,6 +677,18 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   }
 }
 
+__global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kSmemBytes];
+  __shared__ float alpha_s[2 * 64];
+  __shared__ float ml_s[2 * 64];
+  __shared__ float rope_cs[64];
+  __shared__ float ssx[kWaves * 64];
+  __shared__ int lidx[kIdxMax];
+  const AttendShared S{sm, alpha_s, ml_s, rope_cs, ssx, lidx};
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave == 3) attend_wave<true>(a, S, wave);
+  else attend_wave<false>(a, S, wave);
+}
 // Merge the split partials: workgroup (unit, head quad), 64 threads per head,
 // 8 dims each.
 __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) {

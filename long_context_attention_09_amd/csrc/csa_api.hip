@@ -149,6 +149,7 @@ int check_attend(const CsaAttendArgs* a, bool dense) {
     if (!aligned(a->out, 8)) return CSA_EINVAL;
     if (a->kv_stride % 16 || a->kv_seq_stride % 16 || a->win_stride % 16 || a->win_seq_stride % 16)
       return CSA_EINVAL;
+    if (a->kv_stride >= ((int64_t)1 << 31) || a->win_stride >= ((int64_t)1 << 31)) return CSA_EUNSUPPORTED;
   } else if (a->fmt == CSA_FMT_F32) {
     if (a->d > 512 || (a->d & 1) || a->H > 65535) return CSA_EUNSUPPORTED;
     const void* ps[3] = {a->q, a->kv0, a->win0};
