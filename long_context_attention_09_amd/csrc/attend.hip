@@ -42,6 +42,7 @@ constexpr int kChunksPerRow = kDN / 16 + (kDR * 2) / 16;  // 28 + 8 = 36 sixteen
 constexpr int kChunksPerTile = kTile * kChunksPerRow;     // 1152
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 struct ListInfo {
   int n_comp;     // compressed part of the list (top_k for CSA, n_vis for HCA)
@@ -222,18 +223,42 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
-  const ListInfo L = list_info(a, b, r);
-  const int list_len = L.n_comp + L.n_w;
   const int p0 = split * a.split_len;
-  int p1 = p0 + a.split_len;
-  p1 = p1 < list_len ? p1 : list_len;
-  const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
   const int wdim = 128 * wave;              // first output dim of the wave (wave 3: 384)
 
   // The 8 dims of k-step s held by lane half g (A and B operands alike).
   auto kdim = [&](int s) {
     return (kRopeWave && s >= 4) ? kDN + 16 * (s - 4) + 8 * g : wdim + 32 * (s >> 1) + 16 * g + 8 * (s & 1);
   };
+
+  // Prologue.  Loads that do not depend on the list layout go first, so
+  // their latencies overlap: the query, the sink logits and (CSA) the first
+  // tiles' selected indices; then the layout (query position, visible
+  // entries, window start) and the first tiles' row loads.
+  i32x4 qraw[2][8];
+  bool q_ok[2];
+  float sink_raw[2];                         // the heads' sink logits, used by the epilogue
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head_q = hg * 64 + 32 * ht + r32;
+    q_ok[ht] = head_q < a.H;
+    sink_raw[ht] = a.sink[q_ok[ht] ? head_q : 0];
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok[ht] ? head_q : 0)) * kD;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qraw[ht][s] = *(gbl_i32x4*)(qrow + kdim(s));
+  }
+  const int* const idx_row = a.idx ? a.idx + ((int64_t)b * a.n_q + r) * a.top_k : nullptr;
+  int sel0[kStages];                         // first tiles' selected indices (a harmless read for HCA)
+#pragma unroll
+  for (int u = 0; u < kStages; ++u) {
+    const int pos = p0 + u * kTile + r32;
+    sel0[u] = a.idx ? idx_row[pos < a.top_k ? pos : 0] : ((const int*)a.q)[r32];
+  }
+  const ListInfo L = list_info(a, b, r);
+  const int list_len = L.n_comp + L.n_w;
+  int p1 = p0 + a.split_len;
+  p1 = p1 < list_len ? p1 : list_len;
+  const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
 
   // Row pieces of tile t for this lane's entry (list position p0 + 32 t +
   // lane % 32).  Every load is issued (a masked entry reads harmless bytes:
@@ -251,32 +276,16 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   rsrc.n_vis = L.n_vis;
   rsrc.n_w = L.n_w;
   rsrc.gather = a.idx != nullptr;
-  // index of tile t's entry for this lane (staged indices; a harmless read
-  // for HCA)
+  // index of tile t's entry for this lane (tiles from kStages on: staged in LDS)
 #define ATTEND_SEL(t) S.lidx[(t) * kTile + r32 < kIdxMax ? (t) * kTile + r32 : kIdxMax - 1]
   i32x4 kst[kStages][NL];
   uint32_t kmask[kStages];
-
-  // Prologue: the first tiles' row loads (HCA: at once; CSA: once the
-  // selected indices are staged), query loads, RoPE table, the zero tiles.
-  if (!rsrc.gather) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, ATTEND_SEL(u));
-      kmask[u] = rp.live;
+  for (int u = 0; u < kStages; ++u) {
+    const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, sel0[u]);
+    kmask[u] = rp.live;
 #pragma unroll
-      for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
-    }
-  }
-  i32x4 qraw[2][8];
-  bool q_ok[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int head_q = hg * 64 + 32 * ht + r32;
-    q_ok[ht] = head_q < a.H;
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok[ht] ? head_q : 0)) * kD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qraw[ht][s] = *(gbl_i32x4*)(qrow + kdim(s));
+    for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
   }
   if (tid < kDR / 2) {
     float cs, sn;
@@ -294,15 +303,6 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   for (int i = tid; i < kPBytes / 16; i += kThreads) *(i32x4*)(sm + kOffP + 16 * i) = (i32x4){0, 0, 0, 0};
   if (tid < 64) S.alpha[tid] = 1.0f;
   ATTEND_BARRIER(kWaitLgkm0);
-  if (rsrc.gather) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, ATTEND_SEL(u));
-      kmask[u] = rp.live;
-#pragma unroll
-      for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
-    }
-  }
 
   // The query operand: head 32 ht + lane % 32, dims kdim(s) .. +7; RMSNorm
   // over all 512 dims (the four waves add their sums of squares through
@@ -459,6 +459,14 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
         }
         kr[c] = load_chunk<kRopeWave>(c, rp, wdim, g);
       }
+      // issue order: every score MFMA followed by one LDS access and a few
+      // vector ops, so the LDS traffic spreads under the matrix work
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+      }
 
       // O rescaled before tile t-2 joins it, when a running max moved (in
       // place in the accumulation registers)
@@ -578,6 +586,14 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
                   (lds_i16x4*)(vw + row * kVRow + 64 + 2 * (32 * dt + 16 * (G & 1) + 4 * (j16 & 3))));
             }
       }
+      // issue order: every output MFMA followed by one LDS access and the
+      // softmax's vector work
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x080, 1, 1);   // LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);   // VALU
+      }
       ATTEND_BARRIER(kWaitLgkm0);
     }
   }
@@ -602,30 +618,33 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   // covers the whole list, else the fp16 partial) is staged in LDS as
   // [64 heads][512 dims] rows, so the global stores are contiguous 16-byte chunks.
   uint8_t* stage = sm;
+  float scale[2], m_h[2], l_h[2];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int hl = 32 * ht + r32;
-    const int head = hg * 64 + hl;
-    const float m_h = S.ml[2 * hl], l_h = S.ml[2 * hl + 1];
-    float scale;
+    m_h[ht] = S.ml[2 * hl];
+    l_h[ht] = S.ml[2 * hl + 1];
     if (single) {
-      const float z2 = head < a.H ? a.sink[head] * kLog2e : 0.f;
-      const float top = fmaxf(m_h, z2);
-      const float den = l_h * exp2f(m_h - top) + exp2f(z2 - top);
-      scale = exp2f(m_h - top) / den;                 // 0 when no row was seen
+      const float z2 = q_ok[ht] ? sink_raw[ht] * kLog2e : 0.f;
+      const float top = fmaxf(m_h[ht], z2);
+      const float e_m = exp2f(m_h[ht] - top);
+      scale[ht] = e_m / (l_h[ht] * e_m + exp2f(z2 - top));   // 0 when no row was seen
     } else {
-      scale = l_h > 0.f ? 1.0f / l_h : 0.f;
+      scale[ht] = l_h[ht] > 0.f ? 1.0f / l_h[ht] : 0.f;
     }
+  }
+  // lane holds dims wdim + 32 dt + 8 jb + 4 (lane / 32) + i of head 32 ht + lane % 32
+  if (single) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
-        float o[4];
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc_o[dt][ht][4 * jb + i] * scale;
-        uint32_t w0, w1;
-        if (single) {
+        for (int jb = 0; jb < 4; ++jb) {
+          const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = acc_o[dt][ht][4 * jb + i] * scale[ht];
           if (kRopeWave && dt >= NDT8 && inv_rope) {
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
@@ -636,44 +655,52 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
               o[i + 1] = xe * sn + xo * cs;
             }
           }
-          w0 = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-          w1 = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-        } else {
-          typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-          w0 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[0], (_Float16)o[1]});
-          w1 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)o[2], (_Float16)o[3]});
+          const bf16x4 w = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};   // nearest even
+          *(bf16x4*)(stage + (32 * ht + r32) * kStageRow + 2 * d0) = w;
         }
-        *(u32x2*)(stage + hl * kStageRow + 2 * d0) = (u32x2){w0, w1};
-      }
-    if (wave == 0 && g == 0 && head < a.H) {        // one lane per head
+  } else {
+    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
+          f16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (_Float16)(acc_o[dt][ht][4 * jb + i] * scale[ht]);
+          *(f16x4*)(stage + (32 * ht + r32) * kStageRow + 2 * d0) = w;
+        }
+  }
+  if (wave == 0 && g == 0) {                 // one lane per head
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int hl = 32 * ht + r32;
+      const int head = hg * 64 + hl;
+      if (head >= a.H) continue;
       if (single) {
         if (a.out_lse)
           a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
-              l_h > 0.f ? (m_h + log2f(l_h)) * 0.6931471805599453f : -INFINITY;
+              l_h[ht] > 0.f ? (m_h[ht] + log2f(l_h[ht])) * 0.6931471805599453f : -INFINITY;
       } else {
         const int64_t ps = (unit * a.n_splits + split) * 64 + hl;
-        a.part_ml[ps * 2] = m_h;
-        a.part_ml[ps * 2 + 1] = l_h;
+        a.part_ml[ps * 2] = m_h[ht];
+        a.part_ml[ps * 2 + 1] = l_h[ht];
       }
     }
   }
   ATTEND_BARRIER(kWaitLgkm0);
   // 64 rows x 64 chunks of 16 bytes, 16 per thread, consecutive threads on
-  // consecutive chunks of a row
+  // consecutive chunks of a row (a row per wave and pass)
+  uint8_t* const obase = single ? (uint8_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + hg * 64) * (kD * 2)
+                                : (uint8_t*)(a.part_o + (unit * a.n_splits + split) * 64 * kD);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const int c = tid + kThreads * k;
-    const int hl = c >> 6, ch = c & 63;
-    const int head = hg * 64 + hl;
-    if (head >= a.H) continue;
-    const i32x4 v = *(const i32x4*)(stage + hl * kStageRow + 16 * ch);
-    if (single) {
-      uint16_t* orow = (uint16_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
-      *(i32x4*)(orow + 8 * ch) = v;
-    } else {
-      _Float16* po = a.part_o + ((unit * a.n_splits + split) * 64 + hl) * kD;
-      *(i32x4*)(po + 8 * ch) = v;
-    }
+    const int hl = 4 * k + wave;
+    if (hg * 64 + hl >= a.H) break;
+    const i32x4 v = *(const i32x4*)(stage + hl * kStageRow + 16 * lane);
+    *(i32x4*)(obase + (int64_t)hl * (kD * 2) + 16 * lane) = v;
   }
 }
 
