@@ -45,10 +45,10 @@
 
 namespace csa {
 
-constexpr int kTilesPerWave = 64;                    // 16 keys per tile: 1024 keys per wave
+constexpr int kTilesPerWave = 16;                    // 16 keys per tile: 256 keys per wave
 constexpr int kRing = 8;                             // tiles of keys in flight per wave
-constexpr int kWaveKeys = kTilesPerWave * 16;        // 1024
-constexpr int kKeysPerWG = 4 * kWaveKeys;            // 4096
+constexpr int kWaveKeys = kTilesPerWave * 16;        // 256
+constexpr int kKeysPerWG = 4 * kWaveKeys;            // 1024
 constexpr int kChunk = 4096;                         // scores per workgroup in collect / write
 constexpr int kBins1 = 4096;                         // 12-bit first digit
 constexpr int kShift1 = 20;
@@ -156,11 +156,18 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   }
   __syncthreads();
 
-  const int64_t key_base = (int64_t)blockIdx.x * kKeysPerWG + wave * (kTilesPerWave * 16);
+  // Key groups of 64 (four 16-key tiles) are dealt to the waves of the
+  // sequence round-robin: wave W scores groups W, W + NW, W + 2 NW, ... so
+  // the waves of the grid stream one contiguous front of the key cache
+  // (HBM serves that faster than one private stream per wave).
+  const int NW = 4 * (int)gridDim.x;                         // waves per sequence
+  const int W = (int)blockIdx.x * 4 + wave;
+  constexpr int kGroups = kTilesPerWave / 4;                 // groups per wave
+  const int ngv = (nvis_max + 63) / 64;                      // groups with a visible key
   const uint8_t* kc = (const uint8_t*)a.k0 + (int64_t)b * a.n_cap * 64;
   const uint32_t* ks = (const uint32_t*)a.k1 + (int64_t)b * a.n_cap;
 
-  if (key_base < nvis_max) {
+  if (W < ngv) {
     // query operands: head (16 hg + col), bytes 16g .. 16g+15 of its 64-byte row
     i32x4 qa[QT][4];
     int qs[QT][4];
@@ -180,47 +187,44 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         }
       }
     }
-    // Keys and scores go through per-wave buffer resources that cover only
-    // this wave's keys (and only visible keys for the loads): the hardware
-    // range check returns zeros for loads past the end and drops stores past
-    // it, so no memory instruction in the loop is conditional.  That keeps
-    // the compiler's count of loads in flight exact across iterations, and
-    // the ring stays full instead of draining once per round.
-    const int64_t vis_here = (int64_t)nvis_max - key_base;             // > 0
-    const uint32_t n_load = (uint32_t)(vis_here < kWaveKeys ? vis_here : kWaveKeys);
-    const int64_t cap_here = (int64_t)a.n_cap - key_base;              // >= vis_here
-    const uint32_t n_store = (uint32_t)(cap_here < kWaveKeys ? cap_here : kWaveKeys);
+    // Keys and scores go through buffer resources over the sequence (only
+    // visible keys for the loads): the hardware range check returns zeros
+    // for loads past the end and drops stores past it, so no memory
+    // instruction in the loop is conditional.  That keeps the compiler's
+    // count of loads in flight exact across iterations, and the ring stays
+    // full instead of draining once per round.  (Byte offsets fit 32 bits:
+    // n_cap <= 4M keys.)
     const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kc + key_base * 64), 0, (int)(n_load * 64u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)((uint32_t)nvis_max * 64u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(ks + key_base), 0, (int)(n_load * 4u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)((uint32_t)nvis_max * 4u), kBufferWord3);
     __amdgpu_buffer_rsrc_t rsc[QT];
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) {
       const bool live = r0 + qi < a.n_qb;
-      float* srow = a.scores + ((int64_t)b * a.n_qb + (live ? r0 + qi : r0)) * a.n_cap + key_base;
-      rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)(n_store * 4u) : 0, kBufferWord3);
+      float* srow = a.scores + ((int64_t)b * a.n_qb + (live ? r0 + qi : r0)) * a.n_cap;
+      rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)((uint32_t)a.n_cap * 4u) : 0, kBufferWord3);
     }
-    const uint32_t off_c = (uint32_t)col * 64u + (uint32_t)g * 16u;
-    // Scales and scores move four tiles (64 keys) at a time, as one 256-byte
-    // access per wave: lane l loads the scale word of key 64 i + l, and the
-    // lane holding key (16 j + col) of tile j of the group is lane 16 j + col;
-    // lane (g, col) keeps the score of tile g of the group for the store.
-    const uint32_t off_s = (uint32_t)lane * 4u;
-    const uint32_t off_o = (uint32_t)lane * 4u;
-    // ring of kRing tiles in flight: 16 B of codes per lane and tile, plus a
-    // scale word per lane for every group of four; tile t + kRing is
-    // requested as soon as tile t is scored, and the scales of a group with
-    // its last tile, once every tile of the slot's previous group has used
-    // them (tiles past the wave's keys read as zeros without touching memory)
+    const uint32_t gs_c = (uint32_t)NW * 4096u, gs_s = (uint32_t)NW * 256u;   // group strides: codes, words
+    const uint32_t off_c = (uint32_t)W * 4096u + (uint32_t)col * 64u + (uint32_t)g * 16u;
+    // Every lane loads the scale word of its key (16 t + col) with the codes
+    // (the byte of its k-group g is the operand's block scale).  Scores move
+    // four tiles (64 keys) at a time, as one 256-byte store per wave: lane
+    // (g, col) keeps the score of tile g of the group.
+    const uint32_t off_s = (uint32_t)W * 256u + (uint32_t)col * 4u;
+    const uint32_t off_o = (uint32_t)W * 256u + (uint32_t)lane * 4u;
+    // ring of kRing tiles in flight (16 B of codes and a scale word per lane
+    // and tile); tile t + kRing is requested as soon as tile t is scored
+    // (tiles past the wave's keys read as zeros without touching memory)
     static_assert(kRing % 4 == 0, "tiles move in groups of four");
     i32x4 kbuf[kRing];
-    uint32_t kscw[kRing / 4];
+    uint32_t kscw[kRing];
+    // tile t of the wave: tile t % 4 of its group t / 4
     auto fetch = [&](int t, int u) {
+      const uint32_t j = (uint32_t)t >> 2, q = (uint32_t)t & 3u;
       kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rc, off_c + (uint32_t)t * 1024u, 0, 0));
-      if (u % 4 == 3)
-        kscw[u / 4] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)(t - 3) * 64u, 0, 0);
+                                              rc, off_c + j * gs_c + q * 1024u, 0, 0));
+      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + j * gs_s + q * 64u, 0, 0);
     };
     // issue the first round in ring order (the loop consumes it in that order)
 #pragma unroll
@@ -228,57 +232,70 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
       fetch(u, u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int xor16 = (lane ^ 16) << 2, xor32 = (lane ^ 32) << 2;  // ds_bpermute byte addresses
-    const int n_rounds = (int)((n_load + 16 * kRing - 1) / (16 * kRing));
+    // rounds over the wave's groups that hold a visible key
+    int vgroups = (ngv - W + NW - 1) / NW;
+    vgroups = vgroups < kGroups ? vgroups : kGroups;
+    const int n_rounds = (vgroups * 4 + kRing - 1) / kRing;
     for (int t0 = 0; t0 < n_rounds * kRing; t0 += kRing) {
       float keep[QT];
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;
         const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
-        // this tile's scale word for key col sits in lane 16 (u % 4) + col
-        const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * (u % 4) + col) << 2, (int)kscw[u / 4]);
-        const int ksc = (int)((sw >> (8 * g)) & 0xffu);
+        const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
-          float part = 0.f;
+          // per head group: w . ReLU over the lane's 4 heads (short chains),
+          // then the groups in a fixed tree
+          float hpart[4];
 #pragma unroll
           for (int hg = 0; hg < nhg; ++hg) {
             i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0,
                                                                    qs[qi][hg], 0, ksc);
+            float hp = wv[qi][hg][0] * relu(acc[0]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part = fmaf(wv[qi][hg][i], relu(acc[i]), part);
+            for (int i = 1; i < 4; ++i) hp = fmaf(wv[qi][hg][i], relu(acc[i]), hp);
+            hpart[hg] = hp;
           }
-          part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(part)));
-          part += __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(part)));
+          float part = nhg == 1 ? hpart[0]
+                     : nhg == 2 ? hpart[0] + hpart[1]
+                     : nhg == 3 ? (hpart[0] + hpart[1]) + hpart[2]
+                                : (hpart[0] + hpart[1]) + (hpart[2] + hpart[3]);
+          // sum over the four row groups (lanes 16 apart, then 32 apart)
+          const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+          part = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+          const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+          part = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
           // every row group now holds the head sum; group g keeps tile g of the four
           keep[qi] = (u % 4 == g) ? part : keep[qi];
           if (u % 4 == 3) {
-            const int tg = t - 3;                         // first tile of the group
-            const uint32_t kl = (uint32_t)(tg * 16) + (uint32_t)lane;   // key - key_base
-            const bool vis = (int64_t)kl < (int64_t)nvis[qi] - key_base;
+            const uint32_t j = (uint32_t)t >> 2;          // the group
+            const int key = (W + (int)j * NW) * 64 + lane;
+            const bool vis = key < nvis[qi];
             const float sc = vis ? keep[qi] : -INFINITY;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + (uint32_t)tg * 64u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + j * gs_s, 0, 0);
             if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
           }
         }
         fetch(t + kRing, u);
       }
     }
-    // keys of this wave that the rounds did not reach get -inf
+    // groups of this wave that the rounds did not reach get -inf
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi)
-      for (uint32_t k = (uint32_t)(n_rounds * kRing * 16) + lane; k < n_store; k += 64)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], k * 4u, 0, 0);
+      for (uint32_t j = (uint32_t)(n_rounds * kRing / 4); j < (uint32_t)kGroups; ++j)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], off_o + j * gs_s, 0, 0);
   } else {
     // no query sees any key of this wave
     for (int qi = 0; qi < QT; ++qi) {
       if (r0 + qi >= a.n_qb) break;
       float* row = a.scores + ((int64_t)b * a.n_qb + r0 + qi) * a.n_cap;
-      const int64_t wave_end = key_base + kWaveKeys;
-      for (int64_t k = key_base + lane; k < wave_end && k < a.n_cap; k += 64) row[k] = -INFINITY;
+      for (int j = 0; j < kGroups; ++j) {
+        const int64_t k = (int64_t)(W + j * NW) * 64 + lane;
+        if (k < a.n_cap) row[k] = -INFINITY;
+      }
     }
   }
   __syncthreads();
