@@ -99,38 +99,39 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units a running max may lag the true max
 
-// Workgroup of 4 wavefronts, one per SIMD, each with the full register file.
-// Wave w owns a quarter of the 512 dims: FP8 dims 128 w .. +127 for w < 3,
-// and FP8 dims 384 .. 447 plus the 64 BF16 RoPE dims for w = 3.  Per
+// Workgroup of 8 wavefronts, two per SIMD.  Wave w = q + 4 h owns dim
+// quarter q of the 512 dims (FP8 dims 128 q .. +127 for q < 3; FP8 dims
+// 384 .. 447 plus the 64 BF16 RoPE dims for q = 3) and head half h (heads
+// 32 h .. +31); the two waves of a quarter load the same row pieces.  Per
 // 32-entry tile:
 //  * scores: every lane loads 16-byte pieces of one entry row straight from
-//    HBM into registers (three tiles ahead); they are widened FP8 -> BF16 in
+//    HBM into registers (two tiles ahead); they are widened FP8 -> BF16 in
 //    registers and used as the A operand of
-//      S^T[32 entries x 64 heads] (partial over the wave's dims) = K Q^T
-//    (V_MFMA_F32_32X32X16_BF16, 16 per tile) with the normalised, rotated,
-//    pre-scaled query as the B operand; the same raw bytes go to the wave's
-//    own slice of an LDS tile, where the output product reads them back
-//    transposed;
-//  * softmax: the four partial score blocks meet in LDS; wave w runs the
-//    online softmax (log2 domain, lazy rescale) of heads 16 w .. +15, four
-//    lanes per head, and leaves P (BF16) and the rescale factors in LDS;
-//  * output: O^T[wave's 128 dims x 64 heads] += V^T P^T (16 MFMAs per tile),
-//    V^T read from the wave's slice by ds_read_b64_tr_b8 (FP8, widened in
+//      S^T[32 entries x 32 heads] (partial over the quarter's dims) = K Q^T
+//    (V_MFMA_F32_32X32X16_BF16, 8 per tile) with the normalised, rotated,
+//    pre-scaled query as the B operand; the same raw bytes go to the
+//    quarter's slice of an LDS tile, where the output product reads them
+//    back transposed;
+//  * softmax: the four partial score blocks of a head half meet in LDS; wave
+//    w runs the online softmax (log2 domain, lazy rescale) of heads 8 w ..
+//    +7, eight lanes per head, and leaves P (BF16) and the rescale factors in
+//    LDS;
+//  * output: O^T[quarter's 128 dims x 32 heads] += V^T P^T (8 MFMAs per
+//    tile), V^T read from the slice by ds_read_b64_tr_b8 (FP8, widened in
 //    registers) or ds_read_b64_tr_b16 (RoPE dims).
-// The score product of tile t runs before the first barrier of a step and
-// the output product of tile t-1 after it, beside the softmax of tile t, so
-// both phases have matrix work.
-constexpr int kWaves = 4;
+// Two waves per SIMD let one wave's vector work run while the other waits
+// on its matrix instructions or memory.
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kVRow = 208;                      // bytes per entry in a wave's slice (192 used)
-constexpr int kVWave = kTile * kVRow;           // one wave's slice of a tile
-constexpr int kVBuf = kWaves * kVWave;          // one tile
+constexpr int kVRow = 208;                      // bytes per entry in a quarter's slice (192 used)
+constexpr int kVQuarter = kTile * kVRow;        // one quarter's slice of a tile
+constexpr int kVBuf = 4 * kVQuarter;            // one tile
 constexpr int kXsRow = 144;                     // one head's 32 partial scores (fp32) + pad
-constexpr int kXsWave = 64 * kXsRow;            // a wave's partial scores
+constexpr int kXsWave = 32 * kXsRow;            // a wave's partial scores (32 heads)
 constexpr int kPRow = 80;                       // bytes per head in P: 32 BF16 + pad
 constexpr int kPBytes = 64 * kPRow;
 constexpr int kStageRow = kD * 2 + 16;          // output staging: one head's row
-constexpr int kStages = 3;                      // tiles in flight in registers
+constexpr int kStages = 2;                      // tiles in flight in registers
 constexpr int kXsBuf = kWaves * kXsWave;        // one tile's partial scores
 constexpr int kOffXs = 2 * kVBuf;               // slices, partial scores and P are double-buffered
 constexpr int kOffP = kOffXs + 2 * kXsBuf;
@@ -163,11 +164,11 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 struct AttendShared {
-  uint8_t* sm;       // [2 tiles][4 waves][32 entries][kVRow] | xs[2] | P[2]
+  uint8_t* sm;       // [2 tiles][4 quarters][32 entries][kVRow] | xs[2] | P[2]
   float* alpha;      // [2][64] rescale factors per head
   float* ml;         // [64][2] final (max, sum)
   float* rope;       // cos, sin at the query position
-  float* ssx;        // [4 waves][64 heads] query sums of squares
+  float* ssx;        // [4 quarters][64 heads] query sums of squares
   int* lidx;         // staged selected indices (CSA)
 };
 
@@ -205,7 +206,7 @@ __device__ __forceinline__ RowPtrs row_ptrs(const RowSource rs, int p, int sel) 
 }
 
 // Chunk c of a lane's row pieces: FP8 bytes wdim + 32 c + 16 g (the RoPE
-// wave: chunks 0, 1 at 384 + ..., chunks 2..5 the RoPE bytes 32 (c - 2) + 16 g).
+// quarter: chunks 0, 1 at 384 + ..., chunks 2..5 the RoPE bytes 32 (c - 2) + 16 g).
 template <bool kRope>
 __device__ __forceinline__ i32x4 load_chunk(int c, const RowPtrs rp, int wdim, int g) {
   if (kRope && c >= 2) return *(gbl_i32x4*)(rp.pr + 32 * (c - 2) + 16 * g);
@@ -220,11 +221,13 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 5, r32 = lane & 31;
+  const int dq = wave & 3, hh = wave >> 2;  // dim quarter, head half
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
   const int p0 = split * a.split_len;
-  const int wdim = 128 * wave;              // first output dim of the wave (wave 3: 384)
+  const int wdim = 128 * dq;                // first dim of the quarter (quarter 3: 384)
+  const int hq = 32 * hh + r32;             // this lane's head (within the group) in the products
 
   // The 8 dims of k-step s held by lane half g (A and B operands alike).
   auto kdim = [&](int s) {
@@ -232,20 +235,17 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   };
 
   // Prologue.  Loads that do not depend on the list layout go first, so
-  // their latencies overlap: the query, the sink logits and (CSA) the first
+  // their latencies overlap: the query, the sink logit and (CSA) the first
   // tiles' selected indices; then the layout (query position, visible
   // entries, window start) and the first tiles' row loads.
-  i32x4 qraw[2][8];
-  bool q_ok[2];
-  float sink_raw[2];                         // the heads' sink logits, used by the epilogue
+  const int head_q = hg * 64 + hq;
+  const bool q_ok = head_q < a.H;
+  const float sink_raw = a.sink[q_ok ? head_q : 0];   // used by the epilogue
+  i32x4 qraw[8];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok ? head_q : 0)) * kD;
 #pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int head_q = hg * 64 + 32 * ht + r32;
-    q_ok[ht] = head_q < a.H;
-    sink_raw[ht] = a.sink[q_ok[ht] ? head_q : 0];
-    const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + (q_ok[ht] ? head_q : 0)) * kD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qraw[ht][s] = *(gbl_i32x4*)(qrow + kdim(s));
+    for (int s = 0; s < 8; ++s) qraw[s] = *(gbl_i32x4*)(qrow + kdim(s));
   }
   const int* const idx_row = a.idx ? a.idx + ((int64_t)b * a.n_q + r) * a.top_k : nullptr;
   int sel0[kStages];                         // first tiles' selected indices (a harmless read for HCA)
@@ -304,70 +304,58 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   if (tid < 64) S.alpha[tid] = 1.0f;
   ATTEND_BARRIER(kWaitLgkm0);
 
-  // The query operand: head 32 ht + lane % 32, dims kdim(s) .. +7; RMSNorm
-  // over all 512 dims (the four waves add their sums of squares through
-  // LDS), the softmax scale (log2 units), RoPE at the query position, BF16.
-  bf16x8 qv[2][8];
+  // The query operand: head hq, dims kdim(s) .. +7; RMSNorm over all 512
+  // dims (the four quarters add their sums of squares through LDS), the
+  // softmax scale (log2 units), RoPE at the query position, BF16.
+  bf16x8 qv[8];
   {
-    float ss[2];
+    float ss = 0.f;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      ss[ht] = 0.f;
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = q_ok[ht] ? (uint32_t)qraw[ht][s][j] : 0u;
-          const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
-          ss[ht] += lo * lo + hi * hi;
-        }
-      ss[ht] += __shfl_xor(ss[ht], 32, 64);
-    }
-    if (g == 0) {
-      S.ssx[wave * 64 + r32] = ss[0];
-      S.ssx[wave * 64 + 32 + r32] = ss[1];
-    }
-    ATTEND_BARRIER(kWaitLgkm0);
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int h = 32 * ht + r32;
-      const float tot = ((S.ssx[h] + S.ssx[64 + h]) + S.ssx[128 + h]) + S.ssx[192 + h];
-      // RMSNorm and the softmax scale (log2 units) in one factor; RoPE is linear
-      const float rs = ((a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(tot / (float)kD + 1e-6f) : 1.0f) * a.scale_log2;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = q_ok[ht] ? (uint32_t)qraw[ht][s][j] : 0u;
-          x[2 * j] = __uint_as_float(w << 16) * rs;
-          x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
-        }
-        if (kRopeWave && s >= 4) {              // dims 448 .. 511 carry RoPE
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const int u = (16 * (s - 4) + 8 * g + j) >> 1;
-            const float cs = S.rope[u], sn = S.rope[32 + u];
-            const float xe = x[j], xo = x[j + 1];
-            x[j] = xe * cs - xo * sn;
-            x[j + 1] = xe * sn + xo * cs;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qv[ht][s][j] = (__bf16)x[j];   // nearest even
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = q_ok ? (uint32_t)qraw[s][j] : 0u;
+        const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+        ss += lo * lo + hi * hi;
       }
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0) S.ssx[dq * 64 + hq] = ss;
+    ATTEND_BARRIER(kWaitLgkm0);
+    const float tot = ((S.ssx[hq] + S.ssx[64 + hq]) + S.ssx[128 + hq]) + S.ssx[192 + hq];
+    // RMSNorm and the softmax scale (log2 units) in one factor; RoPE is linear
+    const float rs = ((a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(tot / (float)kD + 1e-6f) : 1.0f) * a.scale_log2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = q_ok ? (uint32_t)qraw[s][j] : 0u;
+        x[2 * j] = __uint_as_float(w << 16) * rs;
+        x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
+      }
+      if (kRopeWave && s >= 4) {              // dims 448 .. 511 carry RoPE
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const int u = (16 * (s - 4) + 8 * g + j) >> 1;
+          const float cs = S.rope[u], sn = S.rope[32 + u];
+          const float xe = x[j], xo = x[j + 1];
+          x[j] = xe * cs - xo * sn;
+          x[j + 1] = xe * sn + xo * cs;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[s][j] = (__bf16)x[j];   // nearest even
     }
   }
 
-  f32x16 acc_o[4][2];
+  f32x16 acc_o[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) acc_o[dt][ht] = (f32x16){};
-  // softmax head of the lane (a quad per head; the four heads of a 16-lane
-  // row are 0, 1, 8, 9 apart so their score rows fall on distinct banks)
-  const int hs = 16 * wave + 2 * (lane >> 4) + ((lane >> 2) & 1) + 8 * ((lane >> 3) & 1);
-  const int qq = lane & 3;                  // its entries 8 qq .. +7
+  for (int dt = 0; dt < 4; ++dt) acc_o[dt] = (f32x16){};
+  // softmax heads of the wave: 8 wave .. +7, eight lanes per head, four
+  // entries per lane
+  const int hsl = 8 * dq + (lane >> 3);     // head within the half
+  const int hs = 32 * hh + hsl;             // head within the group
+  const int q8 = lane & 7;                  // its entries 4 q8 .. +3
   float m_run = -INFINITY;   // log2-domain reference max (lags the true max by < the slack)
   float l_part = 0.f;        // this lane's share of the running denominator
   const int G = lane >> 4, j16 = lane & 15;
@@ -388,17 +376,16 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
 
   // Software pipeline, one barrier per step: step t forms the scores of
   // tile t, the online softmax of tile t-1 and the output product of tile
-  // t-2, so the matrix cores have work on both sides of the softmax.  Slices,
-  // partial scores, P and the rescale factors are double-buffered (tile t in
-  // buffer t % 2); row pieces sit in register stage t % 3.  Tiles -2 and -1
-  // are empty (zero V, P = 0, factors 1); tiles past the list are masked
-  // (scores -inf: P = 0, the running max and sum unchanged).  n_tiles + 2
-  // steps, in rounds of three.
+  // t-2, so the matrix cores have work on both sides of the softmax.
+  // Slices, partial scores, P and the rescale factors are double-buffered
+  // and row pieces sit in two register stages: tile t uses buffer and stage
+  // t % 2.  Tiles -2 and -1 are empty (zero V, P = 0, factors 1); tiles past
+  // the list are masked (scores -inf: P = 0, the running max and sum
+  // unchanged).  n_tiles + 2 steps, in rounds of two.
   for (int t0 = 0; t0 <= n_tiles + 1; t0 += kStages) {
 #pragma unroll
     for (int buf = 0; buf < kStages; ++buf) {
       const int t = t0 + buf;
-      const int par = t & 1;
       i32x4 (&kr)[NL] = kst[buf];
       uint32_t& km = kmask[buf];
       // masked entries of tile t read zeros (rare: a list's last tile, unused selections)
@@ -409,26 +396,22 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
         for (int c = 0; c < NL; ++c) kr[c] = mine ? kr[c] : (i32x4){0, 0, 0, 0};
       }
       // LDS reads of the step: P^T and the rescale factors of tile t-2, the
-      // partial scores of tile t-1 (head hs, entries 8 qq .. +7), the staged
-      // index of tile t+3's entry
-      const uint8_t* pb = sm + kOffP + par * kPBytes;
-      bf16x8 pf[2][2];
+      // partial scores of tile t-1 (head hs, entries 4 q8 .. +3), the staged
+      // index of tile t+2's entry
+      const uint8_t* pb = sm + kOffP + buf * kPBytes;
+      bf16x8 pf[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) pf[ks] = *(const bf16x8*)(pb + hq * kPRow + 16 * (2 * ks + g));
+      const float al = S.alpha[buf * 64 + hq];
+      const uint8_t* xr = sm + kOffXs + (buf ^ 1) * kXsBuf + (4 * hh) * kXsWave + hsl * kXsRow + 16 * q8;
+      f32x4 x[4];
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
-          pf[ks][ht] = *(const bf16x8*)(pb + (32 * ht + r32) * kPRow + 16 * (2 * ks + g));
-      const float al0 = S.alpha[par * 64 + r32], al1 = S.alpha[par * 64 + 32 + r32];
-      const uint8_t* xr = sm + kOffXs + (par ^ 1) * kXsBuf + hs * kXsRow + 32 * qq;
-      f32x4 x[4][2];
-#pragma unroll
-      for (int src = 0; src < 4; ++src)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) x[src][u] = *(const f32x4*)(xr + src * kXsWave + 16 * u);
+      for (int src = 0; src < 4; ++src) x[src] = *(const f32x4*)(xr + src * kXsWave);
       const int sel = ATTEND_SEL(t + kStages);
 
-      // tile t's raw bytes into the wave's slice
-      uint8_t* vs = sm + par * kVBuf + wave * kVWave + r32 * kVRow;
+      // tile t's raw bytes into the quarter's slice (both waves of the
+      // quarter write the same bytes)
+      uint8_t* vs = sm + buf * kVBuf + dq * kVQuarter + r32 * kVRow;
       if constexpr (!kRopeWave) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) *(i32x4*)(vs + 32 * c + 16 * g) = kr[c];
@@ -438,67 +421,48 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
 #pragma unroll
         for (int c = 0; c < 4; ++c) *(i32x4*)(vs + 64 + 32 * c + 16 * g) = kr[2 + c];
       }
-      // partial scores of tile t; each chunk's registers take tile t+3's chunk
+      // partial scores of tile t; each chunk's registers take tile t+2's chunk
       // once its k-steps are issued
       const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + (t + kStages) * kTile + r32, sel);
       km = rp.live;
-      f32x16 sc0 = {}, sc1 = {};
+      f32x16 sc = {};
 #pragma unroll
       for (int c = 0; c < NL; ++c) {
         if (kRopeWave && c >= 2) {
-          const bf16x8 kop = __builtin_bit_cast(bf16x8, kr[c]);
-          sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[0][c + 2], sc0, 0, 0, 0);
-          sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[1][c + 2], sc1, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[c]), qv[c + 2], sc, 0, 0, 0);
         } else {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const bf16x8 kop = fp8x8_to_bf16((uint32_t)kr[c][2 * h], (uint32_t)kr[c][2 * h + 1]);
-            sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[0][2 * c + h], sc0, 0, 0, 0);
-            sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[1][2 * c + h], sc1, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[2 * c + h], sc, 0, 0, 0);
           }
         }
         kr[c] = load_chunk<kRopeWave>(c, rp, wdim, g);
       }
-      // issue order: every score MFMA followed by one LDS access and a few
-      // vector ops, so the LDS traffic spreads under the matrix work
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);   // LDS
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
-      }
 
       // O rescaled before tile t-2 joins it, when a running max moved (in
       // place in the accumulation registers)
-      if (__any(al0 != 1.0f || al1 != 1.0f)) {
+      if (__any(al != 1.0f)) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              float e = acc_o[dt][ht][i], tmp;
-              __asm__ __volatile__(
-                  "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                  : "+a"(e), "=&v"(tmp)
-                  : "v"(ht ? al1 : al0));
-              acc_o[dt][ht][i] = e;
-            }
+          for (int i = 0; i < 16; ++i) {
+            float e = acc_o[dt][i], tmp;
+            __asm__ __volatile__(
+                "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                : "+a"(e), "=&v"(tmp)
+                : "v"(al));
+            acc_o[dt][i] = e;
+          }
         __asm__ __volatile__("s_nop 4");      // vector writes before the next matrix read
       }
 
-      // tile t's partial scores: lane holds head 32 ht + lane % 32, entries
+      // tile t's partial scores: lane holds head 32 hh + lane % 32, entries
       // 8 jb + 4 (lane / 32) + i, i.e. the 16-byte group 2 jb + lane / 32
-      uint8_t* xw = sm + kOffXs + par * kXsBuf + wave * kXsWave;
+      uint8_t* xw = sm + kOffXs + buf * kXsBuf + wave * kXsWave + r32 * kXsRow;
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht) {
-        const int head = 32 * ht + r32;
-        const f32x16& sc = ht ? sc1 : sc0;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-          *(f32x4*)(xw + head * kXsRow + 16 * (2 * jb + g)) =
-              (f32x4){sc[4 * jb], sc[4 * jb + 1], sc[4 * jb + 2], sc[4 * jb + 3]};
-      }
+      for (int jb = 0; jb < 4; ++jb)
+        *(f32x4*)(xw + 16 * (2 * jb + g)) = (f32x4){sc[4 * jb], sc[4 * jb + 1], sc[4 * jb + 2], sc[4 * jb + 3]};
 
       // O^T += V^T P^T for tile t-2
 #pragma unroll
@@ -517,51 +481,43 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
               vop[4 + i] = u16_as_bf16((uint16_t)vt16[d2][ks][1][i]);
             }
           }
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-            acc_o[dt][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[ks][ht], acc_o[dt][ht], 0, 0, 0);
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[ks], acc_o[dt], 0, 0, 0);
         }
 
       // online softmax of tile t-1 for head hs
       {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f32x4 s4 = ((x[0][u] + x[1][u]) + x[2][u]) + x[3][u];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * u + i] = s4[i];
-        }
+        const f32x4 s4 = ((x[0] + x[1]) + x[2]) + x[3];
+        float v[4] = {s4[0], s4[1], s4[2], s4[3]};
         if (__builtin_expect(live_prev != 0xffffffffu, 0)) {   // masked entries: -inf
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = (live_prev >> (8 * qq + i)) & 1 ? v[i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) v[i] = (live_prev >> (4 * q8 + i)) & 1 ? v[i] : -INFINITY;
         }
-        float mx = v[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, v[i]);
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         mx = fmaxf(mx, dpp_f32<0xB1>(mx));     // lane ^ 1
         mx = fmaxf(mx, dpp_f32<0x4E>(mx));     // lane ^ 2
+        mx = fmaxf(mx, dpp_f32<0x141>(mx));    // lane 7 - i of each 8: the other quad
         // the reference max moves only when the tile max overtakes it by the
         // slack, so O rescales are rare; probabilities stay below 2^slack
         const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);   // argument <= 0, or -inf
         float psum = 0.f;
-        bf16x8 pk;
+        bf16x4 pk;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(v[i] - m_use);
           psum += p;
           pk[i] = (__bf16)p;                   // nearest even
         }
         l_part = l_part * alpha + psum;
         m_run = m_new;
-        *(bf16x8*)(sm + kOffP + (par ^ 1) * kPBytes + hs * kPRow + 16 * qq) = pk;
-        if (qq == 0) S.alpha[(par ^ 1) * 64 + hs] = alpha;
+        *(bf16x4*)(sm + kOffP + (buf ^ 1) * kPBytes + hs * kPRow + 8 * q8) = pk;
+        if (q8 == 0) S.alpha[(buf ^ 1) * 64 + hs] = alpha;
       }
       live_prev = live_t;
 
-      // V^T of tile t-1 from the wave's slice, for the next step's output product
-      const uint8_t* vw = sm + (par ^ 1) * kVBuf + wave * kVWave;
+      // V^T of tile t-1 from the quarter's slice, for the next step's output product
+      const uint8_t* vw = sm + (buf ^ 1) * kVBuf + dq * kVQuarter;
 #pragma unroll
       for (int dt = 0; dt < NDT8; ++dt)
 #pragma unroll
@@ -586,14 +542,6 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
                   (lds_i16x4*)(vw + row * kVRow + 64 + 2 * (32 * dt + 16 * (G & 1) + 4 * (j16 & 3))));
             }
       }
-      // issue order: every output MFMA followed by one LDS access and the
-      // softmax's vector work
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x080, 1, 1);   // LDS
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 1);   // VALU
-      }
       ATTEND_BARRIER(kWaitLgkm0);
     }
   }
@@ -605,7 +553,8 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
     float l_run = l_part;
     l_run += dpp_f32<0xB1>(l_run);
     l_run += dpp_f32<0x4E>(l_run);
-    if (qq == 0) {
+    l_run += dpp_f32<0x141>(l_run);
+    if (q8 == 0) {
       S.ml[2 * hs] = m_run;
       S.ml[2 * hs + 1] = l_run;
     }
@@ -618,86 +567,71 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   // covers the whole list, else the fp16 partial) is staged in LDS as
   // [64 heads][512 dims] rows, so the global stores are contiguous 16-byte chunks.
   uint8_t* stage = sm;
-  float scale[2], m_h[2], l_h[2];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int hl = 32 * ht + r32;
-    m_h[ht] = S.ml[2 * hl];
-    l_h[ht] = S.ml[2 * hl + 1];
-    if (single) {
-      const float z2 = q_ok[ht] ? sink_raw[ht] * kLog2e : 0.f;
-      const float top = fmaxf(m_h[ht], z2);
-      const float e_m = exp2f(m_h[ht] - top);
-      scale[ht] = e_m / (l_h[ht] * e_m + exp2f(z2 - top));   // 0 when no row was seen
-    } else {
-      scale[ht] = l_h[ht] > 0.f ? 1.0f / l_h[ht] : 0.f;
-    }
+  const float m_h = S.ml[2 * hq], l_h = S.ml[2 * hq + 1];
+  float scale;
+  if (single) {
+    const float z2 = q_ok ? sink_raw * kLog2e : 0.f;
+    const float top = fmaxf(m_h, z2);
+    const float e_m = exp2f(m_h - top);
+    scale = e_m / (l_h * e_m + exp2f(z2 - top));   // 0 when no row was seen
+  } else {
+    scale = l_h > 0.f ? 1.0f / l_h : 0.f;
   }
-  // lane holds dims wdim + 32 dt + 8 jb + 4 (lane / 32) + i of head 32 ht + lane % 32
+  // lane holds dims wdim + 32 dt + 8 jb + 4 (lane / 32) + i of head hq
+  uint8_t* const srow = stage + hq * kStageRow;
   if (single) {
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int jb = 0; jb < 4; ++jb) {
+        const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
+        float o[4];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
-          float o[4];
+        for (int i = 0; i < 4; ++i) o[i] = acc_o[dt][4 * jb + i] * scale;
+        if (kRopeWave && dt >= NDT8 && inv_rope) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = acc_o[dt][ht][4 * jb + i] * scale[ht];
-          if (kRopeWave && dt >= NDT8 && inv_rope) {
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-              const int u = (d0 + i - kDN) >> 1;
-              const float cs = S.rope[u], sn = -S.rope[32 + u];   // rotation by -t
-              const float xe = o[i], xo = o[i + 1];
-              o[i] = xe * cs - xo * sn;
-              o[i + 1] = xe * sn + xo * cs;
-            }
+          for (int i = 0; i < 4; i += 2) {
+            const int u = (d0 + i - kDN) >> 1;
+            const float cs = S.rope[u], sn = -S.rope[32 + u];   // rotation by -t
+            const float xe = o[i], xo = o[i + 1];
+            o[i] = xe * cs - xo * sn;
+            o[i + 1] = xe * sn + xo * cs;
           }
-          const bf16x4 w = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};   // nearest even
-          *(bf16x4*)(stage + (32 * ht + r32) * kStageRow + 2 * d0) = w;
         }
+        const bf16x4 w = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};   // nearest even
+        *(bf16x4*)(srow + 2 * d0) = w;
+      }
   } else {
     typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int jb = 0; jb < 4; ++jb) {
+        const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
+        f16x4 w;
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          const int d0 = wdim + 32 * dt + 8 * jb + 4 * g;
-          f16x4 w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (_Float16)(acc_o[dt][ht][4 * jb + i] * scale[ht]);
-          *(f16x4*)(stage + (32 * ht + r32) * kStageRow + 2 * d0) = w;
-        }
-  }
-  if (wave == 0 && g == 0) {                 // one lane per head
-#pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int hl = 32 * ht + r32;
-      const int head = hg * 64 + hl;
-      if (head >= a.H) continue;
-      if (single) {
-        if (a.out_lse)
-          a.out_lse[((int64_t)b * a.n_q + r) * a.H + head] =
-              l_h[ht] > 0.f ? (m_h[ht] + log2f(l_h[ht])) * 0.6931471805599453f : -INFINITY;
-      } else {
-        const int64_t ps = (unit * a.n_splits + split) * 64 + hl;
-        a.part_ml[ps * 2] = m_h[ht];
-        a.part_ml[ps * 2 + 1] = l_h[ht];
+        for (int i = 0; i < 4; ++i) w[i] = (_Float16)(acc_o[dt][4 * jb + i] * scale);
+        *(f16x4*)(srow + 2 * d0) = w;
       }
+  }
+  if (dq == 0 && g == 0 && q_ok) {           // one lane per head
+    if (single) {
+      if (a.out_lse)
+        a.out_lse[((int64_t)b * a.n_q + r) * a.H + head_q] =
+            l_h > 0.f ? (m_h + log2f(l_h)) * 0.6931471805599453f : -INFINITY;
+    } else {
+      const int64_t ps = (unit * a.n_splits + split) * 64 + hq;
+      a.part_ml[ps * 2] = m_h;
+      a.part_ml[ps * 2 + 1] = l_h;
     }
   }
   ATTEND_BARRIER(kWaitLgkm0);
-  // 64 rows x 64 chunks of 16 bytes, 16 per thread, consecutive threads on
-  // consecutive chunks of a row (a row per wave and pass)
+  // 64 rows x 64 chunks of 16 bytes: a row per wave and pass
   uint8_t* const obase = single ? (uint8_t*)a.out + (((int64_t)b * a.n_q + r) * a.H + hg * 64) * (kD * 2)
                                 : (uint8_t*)(a.part_o + (unit * a.n_splits + split) * 64 * kD);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int hl = 4 * k + wave;
+  for (int k = 0; k < 8; ++k) {
+    const int hl = 8 * k + wave;
     if (hg * 64 + hl >= a.H) break;
     const i32x4 v = *(const i32x4*)(stage + hl * kStageRow + 16 * lane);
     *(i32x4*)(obase + (int64_t)hl * (kD * 2) + 16 * lane) = v;
@@ -709,13 +643,14 @@ __global__ void __launch_bounds__(kThreads, 1) attend_fp8_kernel(AttendLaunch a)
   __shared__ float alpha_s[2 * 64];
   __shared__ float ml_s[2 * 64];
   __shared__ float rope_cs[64];
-  __shared__ float ssx[kWaves * 64];
+  __shared__ float ssx[4 * 64];
   __shared__ int lidx[kIdxMax];
   const AttendShared S{sm, alpha_s, ml_s, rope_cs, ssx, lidx};
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wave == 3) attend_wave<true>(a, S, wave);
+  if ((wave & 3) == 3) attend_wave<true>(a, S, wave);
   else attend_wave<false>(a, S, wave);
 }
+
 // Merge the split partials: workgroup (unit, head quad), 64 threads per head,
 // 8 dims each.
 __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) {

@@ -191,11 +191,11 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   }
   if (s < 1) s = 1;
   int64_t len = (list + s - 1) / s;
-  // The kernel runs n_tiles + 2 pipeline steps in rounds of three: a split
-  // of n_tiles = 1 (mod 3) tiles wastes no step, so the split grows to the
-  // next such length (fewer splits for the combine, same kernel time).
+  // The kernel runs n_tiles + 2 pipeline steps in rounds of two: a split of
+  // an even number of tiles wastes no step, so an odd split grows by a tile
+  // (fewer splits for the combine, same kernel time).
   int64_t tiles = (len + 31) / 32;
-  tiles += (3 - (tiles + 2) % 3) % 3;
+  tiles += tiles & 1;
   len = tiles * 32;
   if (!dense && len > csa::kAttendIdxMax) len = csa::kAttendIdxMax;
   s = (list + len - 1) / len;
