@@ -671,11 +671,11 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
   __syncthreads();
   if (head >= a.H) return;
   const int64_t base = (int64_t)unit * a.n_splits * 64 + hl;
-  // Splits are merged eight at a time, every load of a group in flight
+  // Splits are merged sixteen at a time, every load of a group in flight
   // together, against a running maximum: M over the sink logit and the
   // splits' maxima (output and denominator), Mx over the splits only (LSE).
   typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-  constexpr int kGroup = 8;
+  constexpr int kGroup = 16;
   const float z2 = a.sink[head] * kLog2e;
   float M = z2, den = 1.0f;                 // den = exp2(z2 - M) + sum l_s exp2(m_s - M)
   float Mx = -INFINITY, lsum = 0.f;         // lsum = sum l_s exp2(m_s - Mx)
