@@ -225,7 +225,12 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
-  const int p0 = split * a.split_len;
+  const int n_sp = a.n_splits;
+  // Splits take the list's 32-entry tiles round-robin: local tile t of this
+  // split is tile t n_sp + split of the list, so the workgroups of a query
+  // stream one contiguous front of the cache (HBM serves that faster than
+  // one private stream per workgroup).  List position of lane r32's entry:
+#define ATTEND_POS(t) (((t) * n_sp + split) * kTile + r32)
   const int wdim = 128 * dq;                // first dim of the quarter (quarter 3: 384)
   const int hq = 32 * hh + r32;             // this lane's head (within the group) in the products
 
@@ -251,17 +256,16 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   int sel0[kStages];                         // first tiles' selected indices (a harmless read for HCA)
 #pragma unroll
   for (int u = 0; u < kStages; ++u) {
-    const int pos = p0 + u * kTile + r32;
+    const int pos = ATTEND_POS(u);
     sel0[u] = a.idx ? idx_row[pos < a.top_k ? pos : 0] : ((const int*)a.q)[r32];
   }
   const ListInfo L = list_info(a, b, r);
   const int list_len = L.n_comp + L.n_w;
-  int p1 = p0 + a.split_len;
-  p1 = p1 < list_len ? p1 : list_len;
-  const int n_tiles = p1 > p0 ? (p1 - p0 + kTile - 1) / kTile : 0;
+  const int list_tiles = (list_len + kTile - 1) / kTile;
+  const int n_tiles = list_tiles > split ? (list_tiles - split + n_sp - 1) / n_sp : 0;
 
-  // Row pieces of tile t for this lane's entry (list position p0 + 32 t +
-  // lane % 32).  Every load is issued (a masked entry reads harmless bytes:
+  // Row pieces of local tile t for this lane's entry (list position
+  // ATTEND_POS(t)).  Every load is issued (a masked entry reads harmless bytes:
   // the query) so the count of loads in flight is the same on every path.
   RowSource rsrc;
   rsrc.dummy = (uint64_t)a.q;                // >= 1 KiB of readable bytes
@@ -271,7 +275,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   rsrc.wb1 = (uint64_t)a.win1 + (uint64_t)((int64_t)b * a.win_seq_stride + (int64_t)L.win_lo * a.win_stride);
   rsrc.kvs = (uint32_t)a.kv_stride;
   rsrc.wns = (uint32_t)a.win_stride;
-  rsrc.p1 = p1;
+  rsrc.p1 = list_len;
   rsrc.n_comp = L.n_comp;
   rsrc.n_vis = L.n_vis;
   rsrc.n_w = L.n_w;
@@ -282,7 +286,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   uint32_t kmask[kStages];
 #pragma unroll
   for (int u = 0; u < kStages; ++u) {
-    const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + u * kTile + r32, sel0[u]);
+    const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, ATTEND_POS(u), sel0[u]);
     kmask[u] = rp.live;
 #pragma unroll
     for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
@@ -295,8 +299,11 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   }
   if (a.idx) {
     const int* src = a.idx + ((int64_t)b * a.n_q + r) * a.top_k;
-    const int n_sel = (p1 < L.n_comp ? p1 : L.n_comp) - p0;
-    for (int i = tid; i < n_sel; i += kThreads) S.lidx[i] = src[p0 + i];
+    const int n_loc = n_tiles * kTile < kIdxMax ? n_tiles * kTile : kIdxMax;
+    for (int i = tid; i < n_loc; i += kThreads) {
+      const int pos = ((i / kTile) * n_sp + split) * kTile + (i % kTile);
+      if (pos < L.n_comp) S.lidx[i] = src[pos];
+    }
   }
   // tile -1's slices (buffer 1) and tile -2's P (buffer 0) are zero, its factors 1
   for (int i = tid; i < kVBuf / 16; i += kThreads) *(i32x4*)(sm + kVBuf + 16 * i) = (i32x4){0, 0, 0, 0};
@@ -423,7 +430,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
       }
       // partial scores of tile t; each chunk's registers take tile t+2's chunk
       // once its k-steps are issued
-      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, p0 + (t + kStages) * kTile + r32, sel);
+      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, ATTEND_POS(t + kStages), sel);
       km = rp.live;
       f32x16 sc = {};
 #pragma unroll

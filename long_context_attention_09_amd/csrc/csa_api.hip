@@ -182,23 +182,26 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
     return p;
   }
   const int64_t units = (int64_t)a->B * a->n_q * ((a->H + 63) / 64);
+  // Splits take the list's 32-entry tiles round-robin (split s: tiles s,
+  // s + n_splits, ...).
+  const int64_t tiles = (list + 31) / 32;
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
-  int64_t s_max = (list + 95) / 96;               // at least three 32-entry tiles per split
+  int64_t s_max = (tiles + 2) / 3;                // at least three tiles per split
   if (s > s_max) s = s_max;
-  if (!dense) {                                   // a CSA split's indices fit the kernel's stage
-    const int64_t s_min = (list + csa::kAttendIdxMax - 1) / csa::kAttendIdxMax;
+  const int64_t per_max = csa::kAttendIdxMax / 32;    // a CSA split's indices fit the kernel's stage
+  if (!dense) {
+    const int64_t s_min = (tiles + per_max - 1) / per_max;
     if (s < s_min) s = s_min;
   }
   if (s < 1) s = 1;
-  int64_t len = (list + s - 1) / s;
-  // The kernel runs n_tiles + 2 pipeline steps in rounds of two: a split of
-  // an even number of tiles wastes no step, so an odd split grows by a tile
+  int64_t per = (tiles + s - 1) / s;
+  // The kernel runs n_tiles + 2 pipeline steps in rounds of two: splits of
+  // an even number of tiles waste no step, so an odd count grows by one
   // (fewer splits for the combine, same kernel time).
-  int64_t tiles = (len + 31) / 32;
-  tiles += tiles & 1;
-  len = tiles * 32;
-  if (!dense && len > csa::kAttendIdxMax) len = csa::kAttendIdxMax;
-  s = (list + len - 1) / len;
+  per += per & 1;
+  if (!dense && per > per_max) per = per_max;
+  s = (tiles + per - 1) / per;
+  const int64_t len = per * 32;
   p.n_splits = (int)s;
   p.split_len = (int)len;
   if (s > 1) {
