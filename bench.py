@@ -47,12 +47,12 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "60a846a5d1fe570aebb119dbedc589db114945b7ddbcffb817deca186239b1b8",
-        "fetch_kib": 83314.9, "write_kib": 16512.0},
+        "sha256": "cb8dcc4f50a3f60620c8821f9799d365777e8127fffd38b48f6114930b5c21a9",
+        "fetch_kib": 83362.8, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "010199161a7230f613b006dfe8881458656fbf6ca628216eee265ac2cdc24b54",
-        "fetch_kib": 69825.3, "write_kib": 8276.2},
+        "sha256": "5d2c44ad12f6abfb4759b96586931e93c206c9ed12421e2abd30a771f996e0f8",
+        "fetch_kib": 69829.4, "write_kib": 8517.0},
 }
 
 
