@@ -15,6 +15,13 @@ Caches are kept in three copies that consecutive steps rotate through, so the
 256 MB Infinity Cache cannot serve a step from the previous step's reads (each
 layer of a real model has caches of its own).  All inputs are resident in HBM
 before the timed region.
+
+The same line also carries a prefill measurement (config.prefill): one
+Pro-shaped 8192-token chunk appended to 2^20 cached tokens, for a CSA and an
+HCA layer (compress of the chunk, window store, index + top-k for CSA,
+attention), as tokens/s and as the achieved fraction of the MFMA peaks
+(MXFP4 for the indexer's scoring, BF16 for the attention), next to the fp64
+oracle timed on sampled query rows.
 """
 from __future__ import annotations
 
@@ -31,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s per layer at 1M ctx (CSA+HCA) and % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MXFP4_PEAK_TFLOPS = 10100.0     # dense MFMA, published
+BF16_PEAK_TFLOPS = 2500.0       # dense MFMA, published
 COPIES = 3
 EVENT_DISABLE_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 CSRC = os.path.join(ROOT, "long_context_attention_09_amd", "csrc")
@@ -95,6 +104,29 @@ def algorithmic_bytes(shape, kind):
         return B * (n_vis * 68 + shape.H_I * 68 + shape.H_I * 4)
     rows = (shape.top_k if shape.csa else n_vis) + shape.n_win
     return B * (rows * 576 + 2 * shape.H * shape.d * 2)
+
+
+def prefill_flops(shape):
+    """Algorithmic flops of one prefill chunk (queries t = L .. L + n_q - 1).
+
+    index:  every visible key (t // m entries, capped by the entries that
+            exist) against every indexer head: H_I * d_I multiply-adds.
+    attend: every attended row (CSA: min(top_k, visible) selected entries;
+            HCA: every visible entry; both plus the n_win window rows) against
+            every head: d multiply-adds for the score and d for the output.
+    """
+    import numpy as np
+    t = shape.L + np.arange(shape.n_q, dtype=np.int64)
+    n_all = (shape.L + shape.n_q) // shape.m
+    n_vis = np.minimum(t // shape.m, n_all)
+    out = {}
+    if shape.csa:
+        out["index"] = float(n_vis.sum()) * shape.H_I * shape.d_I * 2
+        rows = np.minimum(n_vis, shape.top_k) + shape.n_win
+    else:
+        rows = n_vis + shape.n_win
+    out["attend"] = float(rows.sum()) * shape.H * shape.d * 4
+    return out
 
 
 def traffic_bytes(label):
@@ -173,6 +205,111 @@ def cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, budget_s=15.0):
                       f"oracle), {t_csa + t_hca:.1f} s; rate = 1 / (t_csa_seq + t_hca_seq)"}
 
 
+def prefill_oracle(shapes, inps, rows_per_layer):
+    """The fp64 oracle on a sample of each prefill chunk: the chunk's own
+    stores once, then rows_per_layer query rows (first, last and evenly
+    spaced between); the chunk time is extrapolated as
+    t_stores + n_q * t_row."""
+    from oracle import pipeline as P
+    per = {}
+    total = 0.0
+    for name, shape, inp in zip(("csa", "hca"), shapes, inps):
+        t0 = time.perf_counter()
+        prep = P.prefill_prepare(shape, inp, 0)
+        t_prep = time.perf_counter() - t0
+        rows = sorted(set(int(round(i * (shape.n_q - 1) / max(rows_per_layer - 1, 1)))
+                          for i in range(rows_per_layer)))
+        t0 = time.perf_counter()
+        for r in rows:
+            P.prefill_query(shape, inp, prep, 0, r)
+        t_row = (time.perf_counter() - t0) / len(rows)
+        t_chunk = t_prep + shape.n_q * t_row
+        total += t_chunk
+        per[name] = {"rows_timed": len(rows), "s_stores": round(t_prep, 3), "s_per_row": round(t_row, 4),
+                     "tokens_per_s": round(shape.n_q / t_chunk, 2)}
+    per["tokens_per_s"] = round(shapes[0].n_q / total, 2)
+    per["sample"] = (f"the chunk's stores plus {rows_per_layer} query rows per layer, fp64 NumPy oracle; "
+                     "chunk time extrapolated as t_stores + 8192 t_row; rate over the CSA+HCA pair")
+    return per
+
+
+def prefill_leg(ev, st, steps, warmup, oracle_rows):
+    """One 8192-token chunk after 2^20 cached tokens through a CSA and an HCA
+    layer, timed with HIP events per operation on the bench stream."""
+    import torch
+    import synth
+    from long_context_attention_09_amd.layer import LayerStep
+
+    csa_shape, hca_shape = synth.PRO_CSA_PREFILL, synth.PRO_HCA_PREFILL
+    print("[bench] prefill: generating inputs", file=sys.stderr, flush=True)
+    csa_inp = synth.quant_prefill_inputs(csa_shape, device="cuda")
+    hca_inp = synth.quant_prefill_inputs(hca_shape, device="cuda")
+    csa = LayerStep(csa_shape, csa_inp, prefill=True)
+    hca = LayerStep(hca_shape, hca_inp, prefill=True)
+    torch.cuda.synchronize()
+    record = ev.h.hipEventRecord
+    n = warmup + steps
+    marks = [[ev.create() for _ in range(7)] for _ in range(n)]
+
+    def step(m):
+        record(C.c_void_p(m[0]), st)
+        csa.compress_all(stream=st)
+        record(C.c_void_p(m[1]), st)
+        csa.index(stream=st)
+        record(C.c_void_p(m[2]), st)
+        csa.attend(stream=st)
+        record(C.c_void_p(m[3]), st)
+        hca.compress_all(stream=st)
+        record(C.c_void_p(m[4]), st)
+        hca.attend(stream=st)
+        record(C.c_void_p(m[5]), st)
+
+    print("[bench] prefill: warmup", file=sys.stderr, flush=True)
+    for k in range(warmup):
+        step(marks[k])
+    torch.cuda.synchronize()
+    print("[bench] prefill: timed", file=sys.stderr, flush=True)
+    for k in range(warmup, n):
+        step(marks[k])
+    torch.cuda.synchronize()
+    timed = marks[warmup:]
+
+    def avg(i, j):
+        return sum(ev.elapsed_ms(m[i], m[j]) for m in timed) / steps
+
+    t = {"csa_compress": avg(0, 1), "csa_index_topk": avg(1, 2), "csa_attend": avg(2, 3),
+         "hca_compress": avg(3, 4), "hca_attend": avg(4, 5)}
+    t_csa = avg(0, 3)
+    t_hca = avg(3, 5)
+    f_csa, f_hca = prefill_flops(csa_shape), prefill_flops(hca_shape)
+
+    def mfma(flops, ms, peak):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 3), "tflop": round(flops / 1e12, 3), "achieved_tflops": round(tf, 1),
+                "peak_tflops": peak, "frac": round(tf / peak, 4)}
+
+    out = {
+        "workload": "Pro-shaped prefill chunk: 8192 new tokens after 2^20 cached tokens, B=1, H=128, "
+                    "CSA (m=4 overlap, indexer 64x128 MXFP4, top-k 1024) and HCA (m=128), window 128, sink",
+        "steps": steps, "warmup": warmup,
+        "csa": {"ms_per_chunk": round(t_csa, 3), "tokens_per_s": round(csa_shape.n_q / (t_csa * 1e-3), 1)},
+        "hca": {"ms_per_chunk": round(t_hca, 3), "tokens_per_s": round(hca_shape.n_q / (t_hca * 1e-3), 1)},
+        "tokens_per_s": round(csa_shape.n_q / ((t_csa + t_hca) * 1e-3), 1),
+        "ops_ms": {k: round(v, 3) for k, v in t.items()},
+        # the index op is the scoring kernel plus the top-k passes of every
+        # query block; its fraction counts the scoring flops only
+        "mfma": {"csa_index_topk(mxfp4)": mfma(f_csa["index"], t["csa_index_topk"], MXFP4_PEAK_TFLOPS),
+                 "csa_attend(bf16)": mfma(f_csa["attend"], t["csa_attend"], BF16_PEAK_TFLOPS),
+                 "hca_attend(bf16)": mfma(f_hca["attend"], t["hca_attend"], BF16_PEAK_TFLOPS)},
+    }
+    if oracle_rows > 0:
+        print("[bench] prefill: oracle sample", file=sys.stderr, flush=True)
+        out["oracle"] = prefill_oracle((csa_shape, hca_shape), (csa_inp, hca_inp), oracle_rows)
+    del csa, hca, csa_inp, hca_inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +317,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--prefill-steps", type=int, default=3,
+                    help="timed prefill chunks (0: no prefill measurement)")
+    ap.add_argument("--prefill-oracle-rows", type=int, default=4,
+                    help="query rows per layer the oracle is timed on (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB elementwise copy used to scale HBM counters")
     args = ap.parse_args()
@@ -281,6 +422,11 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, args.cpu_budget)
+    if args.prefill_steps > 0:
+        del csa, hca, csa_inp, hca_inp
+        torch.cuda.empty_cache()
+        line["config"]["prefill"] = prefill_leg(ev, st, args.prefill_steps, 1,
+                                                0 if args.no_cpu_baseline else args.prefill_oracle_rows)
     print(json.dumps(line), flush=True)
 
 
