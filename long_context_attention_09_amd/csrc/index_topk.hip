@@ -154,6 +154,9 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     nvis[qi] = __builtin_amdgcn_readfirstlane((r0 + qi < a.n_qb) ? query_n_vis(a, b, r0 + qi) : 0);
     nvis_max = nvis[qi] > nvis_max ? nvis[qi] : nvis_max;
   }
+  // (the maximum may be formed with a vector instruction: make it a scalar
+  // again, or every buffer access below turns into a per-lane loop)
+  nvis_max = __builtin_amdgcn_readfirstlane(nvis_max);
   __syncthreads();
 
   // Key groups of 64 (four 16-key tiles) are dealt to the waves of the
@@ -237,7 +240,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     vgroups = vgroups < kGroups ? vgroups : kGroups;
     const int n_rounds = (vgroups * 4 + kRing - 1) / kRing;
     for (int t0 = 0; t0 < n_rounds * kRing; t0 += kRing) {
-      float keep[QT];
+      float part[QT][4];      // lane partials of the group's four tiles
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;
@@ -245,36 +248,39 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
-          // per head group: w . ReLU over the lane's 4 heads (short chains),
-          // then the groups in a fixed tree
-          float hpart[4];
+          // w . ReLU over the lane's 4 heads of every head group, in two
+          // chains (head groups 0-1 and 2-3)
+          float hpart[2] = {0.f, 0.f};
 #pragma unroll
           for (int hg = 0; hg < nhg; ++hg) {
             i32x8 qv = {qa[qi][hg][0], qa[qi][hg][1], qa[qi][hg][2], qa[qi][hg][3], 0, 0, 0, 0};
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv, kb, acc, 4, 4, 0,
                                                                    qs[qi][hg], 0, ksc);
-            float hp = wv[qi][hg][0] * relu(acc[0]);
+            float hp = (hg & 1) ? hpart[hg >> 1] : 0.f;
 #pragma unroll
-            for (int i = 1; i < 4; ++i) hp = fmaf(wv[qi][hg][i], relu(acc[i]), hp);
-            hpart[hg] = hp;
+            for (int i = 0; i < 4; ++i)
+              hp = ((hg & 1) == 0 && i == 0) ? wv[qi][hg][0] * relu(acc[0]) : fmaf(wv[qi][hg][i], relu(acc[i]), hp);
+            hpart[hg >> 1] = hp;
           }
-          float part = nhg == 1 ? hpart[0]
-                     : nhg == 2 ? hpart[0] + hpart[1]
-                     : nhg == 3 ? (hpart[0] + hpart[1]) + hpart[2]
-                                : (hpart[0] + hpart[1]) + (hpart[2] + hpart[3]);
-          // sum over the four row groups (lanes 16 apart, then 32 apart)
-          const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-          part = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
-          const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-          part = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
-          // every row group now holds the head sum; group g keeps tile g of the four
-          keep[qi] = (u % 4 == g) ? part : keep[qi];
+          part[qi][u % 4] = nhg > 2 ? hpart[0] + hpart[1] : hpart[0];
           if (u % 4 == 3) {
+            // Sum the four row groups of each of the group's four tiles and
+            // leave tile g's sum in row group g: swaps 32 lanes apart pair
+            // tiles 0/2 and 1/3 (lanes 0-31 then hold tiles 0 and 1, lanes
+            // 32-63 tiles 2 and 3), a swap 16 lanes apart splits the pairs.
+            const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi][0]),
+                                                              __float_as_uint(part[qi][2]), false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi][1]),
+                                                              __float_as_uint(part[qi][3]), false, false);
+            const float b0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+            const float b1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+            const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b0), __float_as_uint(b1), false, false);
+            const float tot = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
             const uint32_t j = (uint32_t)t >> 2;          // the group
             const int key = (W + (int)j * NW) * 64 + lane;
             const bool vis = key < nvis[qi];
-            const float sc = vis ? keep[qi] : -INFINITY;
+            const float sc = vis ? tot : -INFINITY;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + j * gs_s, 0, 0);
             if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
           }
@@ -302,6 +308,231 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
 #pragma unroll
   for (int qi = 0; qi < QT; ++qi)
     if (r0 + qi < a.n_qb) flush_hist(lhist[qi], a.hist + ((int64_t)b * a.n_qb + r0 + qi) * kBins1, kBins1);
+}
+
+// ------------------------------------------------------------------ MXFP4 indexer, query blocks
+
+// Many queries per call (a prefill chunk) make the scoring compute-bound, and
+// there the ReLU and head weighting cost more vector instructions than the
+// matrix cores spend on the dot products.  This path therefore
+//  * uses V_MFMA_SCALE_F32_32X32X64_F8F6F4, which runs MXFP4 at twice the
+//    rate of the 16x16x128 form: 32 heads x 32 keys per pair of instructions
+//    (two 64-wide halves of the 128-wide dot product);
+//  * writes w ReLU(s) = (w/2)|s| + (w/2)s.  The first term is one fused
+//    multiply-add per head and key with the absolute value taken as an operand
+//    modifier; the second, summed over heads, is u . k with
+//    u = sum_h (w_h/2) q_h, a single dot product per query and key that the
+//    matrix cores take from index_linear_kernel's FP8 split of u (three E4M3
+//    components, each with its own E8M0 block scales, so u is carried to
+//    about 12 significant bits: the score differs from the exact one by at
+//    most about 2^-12 sum_j |u_j k_j|).
+// Every lane of the result holds 16 heads of one key; the two lane halves are
+// summed by one 32-lane swap that also leaves query 0 in lanes 0-31 and
+// query 1 in lanes 32-63.
+//
+// Operand layouts of the 32x32x64 form (per lane l, K-step s of 64 dims):
+//   MXFP4 (keys, query heads): row/column l % 32, dims 64 s + 32 (l / 32) .. +31
+//     = 16 bytes at byte 32 s + 16 (l / 32) of the 64-byte row, E8M0 scale of
+//     block 2 s + l / 32;
+//   FP8: bytes 0-15 hold dims 64 s + 16 (l / 32) .. +15, bytes 16-31 dims
+//     64 s + 32 + 16 (l / 32) .. +15, E8M0 scale of block 2 s + l / 32;
+//   result element 4 j + i: row 8 j + 4 (l / 32) + i, column l % 32.
+constexpr int kLinBytes = kIndexLinBytes;   // per query: FP8 codes [3][128], scales [3][4] at 384
+constexpr int kLinComps = 3;
+constexpr int kMqQT = 2;             // queries per workgroup
+constexpr int kMqTiles = 64;         // 32-key tiles per wave
+constexpr int kMqRing = 4;           // tiles of keys in flight per wave
+
+// u = sum_h (w_h / 2) q_h for query (b, r) of the block, in fp32 over
+// ascending h, then its three FP8 components: c_1 = RNE(u / s_1),
+// c_2 = RNE((u - s_1 c_1) / s_2), ...; each E8M0 scale s puts its 32-dim
+// block's largest magnitude in [128, 256), inside the E4M3 range.
+__global__ void __launch_bounds__(128) index_linear_kernel(IndexLaunch a) {
+  const int r = blockIdx.x, b = blockIdx.y;
+  const int k = threadIdx.x;                  // dim (d_I = 128)
+  const int64_t qrow = ((int64_t)b * a.n_q + a.q_first + r) * a.H_I;
+  const uint8_t* qc = (const uint8_t*)a.q0;
+  const uint8_t* qsc = (const uint8_t*)a.q1;
+  float u = 0.f;
+  for (int hh = 0; hh < a.H_I; ++hh) {
+    const uint32_t byte = qc[(qrow + hh) * 64 + (k >> 1)];
+    const float v = e2m1_to_f32((byte >> (4 * (k & 1))) & 15u) *
+                    ldexpf(1.0f, (int)qsc[(qrow + hh) * 4 + (k >> 5)] - 127);
+    u = fmaf(0.5f * a.w[qrow + hh], v, u);
+  }
+  uint8_t* out = a.lin + ((int64_t)b * a.n_qb + r) * kLinBytes;
+  float res = u;
+  for (int c = 0; c < kLinComps; ++c) {
+    float m = fabsf(res);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+    int e = -127;
+    if (m > 0.0f) {
+      int ex;
+      frexpf(m, &ex);
+      e = ex - 8;                              // m / 2^e in [128, 256)
+    }
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    const uint32_t code = f32_to_e4m3(res * ldexpf(1.0f, -e));
+    out[c * 128 + k] = (uint8_t)code;
+    if ((k & 31) == 0) out[384 + c * 4 + (k >> 5)] = (uint8_t)(e + 127);
+    res -= e4m3_to_f32(code) * ldexpf(1.0f, e);
+  }
+}
+
+template <int NH32>
+__global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
+  constexpr int QT = kMqQT, R = kMqRing, TPW = kMqTiles;
+  __shared__ uint32_t lhist[QT][kBins1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;        // operand dim half / result row half; after the swap: the query
+  const int col = lane & 31;      // key of the tile; row of the query operands
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * QT;
+  const int live_q = a.n_qb - r0 < QT ? a.n_qb - r0 : QT;
+
+  for (int i = threadIdx.x; i < QT * kBins1; i += 256) (&lhist[0][0])[i] = 0;
+  int nvis[QT];
+  int nvis_max = 0;
+#pragma unroll
+  for (int qi = 0; qi < QT; ++qi) {
+    nvis[qi] = __builtin_amdgcn_readfirstlane(qi < live_q ? query_n_vis(a, b, r0 + qi) : 0);
+    nvis_max = nvis[qi] > nvis_max ? nvis[qi] : nvis_max;
+  }
+  nvis_max = __builtin_amdgcn_readfirstlane(nvis_max);
+  __syncthreads();
+
+  // 32-key tiles are dealt to the waves of the sequence round-robin
+  const int NW = 4 * (int)gridDim.x;
+  const int W = (int)blockIdx.x * 4 + wave;
+  const int ntv = (nvis_max + 31) / 32;        // tiles with a visible key
+  const uint8_t* kc = (const uint8_t*)a.k0 + (int64_t)b * a.n_cap * 64;
+  const uint32_t* ks = (const uint32_t*)a.k1 + (int64_t)b * a.n_cap;
+  // both query rows of the block's scores through one resource: rows past
+  // the live queries are outside it, so their stores are dropped
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.scores + ((int64_t)b * a.n_qb + r0) * a.n_cap), 0,
+      (int)((uint32_t)live_q * (uint32_t)a.n_cap * 4u), kBufferWord3);
+  const int my_nvis = h ? nvis[1] : nvis[0];
+  // byte offset of this lane's score for key `key`; keys past the row map
+  // outside the resource (their stores are dropped instead of landing in the
+  // next query's row)
+  auto score_off = [&](int key) {
+    return key < a.n_cap ? ((uint32_t)h * (uint32_t)a.n_cap + (uint32_t)key) * 4u : 0xfffffff0u;
+  };
+
+  if (W < ntv) {
+    i32x4 qa[QT][NH32][2];
+    int qs[QT][NH32][2];
+    float w2[QT][NH32][16];
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      const int r = qi < live_q ? r0 + qi : r0;
+      const int64_t qrow = ((int64_t)b * a.n_q + a.q_first + r) * a.H_I;
+#pragma unroll
+      for (int hg = 0; hg < NH32; ++hg) {
+        const int64_t head = qrow + hg * 32 + col;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          qa[qi][hg][s] = *(const i32x4*)((const uint8_t*)a.q0 + head * 64 + 32 * s + 16 * h);
+          qs[qi][hg][s] = ((const uint8_t*)a.q1)[head * 4 + 2 * s + h];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          w2[qi][hg][e] = 0.5f * a.w[qrow + hg * 32 + 8 * (e >> 2) + 4 * h + (e & 3)];
+      }
+    }
+    // linear operand: row col = component col / 8 (rows 24-31 zero) of query (col % 4) % 2
+    const int lc = col >> 3;
+    const int lq = (col & 1) < live_q ? (col & 1) : 0;
+    const uint8_t* lin = a.lin + ((int64_t)b * a.n_qb + r0 + lq) * kLinBytes;
+    i32x8 la[2];
+    int ls[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const i32x4 lo = lc < kLinComps ? *(const i32x4*)(lin + lc * 128 + 64 * s + 16 * h) : (i32x4){0, 0, 0, 0};
+      const i32x4 hi = lc < kLinComps ? *(const i32x4*)(lin + lc * 128 + 64 * s + 32 + 16 * h) : (i32x4){0, 0, 0, 0};
+      la[s] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      ls[s] = lc < kLinComps ? (int)lin[384 + lc * 4 + 2 * s + h] : 127;
+    }
+    const __amdgpu_buffer_rsrc_t rc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)((uint32_t)nvis_max * 64u), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)((uint32_t)nvis_max * 4u), kBufferWord3);
+    const uint32_t off_c = (uint32_t)W * 2048u + (uint32_t)col * 64u + (uint32_t)h * 16u;
+    const uint32_t off_s = (uint32_t)W * 128u + (uint32_t)col * 4u;
+    const uint32_t st_c = (uint32_t)NW * 2048u, st_s = (uint32_t)NW * 128u;
+    i32x4 kb[R][2];
+    uint32_t kw[R];
+    auto fetch = [&](int j, int u) {
+      kb[u][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, off_c + (uint32_t)j * st_c, 0, 0));
+      kb[u][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, off_c + (uint32_t)j * st_c + 32u, 0, 0));
+      kw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)j * st_s, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      fetch(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    int vt = (ntv - W + NW - 1) / NW;
+    vt = vt < TPW ? vt : TPW;
+    const int n_rounds = (vt + R - 1) / R;
+    for (int j0 = 0; j0 < n_rounds * R; j0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int j = j0 + u;
+        const i32x8 b0 = {kb[u][0][0], kb[u][0][1], kb[u][0][2], kb[u][0][3], 0, 0, 0, 0};
+        const i32x8 b1 = {kb[u][1][0], kb[u][1][1], kb[u][1][2], kb[u][1][3], 0, 0, 0, 0};
+        const int ks0 = (int)((kw[u] >> (8 * h)) & 0xffu);
+        const int ks1 = (int)((kw[u] >> (8 * (2 + h))) & 0xffu);
+        f32x16 accl = {};
+        accl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[0], b0, accl, 0, 4, 0, ls[0], 0, ks0);
+        accl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[1], b1, accl, 0, 4, 0, ls[1], 0, ks1);
+        float part[QT];
+#pragma unroll
+        for (int qi = 0; qi < QT; ++qi) {
+          float p = 0.f;
+#pragma unroll
+          for (int hg = 0; hg < NH32; ++hg) {
+            const i32x8 a0 = {qa[qi][hg][0][0], qa[qi][hg][0][1], qa[qi][hg][0][2], qa[qi][hg][0][3], 0, 0, 0, 0};
+            const i32x8 a1 = {qa[qi][hg][1][0], qa[qi][hg][1][1], qa[qi][hg][1][2], qa[qi][hg][1][3], 0, 0, 0, 0};
+            f32x16 acc = {};
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc, 4, 4, 0, qs[qi][hg][0], 0, ks0);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc, 4, 4, 0, qs[qi][hg][1], 0, ks1);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) p = fmaf(w2[qi][hg][e], fabsf(acc[e]), p);
+          }
+          part[qi] = p;
+        }
+        // lanes 0-31: query 0, lanes 32-63: query 1, summed over both row halves
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+        const float lin0 = (accl[0] + accl[4]) + accl[8];
+        const float lin1 = (accl[1] + accl[5]) + accl[9];
+        const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + (h ? lin1 : lin0);
+        const int key = (W + j * NW) * 32 + col;
+        const bool vis = key < my_nvis;
+        const float sc = vis ? tot : -INFINITY;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, score_off(key), 0, 0);
+        if (vis) atomicAdd(&lhist[h][order_key(sc) >> kShift1], 1u);
+        fetch(j + R, u);
+      }
+    }
+    // tiles of this wave that the rounds did not reach get -inf
+    for (int j = n_rounds * R; j < TPW; ++j) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc, score_off((W + j * NW) * 32 + col), 0, 0);
+    }
+  } else {
+    // no query sees any key of this wave
+    for (int j = 0; j < TPW; ++j) {
+      const int64_t key = (int64_t)(W + j * NW) * 32 + col;
+      if (h < live_q && key < a.n_cap) a.scores[((int64_t)b * a.n_qb + r0 + h) * a.n_cap + key] = -INFINITY;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qi = 0; qi < QT; ++qi)
+    if (qi < live_q) flush_hist(lhist[qi], a.hist + ((int64_t)b * a.n_qb + r0 + qi) * kBins1, kBins1);
 }
 
 // ------------------------------------------------------------------ fp32 indexer (precision mode)
@@ -620,7 +851,15 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
 
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
-  if (a.fmt == CSA_FMT_MXFP4) {
+  if (a.fmt == CSA_FMT_MXFP4 && a.n_qb >= kMqQT && a.H_I % 32 == 0) {
+    index_linear_kernel<<<dim3(a.n_qb, a.B), 128, 0, s>>>(a);
+    const int per_wg = 4 * kMqTiles * 32;
+    dim3 grid((a.n_cap + per_wg - 1) / per_wg, (a.n_qb + kMqQT - 1) / kMqQT, a.B);
+    if (a.H_I == 64)
+      hipExtLaunchKernelGGL(index_mxfp4_mq_kernel<2>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(index_mxfp4_mq_kernel<1>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+  } else if (a.fmt == CSA_FMT_MXFP4) {
     const int kchunks = (a.n_cap + kKeysPerWG - 1) / kKeysPerWG;
     const int nhg = a.H_I / 16;
     auto go = [&](auto qt, auto hg) {

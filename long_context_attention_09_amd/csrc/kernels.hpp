@@ -58,11 +58,13 @@ struct IndexLaunch {
   uint32_t* cand_key;        // [B * n_qb][n_cap]: chunk c's candidates at [c * 4096, ...)
   int32_t* chunk_cand;       // [B * n_qb][n_chunks] candidates per chunk
   int32_t* chunk_above;      // [B * n_qb][n_chunks] scores above the first-digit bucket
+  uint8_t* lin;              // [B * n_qb][512]: FP8 split of the weighted query sum (query blocks)
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
 // Longest split of a CSA selection list the FP8 attention kernel stages in LDS.
 constexpr int kAttendIdxMax = 2048;
+constexpr int kIndexLinBytes = 512;   // per query of a block: the FP8 split of the weighted query sum
 
 struct AttendLaunch {
   int32_t B, n_q, H, d, d_rope, m, fmt, flags;
