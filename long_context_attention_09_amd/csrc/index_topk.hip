@@ -849,6 +849,198 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
     if ((selmask >> j & 1u) && pos < a.top_k) out[pos++] = (int32_t)(e0 + j);
 }
 
+// Query blocks (many queries per call) replace select by two kernels, so
+// the radix search over a query's candidates runs once per query instead of
+// once per chunk workgroup:
+//   threshold (one workgroup per query) finds the k-th key T among the
+//             candidates of every chunk and, per chunk, where the chunk's
+//             selection starts in the output and how many keys equal to T
+//             come before it; the counts go back over chunk_cand /
+//             chunk_above, T and the number of equal keys to take into the
+//             query's state;
+//   emit      (one workgroup per chunk and query) writes the chunk's indices.
+// The result is the one select gives.
+constexpr int kThrCache = 16;                  // candidates per thread held in registers
+constexpr int kSplitSelectQueries = 64;        // queries per call from which threshold + emit replace select
+__global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
+  const int q = blockIdx.x;
+  const TopkState st = a.state[q];
+  if (st.k_rem < 0) return;
+  constexpr int kCPT = kMaxChunks / 256;
+  const int n_act = (st.n_vis + kChunk - 1) / kChunk;
+  __shared__ int pre[kMaxChunks + 1];
+  __shared__ int cgt[kMaxChunks], ceq[kMaxChunks];
+  __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
+  __shared__ uint32_t s_digit[2], s_kin[2];
+  __shared__ int red[4][4];
+  int* const ccnt_g = a.chunk_cand + (int64_t)q * a.n_chunks;
+  int* const cabv_g = a.chunk_above + (int64_t)q * a.n_chunks;
+  // chunk c's candidates are flat indices pre[c] .. pre[c+1]-1; thread t
+  // holds chunks 4t .. 4t+3 for the scans
+  int cnt[kCPT], abv[kCPT];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int c = kCPT * (int)threadIdx.x + j;
+    cnt[j] = c < n_act ? ccnt_g[c] : 0;
+    abv[j] = c < n_act ? cabv_g[c] : 0;
+    mine += cnt[j];
+  }
+  int n_cand;
+  int run = block_excl_scan(mine, red[0], &n_cand);
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int c = kCPT * (int)threadIdx.x + j;
+    pre[c] = run;
+    run += cnt[j];
+    cgt[c] = 0;
+    ceq[c] = 0;
+  }
+  if (threadIdx.x == 0) pre[kMaxChunks] = n_cand;
+  for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
+  if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
+  __syncthreads();
+  const uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap;
+  // flat candidate i: its chunk (last c with pre[c] <= i) and key
+  auto chunk_of = [&](int i) {
+    int lo = 0, hi = n_act;                      // pre[lo] <= i < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= i) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  uint32_t key_c[kThrCache];
+  int chk_c[kThrCache];
+#pragma unroll
+  for (int j = 0; j < kThrCache; ++j) {
+    const int i = (int)threadIdx.x + 256 * j;
+    chk_c[j] = i < n_cand ? chunk_of(i) : 0;
+    key_c[j] = i < n_cand ? ck[(int64_t)chk_c[j] * kChunk + (i - pre[chk_c[j]])] : 0u;
+  }
+  auto for_each = [&](auto&& visit) {
+#pragma unroll
+    for (int j = 0; j < kThrCache; ++j)
+      if ((int)threadIdx.x + 256 * j < n_cand) visit(key_c[j], chk_c[j]);
+    for (int i = (int)threadIdx.x + 256 * kThrCache; i < n_cand; i += 256) {
+      const int c = chunk_of(i);
+      visit(ck[(int64_t)c * kChunk + (i - pre[c])], c);
+    }
+  };
+  // radix select of the k_rem-th largest candidate: bits 19..10, then 9..0
+  uint32_t prefix = st.b1 << kShift1, mask = 0xfff00000u;
+  uint32_t k = (uint32_t)st.k_rem;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    uint32_t* const bp = bins[pass];
+    const uint32_t mk = mask, px = prefix;
+    for_each([bp, mk, px, shift](uint32_t key, int) {
+      if ((key & mk) == px) atomicAdd(&bp[(key >> shift) & 1023u], 1u);
+    });
+    __syncthreads();
+    uint32_t v[4];
+    my_buckets(bins[pass], v);
+    bucket_search(v, k, &s_digit[pass], &s_kin[pass]);
+    prefix |= s_digit[pass] << shift;
+    mask |= 1023u << shift;
+    k = s_kin[pass];
+  }
+  const uint32_t T = prefix;
+  for_each([T](uint32_t key, int c) {
+    if (key > T) atomicAdd(&cgt[c], 1);
+    else if (key == T) atomicAdd(&ceq[c], 1);
+  });
+  __syncthreads();
+  // per chunk: keys equal to T before it, and the start of its selection
+  int eq_mine = 0;
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) eq_mine += ceq[kCPT * (int)threadIdx.x + j];
+  int eq_run = block_excl_scan(eq_mine, red[1]);
+  int sel[kCPT], eqb[kCPT];
+  int sel_mine = 0;
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int c = kCPT * (int)threadIdx.x + j;
+    const int neq = c < n_act ? ceq[c] : 0;
+    int take = (int)k - eq_run;
+    take = take < 0 ? 0 : (take > neq ? neq : take);
+    eqb[j] = eq_run;
+    sel[j] = c < n_act ? abv[j] + cgt[c] + take : 0;
+    sel_mine += sel[j];
+    eq_run += neq;
+  }
+  int sel_run = block_excl_scan(sel_mine, red[2]);
+#pragma unroll
+  for (int j = 0; j < kCPT; ++j) {
+    const int c = kCPT * (int)threadIdx.x + j;
+    if (c < n_act) {
+      ccnt_g[c] = sel_run;
+      cabv_g[c] = eqb[j];
+    }
+    sel_run += sel[j];
+  }
+  if (threadIdx.x == 0) {
+    a.state[q].T = T;
+    a.state[q].k_eq = (int32_t)k;
+  }
+}
+
+__global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
+  const int q = blockIdx.y;
+  const int b = q / a.n_qb, r = q % a.n_qb;
+  const int chunk = blockIdx.x;
+  const int64_t c0 = (int64_t)chunk * kChunk;
+  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  const int64_t e0 = c0 + threadIdx.x * 16;
+  float sv[16];
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    const int64_t i = e0 + j;
+    if (i + 3 < a.n_cap && (((uintptr_t)(sc + i)) & 15) == 0) {
+      const f32x4 x = *(const f32x4*)(sc + i);
+      sv[j] = x[0]; sv[j + 1] = x[1]; sv[j + 2] = x[2]; sv[j + 3] = x[3];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
+    }
+  }
+  const TopkState st = a.state[q];
+  {
+    uint32_t* gh = a.hist + (int64_t)q * kBins1;
+    for (int i = chunk * 256 + threadIdx.x; i < kBins1; i += a.n_chunks * 256) gh[i] = 0;
+  }
+  int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
+  if (st.k_rem < 0) {
+    for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
+    if (chunk == 0)
+      for (int i = st.n_vis + threadIdx.x; i < a.top_k; i += 256) out[i] = -1;
+    return;
+  }
+  if (c0 >= st.n_vis) return;
+  __shared__ int red[2][4];
+  const int sel_before = a.chunk_cand[(int64_t)q * a.n_chunks + chunk];
+  const int eq_before = a.chunk_above[(int64_t)q * a.n_chunks + chunk];
+  const uint32_t T = st.T;
+  uint32_t gtmask = 0, eqmask = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (e0 + j < st.n_vis) {
+      const uint32_t key = order_key(sv[j]);
+      gtmask |= (uint32_t)(key > T) << j;
+      eqmask |= (uint32_t)(key == T) << j;
+    }
+  }
+  const int eq_excl = eq_before + block_excl_scan(__popc(eqmask), red[1]);
+  int can = st.k_eq - eq_excl;
+  uint32_t selmask = gtmask;
+  for (int j = 0; j < 16 && can > 0; ++j)
+    if (eqmask >> j & 1u) { selmask |= 1u << j; --can; }
+  int pos = sel_before + block_excl_scan(__popc(selmask), red[0]);
+  for (int j = 0; j < 16; ++j)
+    if ((selmask >> j & 1u) && pos < a.top_k) out[pos++] = (int32_t)(e0 + j);
+}
+
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
   if (a.fmt == CSA_FMT_MXFP4 && a.n_qb >= kMqQT && a.H_I % 32 == 0) {
@@ -885,7 +1077,12 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   }
   dim3 g2(a.n_chunks, nq);
   topk_collect_kernel<<<g2, 256, 0, s>>>(a);
-  topk_select_kernel<<<g2, 256, 0, s>>>(a);
+  if (nq >= kSplitSelectQueries) {
+    topk_threshold_kernel<<<nq, 256, 0, s>>>(a);
+    topk_emit_kernel<<<g2, 256, 0, s>>>(a);
+  } else {
+    topk_select_kernel<<<g2, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

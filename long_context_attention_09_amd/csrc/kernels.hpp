@@ -34,7 +34,9 @@ struct TopkState {
   uint32_t b1;        // 12-bit bucket (key >> 20) holding the k-th largest key
   int32_t k_rem;      // how many to take inside bucket b1 (-1: every visible entry)
   int32_t n_vis;      // visible entries of the query
-  int32_t pad[5];
+  uint32_t T;         // the k-th largest key (query blocks: set by the threshold pass)
+  int32_t k_eq;       // keys equal to T to take, lowest indices first (same)
+  int32_t pad[3];
 };
 
 struct IndexLaunch {
