@@ -60,8 +60,8 @@ TRAFFIC = {
         "fetch_kib": 83362.8, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "5d2c44ad12f6abfb4759b96586931e93c206c9ed12421e2abd30a771f996e0f8",
-        "fetch_kib": 69829.4, "write_kib": 8517.0},
+        "sha256": "b3aacd340f01ab6fc68ce2651f22648d7a684deee0bb8cacd0ab3c92e189fd9d",
+        "fetch_kib": 69825.7, "write_kib": 8517.0},
 }
 
 
