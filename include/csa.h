@@ -162,7 +162,12 @@ typedef struct CsaCompressArgs {
  * I_i, ties broken toward the lower index, written in ascending index order;
  * with n_vis <= top_k every visible index is written and the rest is -1.
  * Scores are accumulated in fp32 (E2M1 x E2M1 products and 32-element block
- * sums are exact in fp32).
+ * sums are exact in fp32).  With MXFP4, two or more queries per call and H_I a
+ * multiple of 32, the call evaluates w ReLU(s) as (w/2)|s| + (w/2)s and takes
+ * the second term, summed over heads, from a 3-component FP8 E4M3 split of
+ * sum_h (w_h/2) q_h: such scores (out_score included) differ from the exact
+ * ones by at most about 2^-12 sum_j |u_j k_j|, u = sum_h (w_h/2) q_h.  One
+ * query per call (decode) uses the exact form.
  *
  *   fmt F32:   q0 = fp32 [B][n_q][H_I][d_I]; k0 = fp32 [B][n_cap][d_I].
  *   fmt MXFP4: q0 = codes [B][n_q][H_I][d_I/2], q1 = scales [B][n_q][H_I][d_I/32];
