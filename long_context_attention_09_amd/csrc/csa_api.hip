@@ -89,7 +89,7 @@ int check_index(const CsaIndexArgs* a) {
 
 struct IndexPlan {
   int n_qb, n_chunks;
-  size_t off_scores, off_hist, off_state, off_ckey, off_ccnt, off_above, off_lin, total;
+  size_t off_scores, off_hist, off_state, off_ckey, off_ccnt, off_above, off_csel, off_ceqb, off_lin, total;
 };
 
 IndexPlan plan_index(const CsaIndexArgs* a) {
@@ -115,6 +115,8 @@ IndexPlan plan_index(const CsaIndexArgs* a) {
   p.off_ckey = off;   off += align_up(nq * (size_t)a->n_cap * 4);
   p.off_ccnt = off;   off += align_up(nq * (size_t)p.n_chunks * 4);
   p.off_above = off;  off += align_up(nq * (size_t)p.n_chunks * 4);
+  p.off_csel = off;   off += align_up(nq * (size_t)p.n_chunks * 4);
+  p.off_ceqb = off;   off += align_up(nq * (size_t)p.n_chunks * 4);
   p.off_lin = off;    off += align_up(nq * (size_t)csa::kIndexLinBytes);
   p.total = off;
   return p;
@@ -426,6 +428,8 @@ CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, 
     L.cand_key = (uint32_t*)((char*)ws + p.off_ckey);
     L.chunk_cand = (int32_t*)((char*)ws + p.off_ccnt);
     L.chunk_above = (int32_t*)((char*)ws + p.off_above);
+    L.chunk_sel = (int32_t*)((char*)ws + p.off_csel);
+    L.chunk_eqb = (int32_t*)((char*)ws + p.off_ceqb);
     L.lin = (uint8_t*)((char*)ws + p.off_lin);
     L.ev_start = q0 == 0 ? (hipEvent_t)a->ev_start : nullptr;
     L.ev_stop = q0 + p.n_qb >= a->n_q ? (hipEvent_t)a->ev_stop : nullptr;

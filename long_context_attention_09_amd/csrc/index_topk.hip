@@ -596,6 +596,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total = nu
 
 // Per chunk: keys above the first-digit bucket are counted, keys inside it go
 // to the chunk's own region of the query's candidate list (no global atomics).
+// LIST: the chunk's indices above the bucket and its candidates' indices are
+// also written, in index order, over the chunk's scores.
+template <bool LIST>
 __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   const int q = blockIdx.y;
   const int b = q / a.n_qb, r = q % a.n_qb;
@@ -611,50 +614,118 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
     return;
   }
   if (c0 >= n_vis) return;
-  // this chunk's scores are requested first: they do not depend on the search
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
-  float sv[kChunk / 256];
+  if constexpr (!LIST) {
+    // this chunk's scores are requested first: they do not depend on the search
+    const float* sc = a.scores + (int64_t)q * a.n_cap;
+    float sv[kChunk / 256];
 #pragma unroll
-  for (int j = 0; j < kChunk / 256; ++j) {
-    const int64_t i = c0 + j * 256 + threadIdx.x;
-    sv[j] = i < n_vis ? sc[i] : 0.f;
-  }
-  // every workgroup finds the first-digit bucket of the k-th largest score
-  __shared__ uint32_t s_digit, s_kin;
-  if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
-  {
-    uint32_t v[kBins1 / 256];
-    my_buckets(a.hist + (int64_t)q * kBins1, v);
-    bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
-  }
-  TopkState st = {};
-  st.n_vis = n_vis;
-  st.b1 = s_digit;
-  st.k_rem = (int)s_kin;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
-  uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
-  int above = 0;
-  uint32_t want = 0;
-  uint32_t keys[kChunk / 256];
+    for (int j = 0; j < kChunk / 256; ++j) {
+      const int64_t i = c0 + j * 256 + threadIdx.x;
+      sv[j] = i < n_vis ? sc[i] : 0.f;
+    }
+    // every workgroup finds the first-digit bucket of the k-th largest score
+    __shared__ uint32_t s_digit, s_kin;
+    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
+    {
+      uint32_t v[kBins1 / 256];
+      my_buckets(a.hist + (int64_t)q * kBins1, v);
+      bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
+    }
+    TopkState st = {};
+    st.n_vis = n_vis;
+    st.b1 = s_digit;
+    st.k_rem = (int)s_kin;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
+    uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
+    int above = 0;
+    uint32_t want = 0;
+    uint32_t keys[kChunk / 256];
 #pragma unroll
-  for (int j = 0; j < kChunk / 256; ++j) {
-    const int64_t i = c0 + j * 256 + threadIdx.x;
-    const bool in = i < st.n_vis;
-    keys[j] = in ? order_key(sv[j]) : 0u;
-    const uint32_t d1 = keys[j] >> kShift1;
-    above += (in && d1 > st.b1) ? 1 : 0;
-    want |= (uint32_t)(in && d1 == st.b1) << j;
-  }
-  __shared__ int red[4];
-  int n_here;
-  int slot = block_excl_scan(__popc(want), red, &n_here);
+    for (int j = 0; j < kChunk / 256; ++j) {
+      const int64_t i = c0 + j * 256 + threadIdx.x;
+      const bool in = i < st.n_vis;
+      keys[j] = in ? order_key(sv[j]) : 0u;
+      const uint32_t d1 = keys[j] >> kShift1;
+      above += (in && d1 > st.b1) ? 1 : 0;
+      want |= (uint32_t)(in && d1 == st.b1) << j;
+    }
+    __shared__ int red[4];
+    int n_here;
+    int slot = block_excl_scan(__popc(want), red, &n_here);
 #pragma unroll
-  for (int j = 0; j < kChunk / 256; ++j)
-    if (want >> j & 1u) ck[slot++] = keys[j];
-  above = block_sum_int(above, red);
-  if (threadIdx.x == 0) {
-    a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = above;
-    a.chunk_cand[(int64_t)q * a.n_chunks + blockIdx.x] = n_here;
+    for (int j = 0; j < kChunk / 256; ++j)
+      if (want >> j & 1u) ck[slot++] = keys[j];
+    above = block_sum_int(above, red);
+    if (threadIdx.x == 0) {
+      a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = above;
+      a.chunk_cand[(int64_t)q * a.n_chunks + blockIdx.x] = n_here;
+    }
+  } else {
+    // Lists of indices in index order: the chunk's scores are loaded
+    // coalesced (thread t: entries c0 + 256 j + t) and passed through LDS so
+    // that thread t then holds the 16 consecutive entries c0 + 16 t + j; the
+    // scans in thread order then give index order.  (LDS rows padded by one
+    // word per 16 so both passes are free of bank conflicts.)
+    float* const sc = a.scores + (int64_t)q * a.n_cap;
+    constexpr int PT = kChunk / 256;
+    __shared__ float tr[kChunk + kChunk / 16];
+    float sv[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int64_t i = c0 + j * 256 + threadIdx.x;
+      sv[j] = i < n_vis ? sc[i] : 0.f;
+    }
+    __shared__ uint32_t s_digit, s_kin;
+    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
+    {
+      uint32_t v[kBins1 / 256];
+      my_buckets(a.hist + (int64_t)q * kBins1, v);
+      bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
+    }
+    TopkState st = {};
+    st.n_vis = n_vis;
+    st.b1 = s_digit;
+    st.k_rem = (int)s_kin;
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int e = j * 256 + (int)threadIdx.x;
+      tr[e + (e >> 4)] = sv[j];
+    }
+    __syncthreads();
+    const int64_t e0 = c0 + 16 * (int64_t)threadIdx.x;
+    uint32_t keys[PT];
+    uint32_t want = 0, above = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int e = 16 * (int)threadIdx.x + j;
+      const bool in = e0 + j < st.n_vis;
+      keys[j] = in ? order_key(tr[e + (e >> 4)]) : 0u;
+      const uint32_t d1 = keys[j] >> kShift1;
+      above |= (uint32_t)(in && d1 > st.b1) << j;
+      want |= (uint32_t)(in && d1 == st.b1) << j;
+    }
+    __shared__ int red[2][4];
+    int n_here, n_above;
+    int slot = block_excl_scan(__popc(want), red[0], &n_here);
+    int aslot = block_excl_scan(__popc(above), red[1], &n_above);
+    uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
+    // the chunk's own score region (read in full above) takes the indices
+    // above the bucket, then the candidates' indices
+    uint32_t* const lst = (uint32_t*)sc + c0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      if (want >> j & 1u) {
+        ck[slot] = keys[j];
+        lst[n_above + slot] = (uint32_t)(e0 + j);
+        ++slot;
+      }
+      if (above >> j & 1u) lst[aslot++] = (uint32_t)(e0 + j);
+    }
+    if (threadIdx.x == 0) {
+      a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = n_above;
+      a.chunk_cand[(int64_t)q * a.n_chunks + blockIdx.x] = n_here;
+    }
   }
 }
 
@@ -862,10 +933,22 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
 // The result is the one select gives.
 constexpr int kThrCache = 16;                  // candidates per thread held in registers
 constexpr int kSplitSelectQueries = 64;        // queries per call from which threshold + emit replace select
+constexpr int kFusedTopK = 2048;               // largest top_k the threshold pass emits itself (list mode)
 __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
   const int q = blockIdx.x;
   const TopkState st = a.state[q];
-  if (st.k_rem < 0) return;
+  int32_t* const out = a.out_idx + ((int64_t)(q / a.n_qb) * a.n_q + a.q_first + q % a.n_qb) * a.top_k;
+  if (a.list_mode) {
+    // this pass also writes the output: leave the histogram zeroed here
+    uint32_t* gh = a.hist + (int64_t)q * kBins1;
+    for (int i = threadIdx.x; i < kBins1; i += 256) gh[i] = 0;
+  }
+  if (st.k_rem < 0) {
+    if (a.list_mode) {
+      for (int i = threadIdx.x; i < a.top_k; i += 256) out[i] = i < st.n_vis ? i : -1;
+    }
+    return;
+  }
   constexpr int kCPT = kMaxChunks / 256;
   const int n_act = (st.n_vis + kChunk - 1) / kChunk;
   __shared__ int pre[kMaxChunks + 1];
@@ -873,6 +956,8 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
   __shared__ __attribute__((aligned(16))) uint32_t bins[2][1024];
   __shared__ uint32_t s_digit[2], s_kin[2];
   __shared__ int red[4][4];
+  __shared__ int apre[kMaxChunks + 1];          // list mode: above-bucket indices before chunk c
+  __shared__ uint32_t fa[kFusedTopK], fs[kFusedTopK];
   int* const ccnt_g = a.chunk_cand + (int64_t)q * a.n_chunks;
   int* const cabv_g = a.chunk_above + (int64_t)q * a.n_chunks;
   // chunk c's candidates are flat indices pre[c] .. pre[c+1]-1; thread t
@@ -886,17 +971,20 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
     abv[j] = c < n_act ? cabv_g[c] : 0;
     mine += cnt[j];
   }
-  int n_cand;
+  int n_cand, n_ab;
   int run = block_excl_scan(mine, red[0], &n_cand);
+  int arun = block_excl_scan(abv[0] + abv[1] + abv[2] + abv[3], red[1], &n_ab);
 #pragma unroll
   for (int j = 0; j < kCPT; ++j) {
     const int c = kCPT * (int)threadIdx.x + j;
     pre[c] = run;
     run += cnt[j];
+    apre[c] = arun;
+    arun += abv[j];
     cgt[c] = 0;
     ceq[c] = 0;
   }
-  if (threadIdx.x == 0) pre[kMaxChunks] = n_cand;
+  if (threadIdx.x == 0) { pre[kMaxChunks] = n_cand; apre[kMaxChunks] = n_ab; }
   for (int i = threadIdx.x; i < 2 * 1024; i += 256) (&bins[0][0])[i] = 0;
   if (threadIdx.x < 2) { s_digit[threadIdx.x] = 0; s_kin[threadIdx.x] = 0; }
   __syncthreads();
@@ -975,8 +1063,8 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
   for (int j = 0; j < kCPT; ++j) {
     const int c = kCPT * (int)threadIdx.x + j;
     if (c < n_act) {
-      ccnt_g[c] = sel_run;
-      cabv_g[c] = eqb[j];
+      a.chunk_sel[(int64_t)q * a.n_chunks + c] = sel_run;
+      a.chunk_eqb[(int64_t)q * a.n_chunks + c] = eqb[j];
     }
     sel_run += sel[j];
   }
@@ -984,13 +1072,82 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
     a.state[q].T = T;
     a.state[q].k_eq = (int32_t)k;
   }
+  if (!a.list_mode) return;
+  // List mode (collect left, in each chunk's score region, the indices above
+  // the bucket and then the candidates' indices, both ascending): the
+  // selection is the above-bucket indices of every chunk (fa) merged with the
+  // candidates above T and the first k of those equal to T (fs), all in index
+  // order; chunks are ascending index ranges, so flat order is index order.
+  const uint32_t* const lst = (const uint32_t*)(a.scores + (int64_t)q * a.n_cap);
+  auto chunk_in = [&](const int* pf, int i) {   // last c with pf[c] <= i
+    int lo = 0, hi = n_act;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pf[mid] <= i) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  int n_s = 0, eq_seen = 0;
+  for (int j0 = 0; j0 < n_cand; j0 += 256) {
+    const int i = j0 + (int)threadIdx.x;
+    const bool live = i < n_cand;
+    const int c = live ? chunk_of(i) : 0;
+    const uint32_t key = live ? ck[(int64_t)c * kChunk + (i - pre[c])] : 0u;
+    const bool gt = live && key > T, eq = live && key == T;
+    int eq_tot, take_tot;
+    const int er = eq_seen + block_excl_scan(eq ? 1 : 0, red[2], &eq_tot);
+    const bool take = gt || (eq && er < (int)k);
+    const int p = n_s + block_excl_scan(take ? 1 : 0, red[3], &take_tot);
+    if (take && p < kFusedTopK) fs[p] = lst[(int64_t)c * kChunk + (apre[c + 1] - apre[c]) + (i - pre[c])];
+    n_s += take_tot;
+    eq_seen += eq_tot;
+  }
+  for (int i = threadIdx.x; i < n_ab && i < kFusedTopK; i += 256) {
+    const int c = chunk_in(apre, i);
+    fa[i] = lst[(int64_t)c * kChunk + (i - apre[c])];
+  }
+  __syncthreads();
+  auto below = [](const uint32_t* v, int n, uint32_t x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (v[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  // output rank = rank in its own list + elements of the other list below it
+  for (int i = threadIdx.x; i < n_ab; i += 256) {
+    const int pos = i + below(fs, n_s, fa[i]);
+    if (pos < a.top_k) out[pos] = (int32_t)fa[i];
+  }
+  for (int i = threadIdx.x; i < n_s; i += 256) {
+    const int pos = i + below(fa, n_ab, fs[i]);
+    if (pos < a.top_k) out[pos] = (int32_t)fs[i];
+  }
 }
 
+// Emit from the scores: one workgroup per chunk (the caller's score array).
 __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
   const int q = blockIdx.y;
   const int b = q / a.n_qb, r = q % a.n_qb;
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
+  const TopkState st = a.state[q];
+  {
+    uint32_t* gh = a.hist + (int64_t)q * kBins1;
+    for (int i = chunk * 256 + threadIdx.x; i < kBins1; i += a.n_chunks * 256) gh[i] = 0;
+  }
+  int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
+  if (st.k_rem < 0) {
+    for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
+    if (chunk == 0)
+      for (int i = st.n_vis + threadIdx.x; i < a.top_k; i += 256) out[i] = -1;
+    return;
+  }
+  if (c0 >= st.n_vis) return;
+  const int sel_before = a.chunk_sel[(int64_t)q * a.n_chunks + chunk];
+  const int eq_before = a.chunk_eqb[(int64_t)q * a.n_chunks + chunk];
+  const uint32_t T = st.T;
   const float* sc = a.scores + (int64_t)q * a.n_cap;
   const int64_t e0 = c0 + threadIdx.x * 16;
   float sv[16];
@@ -1005,23 +1162,7 @@ __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
       for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
     }
   }
-  const TopkState st = a.state[q];
-  {
-    uint32_t* gh = a.hist + (int64_t)q * kBins1;
-    for (int i = chunk * 256 + threadIdx.x; i < kBins1; i += a.n_chunks * 256) gh[i] = 0;
-  }
-  int32_t* out = a.out_idx + ((int64_t)b * a.n_q + a.q_first + r) * a.top_k;
-  if (st.k_rem < 0) {
-    for (int64_t i = c0 + threadIdx.x; i < c0 + kChunk && i < st.n_vis; i += 256) out[i] = (int32_t)i;
-    if (chunk == 0)
-      for (int i = st.n_vis + threadIdx.x; i < a.top_k; i += 256) out[i] = -1;
-    return;
-  }
-  if (c0 >= st.n_vis) return;
   __shared__ int red[2][4];
-  const int sel_before = a.chunk_cand[(int64_t)q * a.n_chunks + chunk];
-  const int eq_before = a.chunk_above[(int64_t)q * a.n_chunks + chunk];
-  const uint32_t T = st.T;
   uint32_t gtmask = 0, eqmask = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -1040,6 +1181,7 @@ __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
   for (int j = 0; j < 16; ++j)
     if ((selmask >> j & 1u) && pos < a.top_k) out[pos++] = (int32_t)(e0 + j);
 }
+
 
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
@@ -1076,12 +1218,18 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
     hipExtLaunchKernelGGL(index_f32_kernel, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
   }
   dim3 g2(a.n_chunks, nq);
-  topk_collect_kernel<<<g2, 256, 0, s>>>(a);
+  IndexLaunch t = a;
+  // with many queries and the scores in the workspace, collect leaves the
+  // selected-index lists in place of the scores and the threshold pass
+  // writes the output from them (no emit launch)
+  t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK;
+  if (t.list_mode) topk_collect_kernel<true><<<g2, 256, 0, s>>>(t);
+  else topk_collect_kernel<false><<<g2, 256, 0, s>>>(t);
   if (nq >= kSplitSelectQueries) {
-    topk_threshold_kernel<<<nq, 256, 0, s>>>(a);
-    topk_emit_kernel<<<g2, 256, 0, s>>>(a);
+    topk_threshold_kernel<<<nq, 256, 0, s>>>(t);
+    if (!t.list_mode) topk_emit_kernel<<<g2, 256, 0, s>>>(t);
   } else {
-    topk_select_kernel<<<g2, 256, 0, s>>>(a);
+    topk_select_kernel<<<g2, 256, 0, s>>>(t);
   }
   return hipGetLastError();
 }

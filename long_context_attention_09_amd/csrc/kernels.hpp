@@ -60,6 +60,9 @@ struct IndexLaunch {
   uint32_t* cand_key;        // [B * n_qb][n_cap]: chunk c's candidates at [c * 4096, ...)
   int32_t* chunk_cand;       // [B * n_qb][n_chunks] candidates per chunk
   int32_t* chunk_above;      // [B * n_qb][n_chunks] scores above the first-digit bucket
+  int32_t* chunk_sel;        // [B * n_qb][n_chunks] query blocks: output start of the chunk's selection
+  int32_t* chunk_eqb;        // [B * n_qb][n_chunks] query blocks: keys equal to T before the chunk
+  int32_t list_mode;         // collect leaves the chunk's selected-index lists in its score region
   uint8_t* lin;              // [B * n_qb][512]: FP8 split of the weighted query sum (query blocks)
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
