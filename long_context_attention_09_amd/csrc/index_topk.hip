@@ -594,6 +594,29 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total = nu
 
 
 
+// Query blocks: the first-digit bucket of the k-th largest score and the rank
+// inside it, once per query (the list form of collect reads it from the
+// state instead of every chunk workgroup searching the histogram).
+__global__ void __launch_bounds__(256) topk_bucket_kernel(IndexLaunch a) {
+  const int q = blockIdx.x;
+  const int b = q / a.n_qb, r = q % a.n_qb;
+  const int n_vis = query_n_vis(a, b, r);
+  TopkState st = {};
+  st.n_vis = n_vis;
+  if (n_vis <= a.top_k) {                       // every visible entry is taken
+    st.k_rem = -1;
+  } else {
+    __shared__ uint32_t s_digit, s_kin;
+    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
+    uint32_t v[kBins1 / 256];
+    my_buckets(a.hist + (int64_t)q * kBins1, v);
+    bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
+    st.b1 = s_digit;
+    st.k_rem = (int)s_kin;
+  }
+  if (threadIdx.x == 0) a.state[q] = st;
+}
+
 // Per chunk: keys above the first-digit bucket are counted, keys inside it go
 // to the chunk's own region of the query's candidate list (no global atomics).
 // LIST: the chunk's indices above the bucket and its candidates' indices are
@@ -605,7 +628,7 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   const int n_vis = query_n_vis(a, b, r);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   if (n_vis <= a.top_k) {                       // every visible entry is taken
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (!LIST && blockIdx.x == 0 && threadIdx.x == 0) {
       TopkState st = {};
       st.n_vis = n_vis;
       st.k_rem = -1;
@@ -675,18 +698,8 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
       const int64_t i = c0 + j * 256 + threadIdx.x;
       sv[j] = i < n_vis ? sc[i] : 0.f;
     }
-    __shared__ uint32_t s_digit, s_kin;
-    if (threadIdx.x == 0) { s_digit = 0; s_kin = 0; }
-    {
-      uint32_t v[kBins1 / 256];
-      my_buckets(a.hist + (int64_t)q * kBins1, v);
-      bucket_search(v, (uint32_t)a.top_k, &s_digit, &s_kin);
-    }
-    TopkState st = {};
-    st.n_vis = n_vis;
-    st.b1 = s_digit;
-    st.k_rem = (int)s_kin;
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.state[q] = st;
+    // the bucket of the k-th key, found once per query by topk_bucket_kernel
+    const TopkState st = a.state[q];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int e = j * 256 + (int)threadIdx.x;
@@ -1223,8 +1236,12 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   // selected-index lists in place of the scores and the threshold pass
   // writes the output from them (no emit launch)
   t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK;
-  if (t.list_mode) topk_collect_kernel<true><<<g2, 256, 0, s>>>(t);
-  else topk_collect_kernel<false><<<g2, 256, 0, s>>>(t);
+  if (t.list_mode) {
+    topk_bucket_kernel<<<nq, 256, 0, s>>>(t);
+    topk_collect_kernel<true><<<g2, 256, 0, s>>>(t);
+  } else {
+    topk_collect_kernel<false><<<g2, 256, 0, s>>>(t);
+  }
   if (nq >= kSplitSelectQueries) {
     topk_threshold_kernel<<<nq, 256, 0, s>>>(t);
     if (!t.list_mode) topk_emit_kernel<<<g2, 256, 0, s>>>(t);
