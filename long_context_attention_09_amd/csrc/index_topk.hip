@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
 constexpr int kLinBytes = kIndexLinBytes;   // per query: FP8 codes [3][128], scales [3][4] at 384
 constexpr int kLinComps = 3;
 constexpr int kMqQT = 2;             // queries per workgroup
-constexpr int kMqTiles = 64;         // 32-key tiles per wave
+constexpr int kMqTiles = 256;        // 32-key tiles per wave
 constexpr int kMqRing = 4;           // tiles of keys in flight per wave
 
 // u = sum_h (w_h / 2) q_h for query (b, r) of the block, in fp32 over
