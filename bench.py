@@ -60,7 +60,7 @@ TRAFFIC = {
         "fetch_kib": 83362.8, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "b3aacd340f01ab6fc68ce2651f22648d7a684deee0bb8cacd0ab3c92e189fd9d",
+        "sha256": "87922bde620fe4c773d828f48a9d1b2368821f68ee53e6cccd1936397bc7c50e",
         "fetch_kib": 69825.7, "write_kib": 8517.0},
 }
 
