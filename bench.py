@@ -60,7 +60,7 @@ TRAFFIC = {
         "fetch_kib": 83362.8, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "87922bde620fe4c773d828f48a9d1b2368821f68ee53e6cccd1936397bc7c50e",
+        "sha256": "c3ed423c0ab27ac553428022494903b77456bf9d186f6457b46290f78a1bb369",
         "fetch_kib": 69825.7, "write_kib": 8517.0},
 }
 

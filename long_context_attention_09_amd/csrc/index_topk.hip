@@ -14,9 +14,14 @@
 // side.  A 16-key tile is one contiguous 1 KiB read (64 B of codes per key);
 // each lane loads 16 bytes straight into its operand registers, so keys
 // stream from HBM exactly once.  ReLU and the head weights are applied to the
-// 4 accumulator rows a lane holds, and two cross-lane adds finish the head
-// sum.  The kernel also builds the histogram of the top 12 bits of every
-// score's order key for the first radix-select pass.
+// 4 accumulator rows a lane holds, and cross-lane swaps over four tiles at a
+// time finish the head sum.  The kernel also builds the histogram of the top
+// 12 bits of every score's order key for the first radix-select pass.
+//
+// Query blocks (two or more queries per call, H_I a multiple of 32; a prefill
+// chunk) use index_mxfp4_mq_kernel instead: the 32x32x64 form of the scaled
+// MFMA and a split of w ReLU(s) into (w/2)|s| + (w/2)s whose second term comes
+// from an FP8 split of the weighted query sum (see that kernel).
 //
 // Top-k over the 32-bit order keys of the scores.  The scoring kernel builds a
 // histogram of the top 12 key bits, then two kernels follow, one workgroup
@@ -30,6 +35,8 @@
 //           output, and emits the chunk's selected indices in index order,
 //           so the output is ascending; among keys equal to T the lowest
 //           indices are taken.
+// With 64 or more queries per call the radix search runs once per query
+// instead (topk_bucket_kernel, topk_threshold_kernel; see there).
 // Histograms use integer atomics only and candidate lists are compacted per
 // chunk by block scans, so the result does not depend on any ordering and is
 // deterministic.  The histogram is left zeroed by every call.  Kernel
