@@ -298,6 +298,42 @@ def test_prefill_index_dispatch(shape, signed):
     _prefill_check(shape, inp, step, rows)
 
 
+def test_prefill_index_with_scores():
+    """The query-block path with the caller keeping the scores (out_score):
+    the threshold pass then leaves per-chunk counts and the emit kernel writes
+    the selection from the scores; it must equal the list path's selection,
+    and the scores must match the oracle's within the split's bound."""
+    K = _K()
+    from long_context_attention_09_amd.layer import LayerStep
+    shape = synth.PRO_CSA_PREFILL.replace(L=16384, n_q=70)
+    _say(f"prefill index with out_score {shape.name} n_q={shape.n_q}")
+    inp = synth.quant_prefill_inputs(shape)
+    step = LayerStep(shape, to_dev(inp), prefill=True)
+    step.run()
+    torch.cuda.synchronize()
+    kc, ks = step.keys[0]
+    n_cap = kc.shape[1]
+    score = torch.empty(shape.B, shape.n_q, n_cap, device="cuda")
+    idx2 = torch.empty_like(step.idx)
+    K.index_topk(step.inp["q_idx_codes"], step.inp["w"], kc, step.inp["q_pos"], m=shape.m,
+                 top_k=shape.top_k, out_idx=idx2, q1=step.inp["q_idx_scales"], k1=ks,
+                 out_score=score, fmt=K.FMT_MXFP4)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, step.idx), "selection differs between the list and score paths"
+    prep = P.prefill_prepare(shape, inp, 0)
+    for r in (0, shape.n_q // 2, shape.n_q - 1):
+        ref = P.prefill_query(shape, inp, prep, 0, r, sel=idx2[0, r].cpu().numpy())
+        n_vis = ref["n_vis"]
+        sc = score[0, r].cpu().numpy().astype(np.float64)
+        assert np.all(np.isneginf(sc[n_vis:]))
+        rs = ref["scores"]
+        # the FP8 split of the linear half: |error| <= about 2^-12 sum_j |u_j k_j|,
+        # below 5e-4 |s_k| on these inputs (checked against 1e-3 |s_k| here)
+        s_k = np.sort(rs)[::-1][shape.top_k - 1]
+        assert np.abs(sc[:n_vis] - rs).max() <= 1e-3 * abs(s_k), r
+        check_topk(idx2[0, r].cpu().numpy(), rs, shape.top_k)
+
+
 def test_decode_signed_weights():
     K = _K()
     from long_context_attention_09_amd.layer import LayerStep
