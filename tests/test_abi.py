@@ -104,6 +104,25 @@ def test_index_validation_and_workspace(K):
     assert lib.csa_index_topk(C.byref(a), FAKE, n - 256, None) == K.CSA_EWORKSPACE
 
 
+def test_index_workspace_query_blocks(K):
+    """Many queries (a prefill chunk) are scored in blocks that fit a fixed
+    budget of scores + candidate keys (8 B per query and entry), so the
+    workspace stops growing with n_q; with caller-kept scores it holds no
+    score array."""
+    lib = K.load()
+
+    def ws(**kw):
+        a = _index_args(K, B=1, n_cap=264192, **kw)
+        return lib.csa_workspace_bytes(K.OP_INDEX_TOPK, C.cast(C.pointer(a), C.c_void_p))
+
+    per_q = 264192 * 8
+    small, full, twice = ws(n_q=64), ws(n_q=8192), ws(n_q=16384)
+    assert small >= 64 * per_q
+    assert full == twice                      # bounded by the block budget
+    assert (3 << 30) - per_q <= full - 1524 * 16 * 1024 <= (3 << 30) + (16 << 20)
+    assert ws(n_q=64, out_score=FAKE) < small  # no score array in the workspace
+
+
 def _attend_args(K, **kw):
     a = K.AttendArgs(B=32, n_q=1, H=64, d=512, d_rope=64, m=128, fmt=K.FMT_FP8_BF16, flags=1,
                      rope_theta=160000.0, softmax_scale=0.0, top_k=0, n_cap=8192, n_win=128,
