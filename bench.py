@@ -319,7 +319,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="timed prefill chunks (0: no prefill measurement)")
-    ap.add_argument("--prefill-oracle-rows", type=int, default=4,
+    ap.add_argument("--prefill-oracle-rows", type=int, default=16,
                     help="query rows per layer the oracle is timed on (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB elementwise copy used to scale HBM counters")
