@@ -164,10 +164,11 @@ typedef struct CsaCompressArgs {
  * Scores are accumulated in fp32 (E2M1 x E2M1 products and 32-element block
  * sums are exact in fp32).  With MXFP4, two or more queries per call and H_I a
  * multiple of 32, the call evaluates w ReLU(s) as (w/2)|s| + (w/2)s and takes
- * the second term, summed over heads, from a 3-component FP8 E4M3 split of
- * sum_h (w_h/2) q_h: such scores (out_score included) differ from the exact
- * ones by at most about 2^-12 sum_j |u_j k_j|, u = sum_h (w_h/2) q_h.  One
- * query per call (decode) uses the exact form.
+ * the second term, summed over heads, from a 6-component FP8 E4M3 split of
+ * u = sum_h (w_h/2) q_h (per 32-dim block, each component carries 4 more
+ * bits): such scores (out_score included) differ from the exact ones by at
+ * most about 2^-24 sum_blocks max|u| sum|k|, the order of fp32 rounding.
+ * One query per call (decode) uses the exact form.
  *
  *   fmt F32:   q0 = fp32 [B][n_q][H_I][d_I]; k0 = fp32 [B][n_cap][d_I].
  *   fmt MXFP4: q0 = codes [B][n_q][H_I][d_I/2], q1 = scales [B][n_q][H_I][d_I/32];
@@ -185,7 +186,10 @@ typedef struct CsaCompressArgs {
  * Workspace: csa_workspace_bytes(CSA_OP_INDEX_TOPK, &args) bytes of device
  * memory, 256-byte aligned, used by this op only.  It must be zero-filled
  * before its first use; every call leaves its counters and histogram zeroed
- * again, so later calls need no refill (refill after a failed launch).
+ * again, so later calls need no refill (refill after a failed launch).  The
+ * call runs its queries in blocks of csa_index_query_block(&args) queries
+ * per sequence, so the workspace stays below about 3 GiB at any n_q (with
+ * or without out_score).
  * Constraint: n_cap <= 4194304.
  * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
  * records on `stream` around its scoring kernel (with several internal query
@@ -329,6 +333,12 @@ size_t csa_compress_workspace_bytes(const CsaCompressArgs* jobs, int n_jobs);
 int csa_compress_batch_ws(const CsaCompressArgs* jobs, int n_jobs, void* workspace, size_t workspace_bytes,
                           void* stream);
 int csa_index_topk(const CsaIndexArgs* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Queries per sequence that csa_index_topk scores and selects per internal
+ * block for `args` (its workspace holds one block); a negative status for
+ * invalid arguments.  Calls whose visible-entry count changes at a block
+ * boundary are where the blocks meet. */
+int csa_index_query_block(const CsaIndexArgs* args);
 int csa_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 int hca_attend(const CsaAttendArgs* args, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
     lib.csa_compress_workspace_bytes.argtypes = [C.POINTER(CompressArgs), C.c_int]
     lib.csa_compress_batch_ws.argtypes = [C.POINTER(CompressArgs), C.c_int, _vp, C.c_size_t, _vp]
     lib.csa_index_topk.argtypes = [C.POINTER(IndexArgs), _vp, C.c_size_t, _vp]
+    lib.csa_index_query_block.argtypes = [C.POINTER(IndexArgs)]
+    lib.csa_index_query_block.restype = C.c_int
     lib.csa_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
     lib.hca_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
     for fn in ("csa_compress", "csa_compress_batch", "csa_compress_batch_ws", "csa_index_topk", "csa_attend",
@@ -237,6 +239,15 @@ def index_args(q0, w, k0, q_pos, *, m, top_k, out_idx, q1=None, k1=None, n_entri
                      q_pos=_ptr(q_pos), n_entries=_ptr(n_entries), q0=_ptr(q0), q1=_ptr(q1),
                      w=_ptr(w), k0=_ptr(k0), k1=_ptr(k1), out_idx=_ptr(out_idx),
                      out_score=_ptr(out_score))
+
+
+def index_query_block(*args, **kw):
+    """csa_index_query_block: queries per sequence in each internal block of a
+    csa_index_topk call with these arguments."""
+    n = load().csa_index_query_block(C.byref(index_args(*args, **kw)))
+    if n < 1:
+        raise CsaError(n if n < 0 else CSA_EWORKSPACE, "csa_index_query_block")
+    return n
 
 
 def index_topk(*args, workspace=None, **kw):

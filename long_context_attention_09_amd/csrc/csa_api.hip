@@ -1,14 +1,18 @@
 // Host side of the C ABI declared in include/csa.h: argument validation,
-// workspace sizing and kernel launches.  No allocation, no synchronisation,
-// no global mutable state.
+// workspace sizing and kernel launches.  No allocation and no
+// synchronisation; the only global state is the per-device address of the
+// allocation-free entry point's scratch array, looked up once per device.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
 #include "csa.h"
 #include "kernels.hpp"
+#include "api_internal.hpp"
 
 #define CSA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -16,7 +20,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kIdxChunk = 4096;       // scores per workgroup in the radix passes
-constexpr int64_t kWorkspaceBudget = int64_t(3) << 30;   // per-query-block score + candidate bytes
 constexpr int64_t kMaxIndexCap = int64_t(1024) * 4096;  // entries per sequence the top-k handles
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -63,7 +66,12 @@ int check_compress(const CsaCompressArgs* a) {
   return CSA_OK;
 }
 
+}  // namespace
+
 // ------------------------------------------------------------------ index / top-k
+
+namespace csa {
+namespace api {
 
 int check_index(const CsaIndexArgs* a) {
   if (!a) return CSA_EINVAL;
@@ -87,26 +95,13 @@ int check_index(const CsaIndexArgs* a) {
   return CSA_OK;
 }
 
-struct IndexPlan {
-  int n_qb, n_chunks;
-  size_t off_scores, off_hist, off_state, off_ckey, off_ccnt, off_above, off_csel, off_ceqb, off_lin, total;
-};
 
-IndexPlan plan_index(const CsaIndexArgs* a) {
+// Workspace layout for query blocks of n_qb queries per sequence.
+IndexPlan index_layout(const CsaIndexArgs* a, int n_qb) {
   IndexPlan p;
   p.n_chunks = (a->n_cap + kIdxChunk - 1) / kIdxChunk;
-  if (a->out_score) {
-    p.n_qb = a->n_q;
-  } else {
-    // scores + candidate keys: 8 bytes per (query, entry)
-    const int64_t per_q = (int64_t)a->B * a->n_cap * 8;
-    int64_t n = kWorkspaceBudget / (per_q > 0 ? per_q : 1);
-    if (n < 1) n = 1;
-    if (n > a->n_q) n = a->n_q;
-    if (n >= 4) n -= n % 4;
-    p.n_qb = (int)n;
-  }
-  const size_t nq = (size_t)a->B * p.n_qb;
+  p.n_qb = n_qb;
+  const size_t nq = (size_t)a->B * n_qb;
   size_t off = 0;
   p.off_scores = off;
   if (!a->out_score) off += align_up(nq * (size_t)a->n_cap * 4);
@@ -121,6 +116,36 @@ IndexPlan plan_index(const CsaIndexArgs* a) {
   p.total = off;
   return p;
 }
+
+// The largest query block (a multiple of 4 from 4 queries on) whose
+// workspace fits `budget` bytes; n_qb = 0 when one query does not fit.
+IndexPlan plan_index(const CsaIndexArgs* a, int64_t budget) {
+  const int64_t n_chunks = (a->n_cap + kIdxChunk - 1) / kIdxChunk;
+  const int64_t per_q = (int64_t)a->B * ((a->out_score ? 0 : (int64_t)a->n_cap * 4) + (int64_t)a->n_cap * 4 +
+                                         4096 * 4 + (int64_t)sizeof(csa::TopkState) + 4 * n_chunks * 4 +
+                                         csa::kIndexLinBytes);
+  int64_t n = budget / (per_q > 0 ? per_q : 1);
+  if (n > a->n_q) n = a->n_q;
+  if (n >= 4) n -= n % 4;
+  if (n < 1) n = 1;
+  IndexPlan p = index_layout(a, (int)n);
+  while (p.total > (size_t)budget && n > 1) {   // alignment padding
+    n = n > 4 ? n - 4 : n - 1;
+    p = index_layout(a, (int)n);
+  }
+  if (p.total > (size_t)budget) p.n_qb = 0;
+  return p;
+}
+
+}  // namespace api
+}  // namespace csa
+
+namespace {
+
+using csa::api::IndexPlan;
+using csa::api::kWorkspaceBudget;
+using csa::api::check_index;
+using csa::api::plan_index;
 
 // ------------------------------------------------------------------ attention
 
@@ -279,7 +304,8 @@ CSA_EXPORT size_t csa_workspace_bytes(int op, const void* args) {
     case CSA_OP_INDEX_TOPK: {
       const CsaIndexArgs* a = (const CsaIndexArgs*)args;
       if (check_index(a)) return (size_t)-1;
-      return plan_index(a).total;
+      const IndexPlan p = plan_index(a, kWorkspaceBudget);
+      return p.n_qb < 1 ? (size_t)-1 : p.total;
     }
     case CSA_OP_ATTEND:
     case CSA_OP_HCA_ATTEND: {
@@ -408,11 +434,11 @@ CSA_EXPORT int csa_compress(const CsaCompressArgs* a, void* stream) {
   return csa_compress_batch(a, 1, stream);
 }
 
-CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_index(a);
-  if (st) return st;
-  const IndexPlan p = plan_index(a);
-  if (!ws || ws_bytes < p.total || !aligned(ws, kAlign)) return CSA_EWORKSPACE;
+namespace csa {
+namespace api {
+
+// Query blocks of p.n_qb queries, each through the workspace laid out by p.
+int run_index(const CsaIndexArgs* a, const IndexPlan& p, char* ws, void* stream) {
   for (int q0 = 0; q0 < a->n_q; q0 += p.n_qb) {
     csa::IndexLaunch L{};
     L.B = a->B; L.n_q = a->n_q; L.m = a->m; L.n_cap = a->n_cap; L.H_I = a->H_I; L.d_I = a->d_I;
@@ -422,20 +448,49 @@ CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, 
     L.q_pos = a->q_pos; L.n_entries = a->n_entries;
     L.q0 = a->q0; L.q1 = a->q1; L.w = a->w; L.k0 = a->k0; L.k1 = a->k1;
     L.out_idx = a->out_idx; L.out_score = a->out_score;
-    L.scores = a->out_score ? a->out_score : (float*)((char*)ws + p.off_scores);
-    L.hist = (uint32_t*)((char*)ws + p.off_hist);
-    L.state = (csa::TopkState*)((char*)ws + p.off_state);
-    L.cand_key = (uint32_t*)((char*)ws + p.off_ckey);
-    L.chunk_cand = (int32_t*)((char*)ws + p.off_ccnt);
-    L.chunk_above = (int32_t*)((char*)ws + p.off_above);
-    L.chunk_sel = (int32_t*)((char*)ws + p.off_csel);
-    L.chunk_eqb = (int32_t*)((char*)ws + p.off_ceqb);
-    L.lin = (uint8_t*)((char*)ws + p.off_lin);
+    if (a->out_score) {
+      // the caller's [B][n_q][n_cap] array: block rows start at q0 within each sequence
+      L.scores = a->out_score;
+      L.score_seq_rows = a->n_q;
+      L.score_row0 = q0;
+    } else {
+      L.scores = (float*)(ws + p.off_scores);
+      L.score_seq_rows = L.n_qb;
+      L.score_row0 = 0;
+    }
+    L.hist = (uint32_t*)(ws + p.off_hist);
+    L.state = (csa::TopkState*)(ws + p.off_state);
+    L.cand_key = (uint32_t*)(ws + p.off_ckey);
+    L.chunk_cand = (int32_t*)(ws + p.off_ccnt);
+    L.chunk_above = (int32_t*)(ws + p.off_above);
+    L.chunk_sel = (int32_t*)(ws + p.off_csel);
+    L.chunk_eqb = (int32_t*)(ws + p.off_ceqb);
+    L.lin = (uint8_t*)(ws + p.off_lin);
     L.ev_start = q0 == 0 ? (hipEvent_t)a->ev_start : nullptr;
     L.ev_stop = q0 + p.n_qb >= a->n_q ? (hipEvent_t)a->ev_stop : nullptr;
     if (csa::launch_index_topk(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;
   }
   return CSA_OK;
+}
+
+}  // namespace api
+}  // namespace csa
+
+using csa::api::run_index;
+
+CSA_EXPORT int csa_index_query_block(const CsaIndexArgs* a) {
+  const int st = check_index(a);
+  if (st) return st;
+  return plan_index(a, kWorkspaceBudget).n_qb;
+}
+
+CSA_EXPORT int csa_index_topk(const CsaIndexArgs* a, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_index(a);
+  if (st) return st;
+  const IndexPlan p = plan_index(a, kWorkspaceBudget);
+  if (p.n_qb < 1) return CSA_EWORKSPACE;
+  if (!ws || ws_bytes < p.total || !aligned(ws, kAlign)) return CSA_EWORKSPACE;
+  return run_index(a, p, (char*)ws, stream);
 }
 
 CSA_EXPORT int csa_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream) {

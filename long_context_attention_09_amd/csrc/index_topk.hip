@@ -70,6 +70,12 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// Score row of query r of sequence b in this query block: the workspace holds
+// the block's rows [B][n_qb]; a caller's score array holds all [B][n_q] rows.
+__device__ __forceinline__ float* score_row(const IndexLaunch& a, int b, int r) {
+  return a.scores + ((int64_t)b * a.score_seq_rows + a.score_row0 + r) * a.n_cap;
+}
+
 __device__ __forceinline__ int query_n_vis(const IndexLaunch& a, int b, int r) {
   const int64_t t = a.q_pos[(int64_t)b * a.n_q + a.q_first + r];
   int64_t v = t >= 0 ? t / a.m : 0;
@@ -212,7 +218,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) {
       const bool live = r0 + qi < a.n_qb;
-      float* srow = a.scores + ((int64_t)b * a.n_qb + (live ? r0 + qi : r0)) * a.n_cap;
+      float* srow = score_row(a, b, live ? r0 + qi : r0);
       rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)((uint32_t)a.n_cap * 4u) : 0, kBufferWord3);
     }
     const uint32_t gs_c = (uint32_t)NW * 4096u, gs_s = (uint32_t)NW * 256u;   // group strides: codes, words
@@ -304,7 +310,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // no query sees any key of this wave
     for (int qi = 0; qi < QT; ++qi) {
       if (r0 + qi >= a.n_qb) break;
-      float* row = a.scores + ((int64_t)b * a.n_qb + r0 + qi) * a.n_cap;
+      float* row = score_row(a, b, r0 + qi);
       for (int j = 0; j < kGroups; ++j) {
         const int64_t k = (int64_t)(W + j * NW) * 64 + lane;
         if (k < a.n_cap) row[k] = -INFINITY;
@@ -329,10 +335,13 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
 //    multiply-add per head and key with the absolute value taken as an operand
 //    modifier; the second, summed over heads, is u . k with
 //    u = sum_h (w_h/2) q_h, a single dot product per query and key that the
-//    matrix cores take from index_linear_kernel's FP8 split of u (three E4M3
+//    matrix cores take from index_linear_kernel's FP8 split of u (six E4M3
 //    components, each with its own E8M0 block scales, so u is carried to
-//    about 12 significant bits: the score differs from the exact one by at
-//    most about 2^-12 sum_j |u_j k_j|).
+//    about 24 significant bits of its block maximum: the score differs from
+//    the exact one by at most about 2^-24 sum_blocks max|u| sum |k|, the
+//    order of fp32 rounding).  The linear operand's 32 rows hold
+//    component 4 (row / 8) + row % 4 of query (row / 4) % 2, so a lane's
+//    result elements 0-5 are the six components of the query of its lane half.
 // Every lane of the result holds 16 heads of one key; the two lane halves are
 // summed by one 32-lane swap that also leaves query 0 in lanes 0-31 and
 // query 1 in lanes 32-63.
@@ -344,16 +353,22 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
 //   FP8: bytes 0-15 hold dims 64 s + 16 (l / 32) .. +15, bytes 16-31 dims
 //     64 s + 32 + 16 (l / 32) .. +15, E8M0 scale of block 2 s + l / 32;
 //   result element 4 j + i: row 8 j + 4 (l / 32) + i, column l % 32.
-constexpr int kLinBytes = kIndexLinBytes;   // per query: FP8 codes [3][128], scales [3][4] at 384
-constexpr int kLinComps = 3;
+constexpr int kLinComps = 6;
+constexpr int kLinScaleOff = kLinComps * 128;   // per query: FP8 codes [6][128], then E8M0 scales [6][4]
+constexpr int kLinBytes = kIndexLinBytes;
+static_assert(kLinScaleOff + kLinComps * 4 <= kLinBytes, "linear split fits its slot");
 constexpr int kMqQT = 2;             // queries per workgroup
 constexpr int kMqTiles = 256;        // 32-key tiles per wave
 constexpr int kMqRing = 4;           // tiles of keys in flight per wave
 
 // u = sum_h (w_h / 2) q_h for query (b, r) of the block, in fp32 over
-// ascending h, then its three FP8 components: c_1 = RNE(u / s_1),
+// ascending h, then its six FP8 components: c_1 = RNE(u / s_1),
 // c_2 = RNE((u - s_1 c_1) / s_2), ...; each E8M0 scale s puts its 32-dim
-// block's largest magnitude in [128, 256), inside the E4M3 range.
+// block's largest magnitude in [128, 256), inside the E4M3 range.  Every
+// stage leaves at most 2^-4 of the block's largest magnitude (relative
+// rounding 2^-4 for normal codes, 2^-10 absolute below them), so after six
+// the residual of every element is below 2^-24 max_block |u|: the split
+// carries u as far as fp32 does.
 __global__ void __launch_bounds__(128) index_linear_kernel(IndexLaunch a) {
   const int r = blockIdx.x, b = blockIdx.y;
   const int k = threadIdx.x;                  // dim (d_I = 128)
@@ -382,7 +397,7 @@ __global__ void __launch_bounds__(128) index_linear_kernel(IndexLaunch a) {
     e = e < -127 ? -127 : (e > 127 ? 127 : e);
     const uint32_t code = f32_to_e4m3(res * ldexpf(1.0f, -e));
     out[c * 128 + k] = (uint8_t)code;
-    if ((k & 31) == 0) out[384 + c * 4 + (k >> 5)] = (uint8_t)(e + 127);
+    if ((k & 31) == 0) out[kLinScaleOff + c * 4 + (k >> 5)] = (uint8_t)(e + 127);
     res -= e4m3_to_f32(code) * ldexpf(1.0f, e);
   }
 }
@@ -419,7 +434,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   // both query rows of the block's scores through one resource: rows past
   // the live queries are outside it, so their stores are dropped
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.scores + ((int64_t)b * a.n_qb + r0) * a.n_cap), 0,
+      (void*)score_row(a, b, r0), 0,
       (int)((uint32_t)live_q * (uint32_t)a.n_cap * 4u), kBufferWord3);
   const int my_nvis = h ? nvis[1] : nvis[0];
   // byte offset of this lane's score for key `key`; keys past the row map
@@ -450,9 +465,10 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
           w2[qi][hg][e] = 0.5f * a.w[qrow + hg * 32 + 8 * (e >> 2) + 4 * h + (e & 3)];
       }
     }
-    // linear operand: row col = component col / 8 (rows 24-31 zero) of query (col % 4) % 2
-    const int lc = col >> 3;
-    const int lq = (col & 1) < live_q ? (col & 1) : 0;
+    // linear operand: row col = component 4 (col / 8) + col % 4 (components
+    // 6, 7 of the 8-row groups are zero) of query (col / 4) % 2
+    const int lc = 4 * (col >> 3) + (col & 3);
+    const int lq = ((col >> 2) & 1) < live_q ? ((col >> 2) & 1) : 0;
     const uint8_t* lin = a.lin + ((int64_t)b * a.n_qb + r0 + lq) * kLinBytes;
     i32x8 la[2];
     int ls[2];
@@ -461,7 +477,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
       const i32x4 lo = lc < kLinComps ? *(const i32x4*)(lin + lc * 128 + 64 * s + 16 * h) : (i32x4){0, 0, 0, 0};
       const i32x4 hi = lc < kLinComps ? *(const i32x4*)(lin + lc * 128 + 64 * s + 32 + 16 * h) : (i32x4){0, 0, 0, 0};
       la[s] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      ls[s] = lc < kLinComps ? (int)lin[384 + lc * 4 + 2 * s + h] : 127;
+      ls[s] = lc < kLinComps ? (int)lin[kLinScaleOff + lc * 4 + 2 * s + h] : 127;
     }
     const __amdgpu_buffer_rsrc_t rc =
         __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)((uint32_t)nvis_max * 64u), kBufferWord3);
@@ -514,9 +530,9 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
         }
         // lanes 0-31: query 0, lanes 32-63: query 1, summed over both row halves
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-        const float lin0 = (accl[0] + accl[4]) + accl[8];
-        const float lin1 = (accl[1] + accl[5]) + accl[9];
-        const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + (h ? lin1 : lin0);
+        // the linear term of this lane half's query, smallest components first
+        const float lin = ((((accl[5] + accl[4]) + accl[3]) + accl[2]) + accl[1]) + accl[0];
+        const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + lin;
         const int key = (W + j * NW) * 32 + col;
         const bool vis = key < my_nvis;
         const float sc = vis ? tot : -INFINITY;
@@ -533,7 +549,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
     // no query sees any key of this wave
     for (int j = 0; j < TPW; ++j) {
       const int64_t key = (int64_t)(W + j * NW) * 32 + col;
-      if (h < live_q && key < a.n_cap) a.scores[((int64_t)b * a.n_qb + r0 + h) * a.n_cap + key] = -INFINITY;
+      if (h < live_q && key < a.n_cap) score_row(a, b, r0 + h)[key] = -INFINITY;
     }
   }
   __syncthreads();
@@ -565,7 +581,7 @@ __global__ void __launch_bounds__(256) index_f32_kernel(IndexLaunch a) {
       }
       atomicAdd(&lhist[order_key(s) >> kShift1], 1u);
     }
-    a.scores[((int64_t)b * a.n_qb + r) * a.n_cap + key] = s;
+    score_row(a, b, r)[key] = s;
   }
   __syncthreads();
   flush_hist(lhist, a.hist + ((int64_t)b * a.n_qb + r) * kBins1, kBins1);
@@ -646,7 +662,7 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
   if (c0 >= n_vis) return;
   if constexpr (!LIST) {
     // this chunk's scores are requested first: they do not depend on the search
-    const float* sc = a.scores + (int64_t)q * a.n_cap;
+    const float* sc = score_row(a, q / a.n_qb, q % a.n_qb);
     float sv[kChunk / 256];
 #pragma unroll
     for (int j = 0; j < kChunk / 256; ++j) {
@@ -696,7 +712,7 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
     // that thread t then holds the 16 consecutive entries c0 + 16 t + j; the
     // scans in thread order then give index order.  (LDS rows padded by one
     // word per 16 so both passes are free of bank conflicts.)
-    float* const sc = a.scores + (int64_t)q * a.n_cap;
+    float* const sc = score_row(a, q / a.n_qb, q % a.n_qb);
     constexpr int PT = kChunk / 256;
     __shared__ float tr[kChunk + kChunk / 16];
     float sv[PT];
@@ -776,7 +792,7 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   const int slot_shift = __builtin_ctz(slots);
   // ---- one round trip: this thread's 16 scores, the state, every chunk's
   // counts and the leading candidate slots
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  const float* sc = score_row(a, q / a.n_qb, q % a.n_qb);
   const int64_t e0 = c0 + threadIdx.x * 16;
   float sv[16];
 #pragma unroll
@@ -1098,7 +1114,7 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
   // selection is the above-bucket indices of every chunk (fa) merged with the
   // candidates above T and the first k of those equal to T (fs), all in index
   // order; chunks are ascending index ranges, so flat order is index order.
-  const uint32_t* const lst = (const uint32_t*)(a.scores + (int64_t)q * a.n_cap);
+  const uint32_t* const lst = (const uint32_t*)(score_row(a, q / a.n_qb, q % a.n_qb));
   auto chunk_in = [&](const int* pf, int i) {   // last c with pf[c] <= i
     int lo = 0, hi = n_act;
     while (hi - lo > 1) {
@@ -1168,7 +1184,7 @@ __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
   const int sel_before = a.chunk_sel[(int64_t)q * a.n_chunks + chunk];
   const int eq_before = a.chunk_eqb[(int64_t)q * a.n_chunks + chunk];
   const uint32_t T = st.T;
-  const float* sc = a.scores + (int64_t)q * a.n_cap;
+  const float* sc = score_row(a, q / a.n_qb, q % a.n_qb);
   const int64_t e0 = c0 + threadIdx.x * 16;
   float sv[16];
 #pragma unroll

@@ -54,7 +54,9 @@ struct IndexLaunch {
   int32_t* out_idx;
   float* out_score;          // full [B][n_q][n_cap] output (optional)
   // workspace views (per query of the block: q_local = b * n_qb + r)
-  float* scores;             // [B * n_qb][n_cap]
+  float* scores;             // score rows: row (b, r) at (b * score_seq_rows + score_row0 + r) * n_cap
+  int32_t score_seq_rows;    // n_qb for the workspace, n_q for the caller's out_score
+  int32_t score_row0;        // 0 for the workspace, q_first for the caller's out_score
   uint32_t* hist;            // [B * n_qb][4096]            zeroed after use
   TopkState* state;          // [B * n_qb]
   uint32_t* cand_key;        // [B * n_qb][n_cap]: chunk c's candidates at [c * 4096, ...)
@@ -63,13 +65,13 @@ struct IndexLaunch {
   int32_t* chunk_sel;        // [B * n_qb][n_chunks] query blocks: output start of the chunk's selection
   int32_t* chunk_eqb;        // [B * n_qb][n_chunks] query blocks: keys equal to T before the chunk
   int32_t list_mode;         // collect leaves the chunk's selected-index lists in its score region
-  uint8_t* lin;              // [B * n_qb][512]: FP8 split of the weighted query sum (query blocks)
+  uint8_t* lin;              // [B * n_qb][kIndexLinBytes]: FP8 split of the weighted query sum (query blocks)
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
 };
 
 // Longest split of a CSA selection list the FP8 attention kernel stages in LDS.
 constexpr int kAttendIdxMax = 2048;
-constexpr int kIndexLinBytes = 512;   // per query of a block: the FP8 split of the weighted query sum
+constexpr int kIndexLinBytes = 1024;  // per query of a block: the FP8 split of the weighted query sum
 
 struct AttendLaunch {
   int32_t B, n_q, H, d, d_rope, m, fmt, flags;

@@ -41,6 +41,8 @@ class Shape:
     fp32: bool = False
     planted: float = 0.0   # fraction of indexer keys carrying a query-aligned direction
     seed: int = 0
+    signed_w: bool = False  # indexer head weights N(0,1)/sqrt(H_I) instead of |N(0,1)|/sqrt(H_I)
+    mx_exp: tuple = ()      # (lo, hi): MXFP4 block exponents uniform on lo..hi instead of -2..0
 
     @property
     def csa(self) -> bool:
@@ -106,9 +108,13 @@ def mxfp4_codes(shape: Shape, tag: str, rows: int, D: int, device="cpu"):
     mag = torch.multinomial(p, rows * D, replacement=True, generator=g).reshape(rows, D)
     sign = torch.randint(0, 2, (rows, D), generator=g, device=device)
     nib = (mag | (sign << 3)).to(torch.uint8)
-    ex = torch.tensor(list(_SCALE_EXP_P.keys()), device=device)
-    pe = torch.tensor(list(_SCALE_EXP_P.values()), device=device)
-    se = ex[torch.multinomial(pe, rows * (D // 32), replacement=True, generator=g)]
+    if shape.mx_exp:
+        lo, hi = shape.mx_exp
+        se = torch.randint(lo, hi + 1, (rows * (D // 32),), generator=g, device=device)
+    else:
+        ex = torch.tensor(list(_SCALE_EXP_P.keys()), device=device)
+        pe = torch.tensor(list(_SCALE_EXP_P.values()), device=device)
+        se = ex[torch.multinomial(pe, rows * (D // 32), replacement=True, generator=g)]
     scales = (se + 127).to(torch.uint8).reshape(rows, D // 32)
     codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
     return codes, scales
@@ -143,6 +149,12 @@ def plant(shape: Shape, tag: str, codes, scales, q_codes, q_scales, w, device="c
     codes[which] = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
     scales[which] = 126
     return which
+
+
+def head_weights(shape: Shape, size, device="cpu"):
+    """Indexer head weights: |N(0,1)|/sqrt(H_I), or N(0,1)/sqrt(H_I) with signed_w."""
+    w = normal(shape, "w", size, device)
+    return (w if shape.signed_w else w.abs()) / shape.H_I ** 0.5
 
 
 def fp8_bf16_rows(shape: Shape, tag: str, rows: int, device="cpu"):
@@ -217,7 +229,7 @@ def quant_decode_inputs(shape: Shape, device="cpu", copies: int = 1):
         qc, qs = mxfp4_codes(shape, "q_idx", B * shape.H_I, shape.d_I, device)
         inp["q_idx_codes"] = qc.reshape(B, 1, shape.H_I, -1)
         inp["q_idx_scales"] = qs.reshape(B, 1, shape.H_I, -1)
-        inp["w"] = normal(shape, "w", (B, 1, shape.H_I), device).abs() / shape.H_I ** 0.5
+        inp["w"] = head_weights(shape, (B, 1, shape.H_I), device)
         for c in range(copies):
             sfx = "" if c == 0 else f"_{c}"
             kc, ks = mxfp4_codes(shape, f"keys{sfx}", B * n_e, shape.d_I, device)
@@ -260,7 +272,7 @@ def quant_prefill_inputs(shape: Shape, device="cpu"):
         qc, qs = mxfp4_codes(shape, "q_idx", B * n_q * shape.H_I, shape.d_I, device)
         inp["q_idx_codes"] = qc.reshape(B, n_q, shape.H_I, -1)
         inp["q_idx_scales"] = qs.reshape(B, n_q, shape.H_I, -1)
-        inp["w"] = normal(shape, "w", (B, n_q, shape.H_I), device).abs() / shape.H_I ** 0.5
+        inp["w"] = head_weights(shape, (B, n_q, shape.H_I), device)
         kc, ks = mxfp4_codes(shape, "keys", B * n_e, shape.d_I, device)
         inp["keys_codes_old"] = kc.reshape(B, n_e, -1)
         inp["keys_scales_old"] = ks.reshape(B, n_e, -1)

@@ -105,22 +105,34 @@ def test_index_validation_and_workspace(K):
 
 
 def test_index_workspace_query_blocks(K):
-    """Many queries (a prefill chunk) are scored in blocks that fit a fixed
-    budget of scores + candidate keys (8 B per query and entry), so the
-    workspace stops growing with n_q; with caller-kept scores it holds no
-    score array."""
+    """Many queries (a prefill chunk) are scored in blocks whose whole
+    workspace fits a fixed 3 GiB budget, so the workspace stops growing with
+    n_q, also when the caller keeps the scores (then it holds no score array);
+    csa_index_query_block reports the block size the workspace was sized for."""
     lib = K.load()
+    lib.csa_index_query_block.restype = C.c_int
 
     def ws(**kw):
         a = _index_args(K, B=1, n_cap=264192, **kw)
         return lib.csa_workspace_bytes(K.OP_INDEX_TOPK, C.cast(C.pointer(a), C.c_void_p))
 
+    def qb(**kw):
+        a = _index_args(K, B=1, n_cap=264192, **kw)
+        return lib.csa_index_query_block(C.byref(a))
+
     per_q = 264192 * 8
     small, full, twice = ws(n_q=64), ws(n_q=8192), ws(n_q=16384)
-    assert small >= 64 * per_q
-    assert full == twice                      # bounded by the block budget
-    assert (3 << 30) - per_q <= full - 1524 * 16 * 1024 <= (3 << 30) + (16 << 20)
-    assert ws(n_q=64, out_score=FAKE) < small  # no score array in the workspace
+    assert small >= 64 * per_q and qb(n_q=64) == 64
+    assert full == twice and full <= (3 << 30)        # bounded by the block budget
+    n_qb = qb(n_q=8192)
+    assert n_qb % 4 == 0 and (3 << 30) - 5 * (per_q + 20 * 1024) < n_qb * (per_q + 16 * 1024) <= (3 << 30)
+    # caller-kept scores: no score array, and the block budget still holds
+    assert ws(n_q=64, out_score=FAKE) < small
+    s_full, s_twice = ws(n_q=8192, out_score=FAKE), ws(n_q=16384, out_score=FAKE)
+    assert s_full == s_twice and s_full <= (3 << 30)
+    assert qb(n_q=8192, out_score=FAKE) > n_qb
+    bad = _index_args(K, B=1, n_cap=264192, n_q=8, top_k=0)
+    assert lib.csa_index_query_block(C.byref(bad)) == K.CSA_EINVAL
 
 
 def _attend_args(K, **kw):

@@ -1,0 +1,96 @@
+"""GPU parity of the lightning indexer and top-k on inputs chosen to stress
+the arithmetic: head weights of both signs (N(0,1), so head terms cancel)
+and MXFP4 block exponents spread over -20 .. 10 (so block products differ
+by up to 2^30 and the fp32 cross-block sums round).
+
+Every dispatch is covered: one query per call (exact form, select pass),
+query blocks below 64 queries (select pass) and from 64 (list pass without
+scores, threshold + emit with scores).  Scores must match the oracle within
+a bound derived from the arithmetic, the selections with and without
+caller-kept scores must be identical, and both must obey the top-k tie rule
+against the oracle's fp64 scores (the indexer of "DeepSeek-V4 深读", section
+"CSA：4× 压缩之后再 top-k"; MXFP4 QK from its FP4 QAT section).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import csa as OC
+from oracle import formats as F
+
+from parity_util import check_topk
+
+pytestmark = pytest.mark.gpu
+
+ADV = synth.PRO_CSA_PREFILL.replace(name="index-adversarial", signed_w=True, mx_exp=(-20, 10))
+
+
+def _K():
+    import long_context_attention_09_amd._lib as K
+    K.load()
+    return K
+
+
+def _inputs(shape, B, n_q, L, extra=64):
+    n_cap = L // shape.m + extra
+    kc, ks = synth.mxfp4_codes(shape, f"keys/{L}", B * n_cap, shape.d_I)
+    qc, qs = synth.mxfp4_codes(shape, f"q_idx/{L}/{n_q}", B * n_q * shape.H_I, shape.d_I)
+    w = synth.head_weights(shape.replace(name=f"{shape.name}/{L}/{n_q}"), (B, n_q, shape.H_I))
+    q_pos = (L + torch.arange(n_q, dtype=torch.int64)).expand(B, n_q).contiguous()
+    return dict(kc=kc.reshape(B, n_cap, -1), ks=ks.reshape(B, n_cap, -1),
+                qc=qc.reshape(B, n_q, shape.H_I, -1), qs=qs.reshape(B, n_q, shape.H_I, -1), w=w, q_pos=q_pos)
+
+
+def _run(K, inp, top_k, m, with_scores):
+    dev = {k: v.cuda() for k, v in inp.items()}
+    B, n_q = inp["w"].shape[:2]
+    idx = torch.empty(B, n_q, top_k, dtype=torch.int32, device="cuda")
+    score = torch.empty(B, n_q, inp["kc"].shape[1], device="cuda") if with_scores else None
+    K.index_topk(dev["qc"], dev["w"], dev["kc"], dev["q_pos"], m=m, top_k=top_k, out_idx=idx, q1=dev["qs"],
+                 k1=dev["ks"], out_score=score, fmt=K.FMT_MXFP4)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (score.cpu().numpy().astype(np.float64) if with_scores else None)
+
+
+CASES = [(1, 2, 1 << 18), (33, 1, 1 << 16), (70, 1, 1 << 16)]
+
+
+@pytest.mark.parametrize("n_q,B,L", CASES, ids=lambda v: str(v))
+def test_index_signed_weights_spread_exponents(n_q, B, L):
+    K = _K()
+    s = ADV
+    print(f"[gpu] adversarial index n_q={n_q} B={B} L={L}", flush=True)
+    inp = _inputs(s, B, n_q, L)
+    idx_s, sc = _run(K, inp, s.top_k, s.m, True)
+    idx_l, _ = _run(K, inp, s.top_k, s.m, False)
+    assert np.array_equal(idx_s, idx_l), "selection differs with and without caller-kept scores"
+    worst = 0.0
+    for b in range(B):
+        keys = F.decode_mxfp4(inp["kc"][b].numpy(), inp["ks"][b].numpy())
+        for r in sorted({0, n_q // 2, n_q - 1}):
+            qI = F.decode_mxfp4(inp["qc"][b, r].numpy(), inp["qs"][b, r].numpy())
+            w = inp["w"][b, r].numpy().astype(np.float64)
+            t = int(inp["q_pos"][b, r])
+            n_vis = OC.visible_entries(t, s.m, keys.shape[0])
+            ref = OC.index_scores(qI, w, keys, n_vis)
+            # |error| bound: every E2M1 product and 32-element block sum is exact; a
+            # score is then an fp32 sum of about 100 terms (64 weighted head terms,
+            # each an fp32 sum of 4 block terms, and in query blocks the 6 FP8
+            # components x 4 blocks of u . k, u = sum_h (w_h / 2) q_h, whose split
+            # leaves each element of u within 2^-24 of its block's largest
+            # magnitude).  Recursive fp32 summation of n terms errs by at most
+            # (n - 1) 2^-24 times the sum of their magnitudes: 2^-17 here.
+            ak = np.abs(keys[:n_vis])
+            u = np.abs(0.5 * (w[:, None] * qI).sum(0))
+            u_blk = np.repeat(u.reshape(-1, 32).max(axis=1), 32)
+            mag = (ak @ np.abs(qI).T) @ np.abs(w) + ak @ u_blk
+            err = np.abs(sc[b, r, :n_vis] - ref)
+            assert np.all(err <= 2.0 ** -17 * mag), (b, r, float((err / np.maximum(mag, 1e-300)).max()))
+            assert np.all(np.isneginf(sc[b, r, n_vis:]))
+            s_k = np.sort(ref)[::-1][s.top_k - 1]
+            worst = max(worst, float(err.max() / abs(s_k)))
+            check_topk(idx_s[b, r], ref, s.top_k)
+    print(f"[gpu]   worst score error / |s_k| = {worst:.3e}", flush=True)

@@ -259,10 +259,10 @@ def test_prefill_chunk_full_size_sampled(shape):
     torch.cuda.synchronize()
     rows = {0, 1, 3, 4, 127, 128, shape.n_q - 2, shape.n_q - 1}
     if shape.csa:
-        # the library's block: 3 GiB of scores + candidate keys (8 B per query and entry)
-        per_q = shape.B * step.keys[0][0].shape[1] * 8
-        n_qb = min(shape.n_q, (3 << 30) // per_q)
-        n_qb -= n_qb % 4
+        # the library's own query-block size for this call
+        a = step._prepared(0)["index"]
+        n_qb = _K().load().csa_index_query_block(a)
+        assert 4 <= n_qb < shape.n_q
         _say(f"  query block {n_qb}")
         for q0 in range(n_qb, shape.n_q, n_qb):
             rows |= {q0 - 1, q0}
