@@ -25,11 +25,15 @@
  *   - Status: CSA_OK (0); CSA_EINVAL (-1) null pointer, misaligned pointer or
  *     inconsistent shape; CSA_EUNSUPPORTED (-2) a shape or format combination
  *     this build has no kernel for; CSA_EHIP (-3) a launch error reported by
- *     the HIP runtime; CSA_EWORKSPACE (-4) workspace missing or too small.
+ *     the HIP runtime; CSA_EWORKSPACE (-4) workspace missing or too small;
+ *     CSA_ESCRATCH (-5) a problem too large for csa_index_topk_noalloc.
  *   - Deterministic: for a fixed input and shape the results are bitwise
  *     reproducible; no kernel uses order-dependent floating-point atomics.
- *   - Thread-safe: the library keeps no mutable global state.  Calls that
- *     share a workspace must be ordered on one stream by the caller.
+ *   - Thread-safe: the library's only mutable global state is the table of
+ *     per-device scratch addresses of csa_index_topk_noalloc, filled once per
+ *     device under a lock.  Calls that share a workspace (or, for the
+ *     allocation-free entry point, a GPU) must be ordered on one stream by
+ *     the caller.
  *   - Positions are absolute token positions (int64).  Token p of a
  *     sequence is the p-th token of its context, starting at 0.
  *
@@ -64,8 +68,12 @@ enum {
   CSA_EINVAL = -1,
   CSA_EUNSUPPORTED = -2,
   CSA_EHIP = -3,
-  CSA_EWORKSPACE = -4
+  CSA_EWORKSPACE = -4,
+  CSA_ESCRATCH = -5
 };
+
+/* Device bytes of the scratch array behind csa_index_topk_noalloc (per GPU). */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 enum { CSA_FMT_F32 = 0, CSA_FMT_FP8_BF16 = 1, CSA_FMT_MXFP4 = 2 };
 enum { CSA_DT_F32 = 0, CSA_DT_BF16 = 1 };
@@ -333,6 +341,24 @@ size_t csa_compress_workspace_bytes(const CsaCompressArgs* jobs, int n_jobs);
 int csa_compress_batch_ws(const CsaCompressArgs* jobs, int n_jobs, void* workspace, size_t workspace_bytes,
                           void* stream);
 int csa_index_topk(const CsaIndexArgs* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* csa_index_topk without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc).  Same arguments, results and
+ * determinism as csa_index_topk; no allocation of any kind.
+ *
+ * Workspace: a library-owned device array of CSA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held until the process ends; the call runs its queries
+ * in blocks that fit it (fewer queries per block than csa_index_topk uses,
+ * so large prefill chunks take more launches).  A call whose single query
+ * (B sequences of it) does not fit (about B * n_cap * 8 bytes + B * 17 KiB
+ * > 64 MiB; n_cap = 262144 allows B <= 30) returns CSA_ESCRATCH and
+ * launches nothing.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind; the call itself clears what must start at
+ * zero.  Calls that overlap in time on one GPU (different streams or host
+ * threads without ordering) race on the array: order them on one stream.
+ * `stream` must belong to the current device. */
+int csa_index_topk_noalloc(const CsaIndexArgs* args, void* stream);
 
 /* Queries per sequence that csa_index_topk scores and selects per internal
  * block for `args` (its workspace holds one block); a negative status for

@@ -16,7 +16,8 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
-CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP, CSA_EWORKSPACE = 0, -1, -2, -3, -4
+CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP, CSA_EWORKSPACE, CSA_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 FMT_F32, FMT_FP8_BF16, FMT_MXFP4 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 OP_COMPRESS, OP_INDEX_TOPK, OP_ATTEND, OP_HCA_ATTEND = 0, 1, 2, 3
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH):
     lib.csa_compress_workspace_bytes.argtypes = [C.POINTER(CompressArgs), C.c_int]
     lib.csa_compress_batch_ws.argtypes = [C.POINTER(CompressArgs), C.c_int, _vp, C.c_size_t, _vp]
     lib.csa_index_topk.argtypes = [C.POINTER(IndexArgs), _vp, C.c_size_t, _vp]
+    lib.csa_index_topk_noalloc.argtypes = [C.POINTER(IndexArgs), _vp]
+    lib.csa_index_topk_noalloc.restype = C.c_int
     lib.csa_index_query_block.argtypes = [C.POINTER(IndexArgs)]
     lib.csa_index_query_block.restype = C.c_int
     lib.csa_attend.argtypes = [C.POINTER(AttendArgs), _vp, C.c_size_t, _vp]
@@ -255,6 +258,13 @@ def index_topk(*args, workspace=None, **kw):
     ws, n = _workspace(OP_INDEX_TOPK, a, workspace)
     _check(load().csa_index_topk(C.byref(a), _ptr(ws), n, _stream()), "csa_index_topk")
     return ws
+
+
+def index_topk_noalloc(*args, **kw):
+    """csa_index_topk_noalloc: the same selection through the library's
+    per-GPU scratch array (no workspace, no allocation)."""
+    a = index_args(*args, **kw)
+    _check(load().csa_index_topk_noalloc(C.byref(a), _stream()), "csa_index_topk_noalloc")
 
 
 # ---------------------------------------------------------------- attention

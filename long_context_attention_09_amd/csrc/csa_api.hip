@@ -283,6 +283,8 @@ CSA_EXPORT const char* csa_strerror(int status) {
     case CSA_EUNSUPPORTED: return "unsupported shape or format combination";
     case CSA_EHIP: return "HIP runtime reported a launch error";
     case CSA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case CSA_ESCRATCH:
+      return "problem too large for the allocation-free entry point's scratch (CSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,76 @@
+"""csa_index_topk_noalloc (the allocation-free index + top-k entry point)
+against csa_index_topk with a caller workspace: identical selections, on
+consecutive calls through the same per-GPU scratch, the second smaller than
+the first, and a clear error for a problem larger than the scratch."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = synth.PRO_CSA_PREFILL.replace(name="noalloc")
+
+
+def _K():
+    import long_context_attention_09_amd._lib as K
+    K.load()
+    return K
+
+
+def _inputs(B, n_q, L, tag):
+    s = SHAPE
+    n_cap = L // s.m + 64
+    dev = "cuda"
+    kc, ks = synth.mxfp4_codes(s, f"keys/{tag}", B * n_cap, s.d_I, device=dev)
+    qc, qs = synth.mxfp4_codes(s, f"q/{tag}", B * n_q * s.H_I, s.d_I, device=dev)
+    w = synth.head_weights(s.replace(name=f"noalloc/{tag}"), (B, n_q, s.H_I), device=dev)
+    q_pos = (L + torch.arange(n_q, dtype=torch.int64, device=dev)).expand(B, n_q).contiguous()
+    return dict(q0=qc.reshape(B, n_q, s.H_I, -1), q1=qs.reshape(B, n_q, s.H_I, -1), w=w,
+                k0=kc.reshape(B, n_cap, -1), k1=ks.reshape(B, n_cap, -1), q_pos=q_pos)
+
+
+def _both(K, inp, top_k):
+    B, n_q = inp["w"].shape[:2]
+    ref = torch.full((B, n_q, top_k), -7, dtype=torch.int32, device="cuda")
+    got = torch.full_like(ref, -9)
+    args = (inp["q0"], inp["w"], inp["k0"], inp["q_pos"])
+    kw = dict(m=SHAPE.m, top_k=top_k, q1=inp["q1"], k1=inp["k1"], fmt=K.FMT_MXFP4)
+    K.index_topk(*args, out_idx=ref, **kw)
+    K.index_topk_noalloc(*args, out_idx=got, **kw)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def test_noalloc_matches_workspace_entry_point():
+    K = _K()
+    # first call: several query blocks through the scratch (the list and
+    # threshold passes); second, smaller: one query per sequence (the exact
+    # scorer and the select pass) over the contents the first left behind
+    for B, n_q, L, top_k in ((1, 300, 1 << 18, 1024), (2, 1, 1 << 16, 512)):
+        print(f"[gpu] noalloc B={B} n_q={n_q} L={L} top_k={top_k}", flush=True)
+        inp = _inputs(B, n_q, L, f"{B}/{n_q}/{L}")
+        a = K.index_args(inp["q0"], inp["w"], inp["k0"], inp["q_pos"], m=SHAPE.m, top_k=top_k,
+                         out_idx=torch.empty(B, n_q, top_k, dtype=torch.int32, device="cuda"),
+                         q1=inp["q1"], k1=inp["k1"], fmt=K.FMT_MXFP4)
+        ref, got = _both(K, inp, top_k)
+        assert torch.equal(ref, got), (B, n_q, L)
+        assert int((ref >= 0).sum(-1).min()) == top_k
+        del a
+
+
+def test_noalloc_decode_batch_and_limit():
+    K = _K()
+    print("[gpu] noalloc decode B=4 L=2^20", flush=True)
+    inp = _inputs(4, 1, 1 << 20, "decode")
+    ref, got = _both(K, inp, 1024)
+    assert torch.equal(ref, got)
+    # a batch whose single query does not fit the scratch is refused before any launch
+    big = _inputs(40, 1, 1 << 20, "big")
+    out = torch.empty(40, 1, 1024, dtype=torch.int32, device="cuda")
+    with pytest.raises(K.CsaError) as e:
+        K.index_topk_noalloc(big["q0"], big["w"], big["k0"], big["q_pos"], m=SHAPE.m, top_k=1024, out_idx=out,
+                             q1=big["q1"], k1=big["k1"], fmt=K.FMT_MXFP4)
+    assert e.value.status == K.CSA_ESCRATCH
