@@ -154,6 +154,44 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
+def copy_bandwidth():
+    """Measured device bandwidth of a plain elementwise copy (1 GiB read +
+    1 GiB written, best of five), the practical ceiling next to the
+    published 8 TB/s."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None or ms < best else best
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
+def time_steps(ev, st, steps, warmup, fn):
+    """Average ms of fn(k) over `steps` calls after `warmup`, HIP events on st."""
+    import torch
+    record = ev.h.hipEventRecord
+    for k in range(warmup):
+        fn(k)
+    marks = [(ev.create(), ev.create()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        record(C.c_void_p(marks[k][0]), st)
+        fn(warmup + k)
+        record(C.c_void_p(marks[k][1]), st)
+    torch.cuda.synchronize()
+    return sum(ev.elapsed_ms(a, b) for a, b in marks) / steps
+
+
 def cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, budget_s=15.0):
     """The fp64 oracle on this host's cores, on a bounded sample of the same
     workload: whole decode steps of single sequences (CSA and HCA alternately)
@@ -231,6 +269,29 @@ def prefill_oracle(shapes, inps, rows_per_layer):
     per["sample"] = (f"the chunk's stores plus {rows_per_layer} query rows per layer, fp64 NumPy oracle; "
                      "chunk time extrapolated as t_stores + 8192 t_row; rate over the CSA+HCA pair")
     return per
+
+
+def flash_leg(ev, st, steps):
+    """Flash-shaped CSA decode (B=16, 131072 tokens of context, 64 heads,
+    top-k 512): the step time, tokens/s and its fraction of the HBM roofline
+    (algorithmic bytes of the index and attention per step over 8 TB/s)."""
+    import torch
+    import synth
+    from long_context_attention_09_amd.layer import LayerStep
+    shape = synth.FLASH_CSA_DECODE
+    print("[bench] flash csa 128k: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.quant_decode_inputs(shape, device="cuda", copies=COPIES)
+    step = LayerStep(shape, inp, copies=COPIES)
+    torch.cuda.synchronize()
+    t = time_steps(ev, st, steps, 3, lambda k: step.run(k % COPIES, stream=st))
+    byts = algorithmic_bytes(shape, "index") + algorithmic_bytes(shape, "attend")
+    out = {"workload": "Flash-shaped CSA decode: B=16, context 131072 (32768 entries), H=64, top-k 512, "
+                       "indexer 64x128 MXFP4, window 128, sink",
+           "ms_per_step": round(t, 4), "tokens_per_s": round(shape.B / (t * 1e-3), 1),
+           "algorithmic_bytes": byts, "hbm_frac": round(byts / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del step, inp
+    torch.cuda.empty_cache()
+    return out
 
 
 def prefill_leg(ev, st, steps, warmup, oracle_rows):
@@ -317,6 +378,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--flash-steps", type=int, default=20,
+                    help="timed steps of the Flash-shaped CSA decode at 128K (0: none)")
     ap.add_argument("--prefill-steps", type=int, default=3,
                     help="timed prefill chunks (0: no prefill measurement)")
     ap.add_argument("--prefill-oracle-rows", type=int, default=16,
@@ -419,12 +482,46 @@ def main():
         },
         "roofline": roofline,
     }
+    # the same decode step with the newest entries' compression amortised over
+    # the m (CSA) and m' (HCA) tokens a block takes to complete: steps that
+    # only store the window row, plus 1/m of the entry compression
+    print("[bench] amortised compression", file=sys.stderr, flush=True)
+    t_csa_w = time_steps(ev, st, args.steps, 2, lambda k: csa.run(k % COPIES, stream=st, entries=False))
+    t_hca_w = time_steps(ev, st, args.steps, 2, lambda k: hca.run(k % COPIES, stream=st, entries=False))
+    a_csa = t_csa_w + (t_csa - t_csa_w) / csa_shape.m
+    a_hca = t_hca_w + (t_hca - t_hca_w) / hca_shape.m
+    line["config"]["amortised_compress"] = {
+        "csa_ms_per_step": round(a_csa, 4), "hca_ms_per_step": round(a_hca, 4),
+        "tokens_per_s": round(1.0 / (a_csa / csa_shape.B + a_hca / hca_shape.B) * 1e3, 1),
+        "window_only_ms": {"csa": round(t_csa_w, 4), "hca": round(t_hca_w, 4)},
+        "note": "value above compresses the newest entries on every step (the pessimistic form); here "
+                "1/m of that work per token (m = 4 CSA, 128 HCA)"}
+    # batch-invariant mode (fixed attention splits, exact indexer form): cost
+    print("[bench] batch-invariant mode", file=sys.stderr, flush=True)
+    csa_i = LayerStep(csa_shape, csa_inp, copies=COPIES, batch_invariant=True)
+    hca_i = LayerStep(hca_shape, hca_inp, copies=COPIES, batch_invariant=True)
+    t_csa_i = time_steps(ev, st, args.steps, 2, lambda k: csa_i.run(k % COPIES, stream=st))
+    t_hca_i = time_steps(ev, st, args.steps, 2, lambda k: hca_i.run(k % COPIES, stream=st))
+    v_inv = 1.0 / (t_csa_i / csa_shape.B + t_hca_i / hca_shape.B) * 1e3
+    line["config"]["batch_invariant"] = {
+        "csa_ms_per_step": round(t_csa_i, 4), "hca_ms_per_step": round(t_hca_i, 4),
+        "tokens_per_s": round(v_inv, 1), "vs_default": round(v_inv / value, 4)}
+    del csa_i, hca_i
+    # copy bandwidth measured on this GPU: the roofline against it as well
+    bw = copy_bandwidth()
+    roofline["measured_copy_GBps"] = round(bw, 1)
+    roofline["frac_vs_copy"] = round(dom["GB/s"] / bw, 4)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(csa_shape, hca_shape, csa_inp, hca_inp, args.cpu_budget)
-    if args.prefill_steps > 0:
+    if args.flash_steps > 0:
         del csa, hca, csa_inp, hca_inp
         torch.cuda.empty_cache()
+        line["config"]["flash_csa_decode_128k"] = flash_leg(ev, st, args.flash_steps)
+    if args.prefill_steps > 0:
+        if args.flash_steps <= 0:
+            del csa, hca, csa_inp, hca_inp
+            torch.cuda.empty_cache()
         line["config"]["prefill"] = prefill_leg(ev, st, args.prefill_steps, 1,
                                                 0 if args.no_cpu_baseline else args.prefill_oracle_rows)
     print(json.dumps(line), flush=True)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 enum {
   CSA_OK = 0,
@@ -82,7 +82,25 @@ enum { CSA_OP_COMPRESS = 0, CSA_OP_INDEX_TOPK = 1, CSA_OP_ATTEND = 2, CSA_OP_HCA
 /* Attention flags. */
 enum {
   CSA_ATTEND_NORM_Q = 1,      /* RMS-normalise every query head first (weight 1, eps 1e-6) */
-  CSA_ATTEND_NO_INV_ROPE = 2  /* skip the inverse output rotation (test hook) */
+  CSA_ATTEND_NO_INV_ROPE = 2, /* skip the inverse output rotation (test hook) */
+  /* Batch-invariant mode ["DeepSeek-V4 深读", 系统基础设施, batch invariance:
+   * a token's result must not depend on its position in, or the size of,
+   * the batch].  The key/value list of every query is split into pieces of a
+   * fixed length (CSA_INVARIANT_SPLIT_ROWS rows), whatever B and n_q are, so
+   * a query's output and LSE are bitwise the same alone, inside any batch and
+   * as one row of a prefill chunk.  Without it the split count follows B and
+   * n_q (to fill the GPU), which changes the order of the fp32 sums. */
+  CSA_ATTEND_BATCH_INVARIANT = 4
+};
+#define CSA_INVARIANT_SPLIT_ROWS 1024
+
+/* Index flags. */
+enum {
+  /* Batch-invariant mode: every call scores with the exact per-head form
+   * (see csa_index_topk), whatever n_q is, so a query's scores and selection
+   * are bitwise the same in a decode call, inside any batch and as one row
+   * of a prefill chunk.  Costs speed at prefill. */
+  CSA_INDEX_BATCH_INVARIANT = 1
 };
 
 /*
@@ -176,7 +194,8 @@ typedef struct CsaCompressArgs {
  * u = sum_h (w_h/2) q_h (per 32-dim block, each component carries 4 more
  * bits): such scores (out_score included) differ from the exact ones by at
  * most about 2^-24 sum_blocks max|u| sum|k|, the order of fp32 rounding.
- * One query per call (decode) uses the exact form.
+ * One query per call (decode), and every call with CSA_INDEX_BATCH_INVARIANT,
+ * uses the exact form.
  *
  *   fmt F32:   q0 = fp32 [B][n_q][H_I][d_I]; k0 = fp32 [B][n_cap][d_I].
  *   fmt MXFP4: q0 = codes [B][n_q][H_I][d_I/2], q1 = scales [B][n_q][H_I][d_I/32];
@@ -212,6 +231,8 @@ typedef struct CsaIndexArgs {
   int32_t d_I;
   int32_t fmt;
   int32_t top_k;
+  int32_t flags;     /* CSA_INDEX_* */
+  int32_t _pad0;
   const int64_t* q_pos;
   const int32_t* n_entries;
   const void* q0;

@@ -21,8 +21,10 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 FMT_F32, FMT_FP8_BF16, FMT_MXFP4 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 OP_COMPRESS, OP_INDEX_TOPK, OP_ATTEND, OP_HCA_ATTEND = 0, 1, 2, 3
-ATTEND_NORM_Q, ATTEND_NO_INV_ROPE = 1, 2
-ABI_VERSION = 1
+ATTEND_NORM_Q, ATTEND_NO_INV_ROPE, ATTEND_BATCH_INVARIANT = 1, 2, 4
+INDEX_BATCH_INVARIANT = 1
+INVARIANT_SPLIT_ROWS = 1024
+ABI_VERSION = 2
 
 _vp = C.c_void_p
 
@@ -42,7 +44,7 @@ class CompressArgs(C.Structure):
 class IndexArgs(C.Structure):
     _fields_ = [("B", C.c_int32), ("n_q", C.c_int32), ("m", C.c_int32), ("n_cap", C.c_int32),
                 ("H_I", C.c_int32), ("d_I", C.c_int32), ("fmt", C.c_int32), ("top_k", C.c_int32),
-                ("q_pos", _vp), ("n_entries", _vp), ("q0", _vp), ("q1", _vp), ("w", _vp),
+                ("flags", C.c_int32), ("_pad0", C.c_int32), ("q_pos", _vp), ("n_entries", _vp), ("q0", _vp), ("q1", _vp), ("w", _vp),
                 ("k0", _vp), ("k1", _vp), ("out_idx", _vp), ("out_score", _vp),
                 ("ev_start", _vp), ("ev_stop", _vp)]
 
@@ -220,7 +222,7 @@ def compress_workspace_bytes(jobs):
 
 
 def index_args(q0, w, k0, q_pos, *, m, top_k, out_idx, q1=None, k1=None, n_entries=None,
-               out_score=None, fmt=FMT_MXFP4):
+               out_score=None, fmt=FMT_MXFP4, flags=0):
     """Fill IndexArgs.  MXFP4: q0 [B, n_q, H_I, d_I/2] u8, q1 [B, n_q, H_I, d_I/32] u8,
     k0 [B, n_cap, d_I/2] u8, k1 [B, n_cap, d_I/32] u8.  F32: q0 [B, n_q, H_I, d_I],
     k0 [B, n_cap, d_I].  w [B, n_q, H_I] fp32, q_pos [B, n_q] int64, out_idx
@@ -239,7 +241,7 @@ def index_args(q0, w, k0, q_pos, *, m, top_k, out_idx, q1=None, k1=None, n_entri
     if out_score is not None and tuple(out_score.shape) != (B, n_q, n_cap):
         raise ValueError("out_score must be [B, n_q, n_cap]")
     return IndexArgs(B=B, n_q=n_q, m=m, n_cap=n_cap, H_I=H_I, d_I=d_I, fmt=fmt, top_k=top_k,
-                     q_pos=_ptr(q_pos), n_entries=_ptr(n_entries), q0=_ptr(q0), q1=_ptr(q1),
+                     flags=flags, _pad0=0, q_pos=_ptr(q_pos), n_entries=_ptr(n_entries), q0=_ptr(q0), q1=_ptr(q1),
                      w=_ptr(w), k0=_ptr(k0), k1=_ptr(k1), out_idx=_ptr(out_idx),
                      out_score=_ptr(out_score))
 

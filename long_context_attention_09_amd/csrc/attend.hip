@@ -72,6 +72,18 @@ __device__ __forceinline__ ListInfo list_info(const AttendLaunch& a, int b, int 
   return L;
 }
 
+// Splits of a query's list.  Normally the launch's split count (chosen to fill
+// the GPU); in the batch-invariant mode a count fixed by the query's own list
+// length (pieces of CSA_INVARIANT_SPLIT_ROWS rows), so the order of every sum
+// depends on nothing but the query.
+__device__ __forceinline__ int query_splits(const AttendLaunch& a, const ListInfo& L) {
+  if (!(a.flags & CSA_ATTEND_BATCH_INVARIANT)) return a.n_splits;
+  const int tiles = (L.n_comp + L.n_w + kTile - 1) / kTile;
+  constexpr int per = CSA_INVARIANT_SPLIT_ROWS / kTile;
+  const int n = (tiles + per - 1) / per;
+  return n < 1 ? 1 : n;
+}
+
 // Resolve list position p to (nope row pointer, rope row pointer); false when masked.
 __device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, const ListInfo& L, int p,
                                          const uint8_t** pn, const uint8_t** pr) {
@@ -225,7 +237,13 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   const int split = blockIdx.x, hg = blockIdx.y;
   const int br = blockIdx.z;
   const int b = br / a.n_q, r = br % a.n_q;
-  const int n_sp = a.n_splits;
+  // (batch-invariant mode: the split count follows the query's list, so the
+  // layout comes first; otherwise its loads overlap the first index reads)
+  const bool inv = (a.flags & CSA_ATTEND_BATCH_INVARIANT) != 0;
+  ListInfo L{};
+  if (inv) L = list_info(a, b, r);
+  const int n_sp = inv ? query_splits(a, L) : a.n_splits;
+  if (split >= n_sp) return;                 // (invariant mode: a shorter list than the launch's longest)
   // Splits take the list's 32-entry tiles round-robin: local tile t of this
   // split is tile t n_sp + split of the list, so the workgroups of a query
   // stream one contiguous front of the cache (HBM serves that faster than
@@ -259,7 +277,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
     const int pos = ATTEND_POS(u);
     sel0[u] = a.idx ? idx_row[pos < a.top_k ? pos : 0] : ((const int*)a.q)[r32];
   }
-  const ListInfo L = list_info(a, b, r);
+  if (!inv) L = list_info(a, b, r);
   const int list_len = L.n_comp + L.n_w;
   const int list_tiles = (list_len + kTile - 1) / kTile;
   const int n_tiles = list_tiles > split ? (list_tiles - split + n_sp - 1) / n_sp : 0;
@@ -569,7 +587,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   __syncthreads();
   const int64_t unit = (int64_t)br * gridDim.y + hg;
   const bool inv_rope = !(a.flags & CSA_ATTEND_NO_INV_ROPE);
-  const bool single = a.n_splits == 1;
+  const bool single = n_sp == 1;
   // The normalised output (BF16 with the sink and inverse RoPE when the split
   // covers the whole list, else the fp16 partial) is staged in LDS as
   // [64 heads][512 dims] rows, so the global stores are contiguous 16-byte chunks.
@@ -669,6 +687,10 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
   const int d0 = (threadIdx.x & 63) * 8;
   const int head = hg * 64 + hl;
   const int64_t t = a.q_pos[(int64_t)b * a.n_q + r];
+  // splits this query's partials came from (the attention kernel finalised a
+  // query with a single split itself)
+  const int n_sp = (a.flags & CSA_ATTEND_BATCH_INVARIANT) ? query_splits(a, list_info(a, b, r)) : a.n_splits;
+  if (n_sp == 1) return;
   if (threadIdx.x < 32) {
     float cs, sn;
     rope_cos_sin(-(double)t, threadIdx.x, kDR, a.log_theta, &cs, &sn);
@@ -687,12 +709,12 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
   float M = z2, den = 1.0f;                 // den = exp2(z2 - M) + sum l_s exp2(m_s - M)
   float Mx = -INFINITY, lsum = 0.f;         // lsum = sum l_s exp2(m_s - Mx)
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.n_splits; s0 += kGroup) {
+  for (int s0 = 0; s0 < n_sp; s0 += kGroup) {
     float ms[kGroup], ls[kGroup];
     f16x8 v[kGroup];
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      const int sj = s0 + j < a.n_splits ? s0 + j : s0;
+      const int sj = s0 + j < n_sp ? s0 + j : s0;
       const int64_t rj = base + (int64_t)sj * 64;
       ms[j] = a.part_ml[rj * 2];
       ls[j] = a.part_ml[rj * 2 + 1];
@@ -701,7 +723,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttendLaunch a, int n_hg) 
     float cm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) {
-      if (s0 + j >= a.n_splits) ms[j] = -INFINITY;
+      if (s0 + j >= n_sp) ms[j] = -INFINITY;
       cm = fmaxf(cm, ms[j]);
     }
     if (cm == -INFINITY) continue;          // no split of the group saw a row

@@ -78,6 +78,7 @@ int check_index(const CsaIndexArgs* a) {
   if (a->B < 1 || a->n_q < 1 || a->m < 1 || a->n_cap < 1 || a->H_I < 1 || a->d_I < 1 || a->top_k < 1)
     return CSA_EINVAL;
   if (a->n_cap > kMaxIndexCap) return CSA_EUNSUPPORTED;
+  if (a->flags & ~CSA_INDEX_BATCH_INVARIANT) return CSA_EINVAL;
   if (!a->q_pos || !a->q0 || !a->w || !a->k0 || !a->out_idx) return CSA_EINVAL;
   if (!aligned(a->q_pos, 8) || !aligned(a->w, 4) || !aligned(a->out_idx, 4)) return CSA_EINVAL;
   if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
@@ -213,6 +214,20 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   // Splits take the list's 32-entry tiles round-robin (split s: tiles s,
   // s + n_splits, ...).
   const int64_t tiles = (list + 31) / 32;
+  if (a->flags & CSA_ATTEND_BATCH_INVARIANT) {
+    // a split count fixed by the list length alone: every query of any batch
+    // sums its rows in the same order
+    const int64_t per_inv = CSA_INVARIANT_SPLIT_ROWS / 32;
+    p.n_splits = (int)((tiles + per_inv - 1) / per_inv);
+    p.split_len = CSA_INVARIANT_SPLIT_ROWS;
+    if (p.n_splits > 1) {
+      const size_t rows = (size_t)units * p.n_splits * 64;
+      p.off_o = 0;
+      p.off_ml = align_up(rows * 512 * 2);
+      p.total = p.off_ml + align_up(rows * 2 * 4);
+    }
+    return p;
+  }
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
   int64_t s_max = (tiles + 2) / 3;                // at least three tiles per split
   if (s > s_max) s = s_max;
@@ -444,7 +459,7 @@ int run_index(const CsaIndexArgs* a, const IndexPlan& p, char* ws, void* stream)
   for (int q0 = 0; q0 < a->n_q; q0 += p.n_qb) {
     csa::IndexLaunch L{};
     L.B = a->B; L.n_q = a->n_q; L.m = a->m; L.n_cap = a->n_cap; L.H_I = a->H_I; L.d_I = a->d_I;
-    L.fmt = a->fmt; L.top_k = a->top_k; L.n_chunks = p.n_chunks;
+    L.fmt = a->fmt; L.top_k = a->top_k; L.n_chunks = p.n_chunks; L.flags = a->flags;
     L.q_first = q0;
     L.n_qb = a->n_q - q0 < p.n_qb ? a->n_q - q0 : p.n_qb;
     L.q_pos = a->q_pos; L.n_entries = a->n_entries;

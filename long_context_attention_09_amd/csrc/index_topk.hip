@@ -1221,7 +1221,7 @@ __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
 
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   const int nq = a.B * a.n_qb;
-  if (a.fmt == CSA_FMT_MXFP4 && a.n_qb >= kMqQT && a.H_I % 32 == 0) {
+  if (a.fmt == CSA_FMT_MXFP4 && a.n_qb >= kMqQT && a.H_I % 32 == 0 && !(a.flags & CSA_INDEX_BATCH_INVARIANT)) {
     index_linear_kernel<<<dim3(a.n_qb, a.B), 128, 0, s>>>(a);
     const int per_wg = 4 * kMqTiles * 32;
     dim3 grid((a.n_cap + per_wg - 1) / per_wg, (a.n_qb + kMqQT - 1) / kMqQT, a.B);

@@ -41,6 +41,7 @@ struct TopkState {
 
 struct IndexLaunch {
   int32_t B, n_q, m, n_cap, H_I, d_I, fmt, top_k;
+  int32_t flags;             // CSA_INDEX_*
   int32_t n_chunks;          // 4096-score chunks per query
   int32_t q_first;           // first query of this query block
   int32_t n_qb;              // queries in this block

@@ -34,8 +34,11 @@ class LayerStep:
     seeded generator lays them out (decode: quant_decode_inputs, prefill:
     quant_prefill_inputs)."""
 
-    def __init__(self, shape, inp, prefill: bool = False, copies: int = 1):
+    def __init__(self, shape, inp, prefill: bool = False, copies: int = 1, batch_invariant: bool = False):
         self.s = shape
+        # batch-invariant mode: fixed attention splits and the exact indexer form
+        self.attend_flags = K.ATTEND_NORM_Q | (K.ATTEND_BATCH_INVARIANT if batch_invariant else 0)
+        self.index_flags = K.INDEX_BATCH_INVARIANT if batch_invariant else 0
         self.inp = inp
         self.prefill = prefill
         s = shape
@@ -142,24 +145,31 @@ class LayerStep:
                 kc, ks = self.keys[c]
                 p["index"] = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
                                           top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
-                                          fmt=K.FMT_MXFP4)
+                                          fmt=K.FMT_MXFP4, flags=self.index_flags)
             nope, rope = K.split_main(self.caches[c])
             wn, wr = K.split_main(self.win)
             p["attend"] = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0,
                                         self.inp["sink"], self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
                                         idx=self.idx if s.csa else None, out_lse=self.lse, d_rope=s.d_r,
-                                        rope_theta=s.theta, fmt=K.FMT_FP8_BF16)
+                                        rope_theta=s.theta, fmt=K.FMT_FP8_BF16, flags=self.attend_flags)
             self._prep[c] = p
         return p
 
-    def compress_all(self, c=0, stream=None):
+    def compress_all(self, c=0, stream=None, entries=True):
         """Every store of the step in one batched call: the newest entry (and,
         for CSA, the newest indexer key) and the raw window rows; long blocks
-        are pooled over many workgroups through the step's workspace."""
+        are pooled over many workgroups through the step's workspace.  With
+        entries=False only the window row is stored (a decode step whose
+        position completes no block: m - 1 of every m steps)."""
         p = self._prepared(c)
         st = K._stream() if stream is None else stream
-        K._check(self._fn_compress(p["jobs"], p["n_jobs"], self._ws_c[0], self._ws_c[1], st),
-                 "csa_compress_batch_ws")
+        if entries:
+            jobs, n = p["jobs"], p["n_jobs"]
+        else:
+            if "win_only" not in p:
+                p["win_only"] = (K.CompressArgs * 1)(self._window_job())
+            jobs, n = p["win_only"], 1
+        K._check(self._fn_compress(jobs, n, self._ws_c[0], self._ws_c[1], st), "csa_compress_batch_ws")
 
     def index(self, c=0, events=(None, None), stream=None):
         """csa_index_topk; `events` = optional HIP event handles recorded around
@@ -185,7 +195,7 @@ class LayerStep:
             kc, ks = self.keys[0]
             a = K.index_args(self.inp["q_idx_codes"], self.inp["w"], kc, self.inp["q_pos"], m=s.m,
                              top_k=s.top_k, out_idx=self.idx, q1=self.inp["q_idx_scales"], k1=ks,
-                             fmt=K.FMT_MXFP4)
+                             fmt=K.FMT_MXFP4, flags=self.index_flags)
             n = K.workspace_bytes(K.OP_INDEX_TOPK, a)
             self.ws_index = (torch.zeros(max(n, 256), dtype=torch.uint8, device=dev), n)
         nope, rope = K.split_main(self.caches[0])
@@ -193,7 +203,7 @@ class LayerStep:
         a = K.attend_args(self.inp["q"], self.inp["q_pos"], nope, wn, self.win_pos0, self.inp["sink"],
                           self.out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
                           idx=self.idx if s.csa else None, d_rope=s.d_r, rope_theta=s.theta,
-                          fmt=K.FMT_FP8_BF16)
+                          fmt=K.FMT_FP8_BF16, flags=self.attend_flags)
         n = K.workspace_bytes(K.OP_ATTEND if s.csa else K.OP_HCA_ATTEND, a)
         self.ws_attend = (torch.zeros(max(n, 256), dtype=torch.uint8, device=dev) if n else None, n)
         # the library entry points and workspace (pointer, bytes) pairs, bound once
@@ -207,14 +217,15 @@ class LayerStep:
 
     # ------------------------------------------------------------ whole step
 
-    def run(self, c=0, events=None, stream=None):
+    def run(self, c=0, events=None, stream=None, entries=True):
         """One full step on the current stream (or `stream`, a HIP stream
         handle), no synchronisation.  `events` optionally maps 'index' /
         'attend' to (start, stop) HIP event handles recorded around the scoring
-        and attention kernels."""
+        and attention kernels.  entries=False: a step that completes no block
+        (only the window row is stored)."""
         ev = events or {}
         st = K._stream() if stream is None else stream
-        self.compress_all(c, stream=st)
+        self.compress_all(c, stream=st, entries=entries)
         if self.s.csa:
             self.index(c, events=ev.get("index", (None, None)), stream=st)
         self.attend(c, events=ev.get("attend", (None, None)), stream=st)

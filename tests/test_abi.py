@@ -192,3 +192,28 @@ def test_compress_workspace_rules(K):
     assert lib.csa_compress_batch_ws(arr, 1, None, 0, None) == K.CSA_EWORKSPACE
     assert lib.csa_compress_batch_ws(arr, 1, C.c_void_p(1 << 20), 16, None) == K.CSA_EWORKSPACE
     assert lib.csa_compress_batch_ws(arr, 1, C.c_void_p((1 << 20) + 8), 1 << 20, None) == K.CSA_EWORKSPACE
+
+
+def test_batch_invariant_flags(K):
+    """Batch-invariant mode: the attention's split count (hence its workspace
+    per query) is fixed by the list length alone, not by B; unknown index
+    flags are refused."""
+    lib = K.load()
+
+    def ws(op, **kw):
+        a = _attend_args(K, **kw)
+        return lib.csa_workspace_bytes(op, C.cast(C.pointer(a), C.c_void_p))
+
+    inv = K.ATTEND_NORM_Q | K.ATTEND_BATCH_INVARIANT
+    one, many = ws(K.OP_HCA_ATTEND, B=1, flags=inv), ws(K.OP_HCA_ATTEND, B=32, flags=inv)
+    # 8192 + 128 rows in pieces of 1024: 9 splits of fp16 partials per query and head group
+    splits = -(-(8192 + 128) // K.INVARIANT_SPLIT_ROWS)
+    assert one >= splits * 64 * 512 * 2 and many >= 32 * splits * 64 * 512 * 2
+    assert many <= 32 * one
+    # the default mode fills the GPU instead: one sequence gets more splits than in a batch of 32
+    assert ws(K.OP_HCA_ATTEND, B=1) * 32 > ws(K.OP_HCA_ATTEND, B=32)
+    a = _index_args(K, flags=K.INDEX_BATCH_INVARIANT)
+    n = lib.csa_workspace_bytes(K.OP_INDEX_TOPK, C.cast(C.pointer(a), C.c_void_p))
+    assert 0 < n < (1 << 40)
+    bad = _index_args(K, flags=2)
+    assert lib.csa_index_topk(C.byref(bad), FAKE, n, None) == K.CSA_EINVAL
