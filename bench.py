@@ -271,6 +271,50 @@ def prefill_oracle(shapes, inps, rows_per_layer):
     return per
 
 
+def bf16_scores_leg(ev, st, step, shape, steps):
+    """The CSA index op with fp32 and with BF16 scores over the same caches:
+    selector time (the op minus its scoring kernel, HIP events on the bench
+    stream) and the fraction of the fp32 selection the BF16 one keeps."""
+    import torch
+    from long_context_attention_09_amd import _lib as K
+    res = {}
+    sel = {}
+    for name, flags in (("fp32", 0), ("bf16", K.INDEX_BF16_SCORES)):
+        kc, ks = step.keys[0]
+        idx = torch.empty_like(step.idx)
+        a = K.index_args(step.inp["q_idx_codes"], step.inp["w"], kc, step.inp["q_pos"], m=shape.m,
+                         top_k=shape.top_k, out_idx=idx, q1=step.inp["q_idx_scales"], k1=ks, fmt=K.FMT_MXFP4,
+                         flags=flags)
+        n = K.workspace_bytes(K.OP_INDEX_TOPK, a)
+        ws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
+        lib = K.load()
+        e_sc = [(ev.create(), ev.create()) for _ in range(steps + 2)]
+        e_op = [(ev.create(), ev.create()) for _ in range(steps + 2)]
+        torch.cuda.synchronize()
+        for k in range(steps + 2):
+            a.ev_start, a.ev_stop = e_sc[k]
+            ev.h.hipEventRecord(C.c_void_p(e_op[k][0]), st)
+            K._check(lib.csa_index_topk(C.byref(a), K._ptr(ws), ws.numel(), st), "csa_index_topk")
+            ev.h.hipEventRecord(C.c_void_p(e_op[k][1]), st)
+        torch.cuda.synchronize()
+        t_op = sum(ev.elapsed_ms(*e_op[k]) for k in range(2, steps + 2)) / steps
+        t_sc = sum(ev.elapsed_ms(*e_sc[k]) for k in range(2, steps + 2)) / steps
+        res[name] = {"op_us": round(t_op * 1e3, 2), "scoring_us": round(t_sc * 1e3, 2),
+                     "selector_us": round((t_op - t_sc) * 1e3, 2)}
+        sel[name] = idx.clone()
+        del ws
+    kept = torch.isin(sel["bf16"].view(-1, shape.top_k)[0], sel["fp32"].view(-1, shape.top_k)[0])
+    rec = []
+    for r in range(sel["fp32"].shape[0] * sel["fp32"].shape[1]):
+        a32 = sel["fp32"].view(-1, shape.top_k)[r]
+        a16 = sel["bf16"].view(-1, shape.top_k)[r]
+        rec.append(float(torch.isin(a16, a32).float().mean()))
+    res["recall_of_fp32_selection"] = {"min": round(min(rec), 5), "mean": round(sum(rec) / len(rec), 5)}
+    res["selector_speedup"] = round(res["fp32"]["selector_us"] / max(res["bf16"]["selector_us"], 1e-9), 3)
+    del kept
+    return res
+
+
 def flash_leg(ev, st, steps):
     """Flash-shaped CSA decode (B=16, 131072 tokens of context, 64 heads,
     top-k 512): the step time, tokens/s and its fraction of the HBM roofline
@@ -496,6 +540,10 @@ def main():
         "window_only_ms": {"csa": round(t_csa_w, 4), "hca": round(t_hca_w, 4)},
         "note": "value above compresses the newest entries on every step (the pessimistic form); here "
                 "1/m of that work per token (m = 4 CSA, 128 HCA)"}
+    # BF16 index scores: selector time against fp32 scores and recall of the
+    # fp32 selection, on this workload
+    print("[bench] bf16 index scores", file=sys.stderr, flush=True)
+    line["config"]["bf16_index_scores"] = bf16_scores_leg(ev, st, csa, csa_shape, args.steps)
     # batch-invariant mode (fixed attention splits, exact indexer form): cost
     print("[bench] batch-invariant mode", file=sys.stderr, flush=True)
     csa_i = LayerStep(csa_shape, csa_inp, copies=COPIES, batch_invariant=True)

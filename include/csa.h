@@ -100,7 +100,15 @@ enum {
    * (see csa_index_topk), whatever n_q is, so a query's scores and selection
    * are bitwise the same in a decode call, inside any batch and as one row
    * of a prefill chunk.  Costs speed at prefill. */
-  CSA_INDEX_BATCH_INVARIANT = 1
+  CSA_INDEX_BATCH_INVARIANT = 1,
+  /* BF16 index scores ["DeepSeek-V4 深读", FP4 QAT section: index scores
+   * kept in BF16 instead of FP32 make the top-k selector about twice as fast
+   * and keep 99.7% of the selected entries].  Every score is rounded to BF16
+   * (nearest even) before it is stored and selected on; selection then
+   * follows the same rule on the rounded scores (ties, now more frequent,
+   * go to the lower index).  out_score, when given, receives the BF16 codes
+   * (2 bytes per score, same [B][n_q][n_cap] layout). */
+  CSA_INDEX_BF16_SCORES = 2
 };
 
 /*
@@ -205,8 +213,8 @@ typedef struct CsaCompressArgs {
  *   n_entries  device int32 [B] entries present per sequence (NULL = n_cap).
  *   w          device fp32 [B][n_q][H_I] head weights (any sign).
  *   out_idx    device int32 [B][n_q][top_k].
- *   out_score  optional device fp32 [B][n_q][n_cap]: I_i for i < n_vis,
- *              -inf beyond.
+ *   out_score  optional device fp32 [B][n_q][n_cap] (BF16 codes with
+ *              CSA_INDEX_BF16_SCORES): I_i for i < n_vis, -inf beyond.
  * Constraints: MXFP4 needs d_I == 128 and H_I a multiple of 16 up to 64
  * (the matrix-core path); F32 needs d_I <= 1024; top_k >= 1; n_cap >= 1;
  * m >= 1.
@@ -241,7 +249,7 @@ typedef struct CsaIndexArgs {
   const void* k0;
   const void* k1;
   int32_t* out_idx;
-  float* out_score;
+  void* out_score;   /* fp32, or BF16 codes with CSA_INDEX_BF16_SCORES */
   void* ev_start;   /* optional hipEvent_t recorded just before the scoring kernel */
   void* ev_stop;    /* optional hipEvent_t recorded just after it (NULL = none) */
 } CsaIndexArgs;

@@ -22,7 +22,7 @@ FMT_F32, FMT_FP8_BF16, FMT_MXFP4 = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 OP_COMPRESS, OP_INDEX_TOPK, OP_ATTEND, OP_HCA_ATTEND = 0, 1, 2, 3
 ATTEND_NORM_Q, ATTEND_NO_INV_ROPE, ATTEND_BATCH_INVARIANT = 1, 2, 4
-INDEX_BATCH_INVARIANT = 1
+INDEX_BATCH_INVARIANT, INDEX_BF16_SCORES = 1, 2
 INVARIANT_SPLIT_ROWS = 1024
 ABI_VERSION = 2
 
@@ -240,6 +240,9 @@ def index_args(q0, w, k0, q_pos, *, m, top_k, out_idx, q1=None, k1=None, n_entri
         raise ValueError("out_idx must be [B, n_q, top_k] and q_pos [B, n_q]")
     if out_score is not None and tuple(out_score.shape) != (B, n_q, n_cap):
         raise ValueError("out_score must be [B, n_q, n_cap]")
+    want = torch.bfloat16 if flags & INDEX_BF16_SCORES else torch.float32
+    if out_score is not None and out_score.dtype != want:
+        raise ValueError(f"out_score must be {want} with these flags")
     return IndexArgs(B=B, n_q=n_q, m=m, n_cap=n_cap, H_I=H_I, d_I=d_I, fmt=fmt, top_k=top_k,
                      flags=flags, _pad0=0, q_pos=_ptr(q_pos), n_entries=_ptr(n_entries), q0=_ptr(q0), q1=_ptr(q1),
                      w=_ptr(w), k0=_ptr(k0), k1=_ptr(k1), out_idx=_ptr(out_idx),

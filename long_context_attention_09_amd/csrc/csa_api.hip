@@ -78,11 +78,11 @@ int check_index(const CsaIndexArgs* a) {
   if (a->B < 1 || a->n_q < 1 || a->m < 1 || a->n_cap < 1 || a->H_I < 1 || a->d_I < 1 || a->top_k < 1)
     return CSA_EINVAL;
   if (a->n_cap > kMaxIndexCap) return CSA_EUNSUPPORTED;
-  if (a->flags & ~CSA_INDEX_BATCH_INVARIANT) return CSA_EINVAL;
+  if (a->flags & ~(CSA_INDEX_BATCH_INVARIANT | CSA_INDEX_BF16_SCORES)) return CSA_EINVAL;
   if (!a->q_pos || !a->q0 || !a->w || !a->k0 || !a->out_idx) return CSA_EINVAL;
   if (!aligned(a->q_pos, 8) || !aligned(a->w, 4) || !aligned(a->out_idx, 4)) return CSA_EINVAL;
   if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
-  if (a->out_score && !aligned(a->out_score, 4)) return CSA_EINVAL;
+  if (a->out_score && !aligned(a->out_score, (a->flags & CSA_INDEX_BF16_SCORES) ? 2 : 4)) return CSA_EINVAL;
   if (a->fmt == CSA_FMT_MXFP4) {
     if (!a->q1 || !a->k1) return CSA_EINVAL;
     if (a->d_I != 128 || a->H_I % 16 || a->H_I > 64) return CSA_EUNSUPPORTED;
@@ -105,7 +105,8 @@ IndexPlan index_layout(const CsaIndexArgs* a, int n_qb) {
   const size_t nq = (size_t)a->B * n_qb;
   size_t off = 0;
   p.off_scores = off;
-  if (!a->out_score) off += align_up(nq * (size_t)a->n_cap * 4);
+  const size_t es = (a->flags & CSA_INDEX_BF16_SCORES) ? 2 : 4;   // bytes per score
+  if (!a->out_score) off += align_up(nq * (size_t)a->n_cap * es);
   p.off_hist = off;   off += align_up(nq * 4096 * 4);
   p.off_state = off;  off += align_up(nq * sizeof(csa::TopkState));
   p.off_ckey = off;   off += align_up(nq * (size_t)a->n_cap * 4);
@@ -122,7 +123,8 @@ IndexPlan index_layout(const CsaIndexArgs* a, int n_qb) {
 // workspace fits `budget` bytes; n_qb = 0 when one query does not fit.
 IndexPlan plan_index(const CsaIndexArgs* a, int64_t budget) {
   const int64_t n_chunks = (a->n_cap + kIdxChunk - 1) / kIdxChunk;
-  const int64_t per_q = (int64_t)a->B * ((a->out_score ? 0 : (int64_t)a->n_cap * 4) + (int64_t)a->n_cap * 4 +
+  const int64_t es = (a->flags & CSA_INDEX_BF16_SCORES) ? 2 : 4;
+  const int64_t per_q = (int64_t)a->B * ((a->out_score ? 0 : (int64_t)a->n_cap * es) + (int64_t)a->n_cap * 4 +
                                          4096 * 4 + (int64_t)sizeof(csa::TopkState) + 4 * n_chunks * 4 +
                                          csa::kIndexLinBytes);
   int64_t n = budget / (per_q > 0 ? per_q : 1);
@@ -464,10 +466,10 @@ int run_index(const CsaIndexArgs* a, const IndexPlan& p, char* ws, void* stream)
     L.n_qb = a->n_q - q0 < p.n_qb ? a->n_q - q0 : p.n_qb;
     L.q_pos = a->q_pos; L.n_entries = a->n_entries;
     L.q0 = a->q0; L.q1 = a->q1; L.w = a->w; L.k0 = a->k0; L.k1 = a->k1;
-    L.out_idx = a->out_idx; L.out_score = a->out_score;
+    L.out_idx = a->out_idx; L.out_score = (float*)a->out_score;
     if (a->out_score) {
       // the caller's [B][n_q][n_cap] array: block rows start at q0 within each sequence
-      L.scores = a->out_score;
+      L.scores = (float*)a->out_score;
       L.score_seq_rows = a->n_q;
       L.score_row0 = q0;
     } else {

@@ -72,8 +72,44 @@ __device__ __forceinline__ float relu(float x) {
 
 // Score row of query r of sequence b in this query block: the workspace holds
 // the block's rows [B][n_qb]; a caller's score array holds all [B][n_q] rows.
+// Scores are fp32, or BF16 codes (2 bytes) with CSA_INDEX_BF16_SCORES.
+__device__ __forceinline__ bool bf16_scores(const IndexLaunch& a) { return (a.flags & CSA_INDEX_BF16_SCORES) != 0; }
 __device__ __forceinline__ float* score_row(const IndexLaunch& a, int b, int r) {
-  return a.scores + ((int64_t)b * a.score_seq_rows + a.score_row0 + r) * a.n_cap;
+  const int64_t row = (int64_t)b * a.score_seq_rows + a.score_row0 + r;
+  return (float*)((char*)a.scores + row * a.n_cap * (bf16_scores(a) ? 2 : 4));
+}
+// score i of a row (BF16 codes widen exactly)
+__device__ __forceinline__ float load_score(const IndexLaunch& a, const float* row, int64_t i) {
+  if (bf16_scores(a)) return bf16_to_f32(((const uint16_t*)row)[i]);
+  return row[i];
+}
+__device__ __forceinline__ void store_score(const IndexLaunch& a, float* row, int64_t i, float v) {
+  if (bf16_scores(a)) ((uint16_t*)row)[i] = f32_to_bf16(v);
+  else row[i] = v;
+}
+// the value a score is stored as (BF16 rounds to nearest even)
+__device__ __forceinline__ float stored_score(const IndexLaunch& a, float v) {
+  return bf16_scores(a) ? bf16_to_f32(f32_to_bf16(v)) : v;
+}
+// scores i .. i+3 of a row (i + 3 < n_cap), one vector load when aligned
+__device__ __forceinline__ void load_score4(const IndexLaunch& a, const float* row, int64_t i, float* out) {
+  if (bf16_scores(a)) {
+    const uint16_t* r16 = (const uint16_t*)row;
+    if ((((uintptr_t)(r16 + i)) & 7) == 0) {
+      const u32x2 x = *(const u32x2*)(r16 + i);
+      out[0] = __uint_as_float(x[0] << 16); out[1] = __uint_as_float(x[0] & 0xffff0000u);
+      out[2] = __uint_as_float(x[1] << 16); out[3] = __uint_as_float(x[1] & 0xffff0000u);
+    } else {
+      for (int u = 0; u < 4; ++u) out[u] = bf16_to_f32(r16[i + u]);
+    }
+    return;
+  }
+  if ((((uintptr_t)(row + i)) & 15) == 0) {
+    const f32x4 x = *(const f32x4*)(row + i);
+    out[0] = x[0]; out[1] = x[1]; out[2] = x[2]; out[3] = x[3];
+  } else {
+    for (int u = 0; u < 4; ++u) out[u] = row[i + u];
+  }
 }
 
 __device__ __forceinline__ int query_n_vis(const IndexLaunch& a, int b, int r) {
@@ -219,7 +255,9 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     for (int qi = 0; qi < QT; ++qi) {
       const bool live = r0 + qi < a.n_qb;
       float* srow = score_row(a, b, live ? r0 + qi : r0);
-      rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? (int)((uint32_t)a.n_cap * 4u) : 0, kBufferWord3);
+      rsc[qi] = __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0,
+                                                  live ? (int)((uint32_t)a.n_cap * (bf16_scores(a) ? 2u : 4u)) : 0,
+                                                  kBufferWord3);
     }
     const uint32_t gs_c = (uint32_t)NW * 4096u, gs_s = (uint32_t)NW * 256u;   // group strides: codes, words
     const uint32_t off_c = (uint32_t)W * 4096u + (uint32_t)col * 64u + (uint32_t)g * 16u;
@@ -294,8 +332,13 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
             const int key = (W + (int)j * NW) * 64 + lane;
             const bool vis = key < nvis[qi];
             const float sc = vis ? tot : -INFINITY;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + j * gs_s, 0, 0);
-            if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
+            if (bf16_scores(a)) {
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(sc), rsc[qi], (off_o + j * gs_s) >> 1, 0, 0);
+              if (vis) atomicAdd(&lhist[qi][order_key(bf16_to_f32(f32_to_bf16(sc))) >> kShift1], 1u);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc[qi], off_o + j * gs_s, 0, 0);
+              if (vis) atomicAdd(&lhist[qi][order_key(sc) >> kShift1], 1u);
+            }
           }
         }
         fetch(t + kRing, u);
@@ -304,8 +347,12 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // groups of this wave that the rounds did not reach get -inf
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi)
-      for (uint32_t j = (uint32_t)(n_rounds * kRing / 4); j < (uint32_t)kGroups; ++j)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], off_o + j * gs_s, 0, 0);
+      for (uint32_t j = (uint32_t)(n_rounds * kRing / 4); j < (uint32_t)kGroups; ++j) {
+        if (bf16_scores(a))
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0xff80u, rsc[qi], (off_o + j * gs_s) >> 1, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], off_o + j * gs_s, 0, 0);
+      }
   } else {
     // no query sees any key of this wave
     for (int qi = 0; qi < QT; ++qi) {
@@ -313,7 +360,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
       float* row = score_row(a, b, r0 + qi);
       for (int j = 0; j < kGroups; ++j) {
         const int64_t k = (int64_t)(W + j * NW) * 64 + lane;
-        if (k < a.n_cap) row[k] = -INFINITY;
+        if (k < a.n_cap) store_score(a, row, k, -INFINITY);
       }
     }
   }
@@ -435,13 +482,18 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   // the live queries are outside it, so their stores are dropped
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)score_row(a, b, r0), 0,
-      (int)((uint32_t)live_q * (uint32_t)a.n_cap * 4u), kBufferWord3);
+      (int)((uint32_t)live_q * (uint32_t)a.n_cap * (bf16_scores(a) ? 2u : 4u)), kBufferWord3);
   const int my_nvis = h ? nvis[1] : nvis[0];
   // byte offset of this lane's score for key `key`; keys past the row map
   // outside the resource (their stores are dropped instead of landing in the
   // next query's row)
+  const uint32_t es = bf16_scores(a) ? 2u : 4u;
   auto score_off = [&](int key) {
-    return key < a.n_cap ? ((uint32_t)h * (uint32_t)a.n_cap + (uint32_t)key) * 4u : 0xfffffff0u;
+    return key < a.n_cap ? ((uint32_t)h * (uint32_t)a.n_cap + (uint32_t)key) * es : 0xfffffff0u;
+  };
+  auto store_sc = [&](float v, uint32_t off) {
+    if (es == 2u) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rsc, off, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsc, off, 0, 0);
   };
 
   if (W < ntv) {
@@ -536,20 +588,20 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
         const int key = (W + j * NW) * 32 + col;
         const bool vis = key < my_nvis;
         const float sc = vis ? tot : -INFINITY;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, score_off(key), 0, 0);
-        if (vis) atomicAdd(&lhist[h][order_key(sc) >> kShift1], 1u);
+        store_sc(sc, score_off(key));
+        if (vis) atomicAdd(&lhist[h][order_key(stored_score(a, sc)) >> kShift1], 1u);
         fetch(j + R, u);
       }
     }
     // tiles of this wave that the rounds did not reach get -inf
     for (int j = n_rounds * R; j < TPW; ++j) {
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc, score_off((W + j * NW) * 32 + col), 0, 0);
+      store_sc(-INFINITY, score_off((W + j * NW) * 32 + col));
     }
   } else {
     // no query sees any key of this wave
     for (int j = 0; j < TPW; ++j) {
       const int64_t key = (int64_t)(W + j * NW) * 32 + col;
-      if (h < live_q && key < a.n_cap) score_row(a, b, r0 + h)[key] = -INFINITY;
+      if (h < live_q && key < a.n_cap) store_score(a, score_row(a, b, r0 + h), key, -INFINITY);
     }
   }
   __syncthreads();
@@ -579,9 +631,9 @@ __global__ void __launch_bounds__(256) index_f32_kernel(IndexLaunch a) {
         for (int c = 0; c < a.d_I; ++c) dot = fmaf(q[c], k[c], dot);
         s += a.w[qrow + h] * fmaxf(dot, 0.f);
       }
-      atomicAdd(&lhist[order_key(s) >> kShift1], 1u);
+      atomicAdd(&lhist[order_key(stored_score(a, s)) >> kShift1], 1u);
     }
-    score_row(a, b, r)[key] = s;
+    store_score(a, score_row(a, b, r), key, s);
   }
   __syncthreads();
   flush_hist(lhist, a.hist + ((int64_t)b * a.n_qb + r) * kBins1, kBins1);
@@ -667,7 +719,7 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
 #pragma unroll
     for (int j = 0; j < kChunk / 256; ++j) {
       const int64_t i = c0 + j * 256 + threadIdx.x;
-      sv[j] = i < n_vis ? sc[i] : 0.f;
+      sv[j] = i < n_vis ? load_score(a, sc, i) : 0.f;
     }
     // every workgroup finds the first-digit bucket of the k-th largest score
     __shared__ uint32_t s_digit, s_kin;
@@ -719,7 +771,7 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       const int64_t i = c0 + j * 256 + threadIdx.x;
-      sv[j] = i < n_vis ? sc[i] : 0.f;
+      sv[j] = i < n_vis ? load_score(a, sc, i) : 0.f;
     }
     // the bucket of the k-th key, found once per query by topk_bucket_kernel
     const TopkState st = a.state[q];
@@ -798,12 +850,11 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
 #pragma unroll
   for (int j = 0; j < 16; j += 4) {
     const int64_t i = e0 + j;
-    if (i + 3 < a.n_cap && (((uintptr_t)(sc + i)) & 15) == 0) {
-      const f32x4 x = *(const f32x4*)(sc + i);
-      sv[j] = x[0]; sv[j + 1] = x[1]; sv[j + 2] = x[2]; sv[j + 3] = x[3];
+    if (i + 3 < a.n_cap) {
+      load_score4(a, sc, i, sv + j);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
+      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? load_score(a, sc, i + u) : -INFINITY;
     }
   }
   const TopkState st = a.state[q];
@@ -1190,12 +1241,11 @@ __global__ void __launch_bounds__(256) topk_emit_kernel(IndexLaunch a) {
 #pragma unroll
   for (int j = 0; j < 16; j += 4) {
     const int64_t i = e0 + j;
-    if (i + 3 < a.n_cap && (((uintptr_t)(sc + i)) & 15) == 0) {
-      const f32x4 x = *(const f32x4*)(sc + i);
-      sv[j] = x[0]; sv[j + 1] = x[1]; sv[j + 2] = x[2]; sv[j + 3] = x[3];
+    if (i + 3 < a.n_cap) {
+      load_score4(a, sc, i, sv + j);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? sc[i + u] : -INFINITY;
+      for (int u = 0; u < 4; ++u) sv[j + u] = i + u < a.n_cap ? load_score(a, sc, i + u) : -INFINITY;
     }
   }
   __shared__ int red[2][4];
@@ -1258,7 +1308,9 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   // with many queries and the scores in the workspace, collect leaves the
   // selected-index lists in place of the scores and the threshold pass
   // writes the output from them (no emit launch)
-  t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK;
+  // (BF16 scores: a chunk's 2-byte score slots cannot hold its index lists)
+  t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK &&
+                !(a.flags & CSA_INDEX_BF16_SCORES);
   if (t.list_mode) {
     topk_bucket_kernel<<<nq, 256, 0, s>>>(t);
     topk_collect_kernel<true><<<g2, 256, 0, s>>>(t);

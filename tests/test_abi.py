@@ -215,5 +215,5 @@ def test_batch_invariant_flags(K):
     a = _index_args(K, flags=K.INDEX_BATCH_INVARIANT)
     n = lib.csa_workspace_bytes(K.OP_INDEX_TOPK, C.cast(C.pointer(a), C.c_void_p))
     assert 0 < n < (1 << 40)
-    bad = _index_args(K, flags=2)
+    bad = _index_args(K, flags=4)
     assert lib.csa_index_topk(C.byref(bad), FAKE, n, None) == K.CSA_EINVAL
