@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 enum {
   CSA_OK = 0,
@@ -90,7 +90,15 @@ enum {
    * a query's output and LSE are bitwise the same alone, inside any batch and
    * as one row of a prefill chunk.  Without it the split count follows B and
    * n_q (to fill the GPU), which changes the order of the fp32 sums. */
-  CSA_ATTEND_BATCH_INVARIANT = 4
+  CSA_ATTEND_BATCH_INVARIANT = 4,
+  /* The window buffer is a per-request ring (the state cache of the paged
+   * layout below): position p sits at row p % win_len, and the ring holds
+   * positions win_pos0[b] .. win_pos0[b] + win_len - 1 (older rows have been
+   * overwritten); with win_pos0 NULL a query at position t finds positions
+   * max(0, t - win_len + 1) .. t there (decode: the newest token's row has
+   * just been stored).  Without the flag position p sits at row
+   * p - win_pos0[b]. */
+  CSA_ATTEND_WIN_RING = 8
 };
 #define CSA_INVARIANT_SPLIT_ROWS 1024
 
@@ -110,6 +118,35 @@ enum {
    * (2 bytes per score, same [B][n_q][n_cap] layout). */
   CSA_INDEX_BF16_SCORES = 2
 };
+
+/*
+ * ---------------------------------------------------------------- paged layout
+ * Heterogeneous KV cache [W1 "关键观察" observation 3 and "训练与推理基础设施"
+ * (异构 KV); W2 "异构 KV cache 与磁盘前缀复用" and Fig. 5]: the layers' caches
+ * grow at different rates (one CSA entry and one indexer key per 4 tokens,
+ * one HCA entry per 128, window rows per token), so one block size in tokens
+ * cannot serve them all.  Compressed entries live in a classical block cache
+ * whose blocks cover lcm(4, 128) = 128 raw tokens each: 32 CSA main entries,
+ * 32 indexer keys or 1 HCA entry per block of a layer's pool; the sliding
+ * window and the not-yet-compressed tail of every request live in a
+ * fixed-size per-request state cache (rings).
+ *
+ * Block tables.  An op that takes `block_table` (int32 [B][bt_stride], device)
+ * reads or writes entry i of sequence b in physical block
+ * blk = block_table[b * bt_stride + i / block_rows], at row i % block_rows of
+ * that block: byte offset (blk * block_rows + i % block_rows) * row_stride
+ * from the base pointer of each array (the pool), for every array of the
+ * call with its own row stride; the per-sequence stride is then unused.
+ * bt_stride * block_rows must cover the op's entry capacity (n_cap).  A
+ * block id outside [0, pool_blocks) marks an unallocated block: attention
+ * skips its entries, the indexer reads its keys as zero, compression skips
+ * its stores.  Block tables must not change while a call that reads them
+ * runs.
+ *
+ * Rings.  csa_compress reads its inputs from rings of `in_ring` rows
+ * (position p at row p % in_ring) and the attention reads the window from a
+ * ring with CSA_ATTEND_WIN_RING: the state cache.
+ */
 
 /*
  * ---------------------------------------------------------------- csa_compress
@@ -152,6 +189,30 @@ enum {
  *                     (d % 32 == 0, d_rope == 0, do_norm == 0 expected).
  * Constraints: 1 <= m <= 1024, 1 <= d <= 1024, d % 8 == 0, d_rope even and
  * <= d, n_rows >= 0, B >= 1.  n_rows = 0 or no complete block is a no-op.
+ *
+ * State cache and paged outputs (ABI 3; see "paged layout" above):
+ *   in_ring > 0     the inputs are rings: the token at position p is at row
+ *                   p % in_ring (the rows of positions pos0 .. pos0 + n_rows - 1
+ *                   must be present, so n_rows <= in_ring); in_seq_stride
+ *                   separates the sequences' rings.
+ *   out_block_table entry i of sequence b is stored in block
+ *                   out_block_table[b * out_bt_stride + i / out_block_rows] of
+ *                   each output pool, at row i % out_block_rows (out_row0 must
+ *                   be 0; the out*_seq_stride are unused); block ids outside
+ *                   [0, out_pool_blocks) skip the store.
+ *   out_ring > 0    entry i is stored at output row i % out_ring (a window
+ *                   ring; out_row0 must be 0, no block table).
+ *   seq_pos         per-sequence decode mode: sequence b's newest token is at
+ *                   position seq_pos[b] (its rows already in the rings, so
+ *                   in_ring > 0 is required: in_ring >= 2m with overlap, >= m
+ *                   without); the call stores the one entry that token
+ *                   completes, entry (seq_pos[b] + 1)/m - 1 when
+ *                   (seq_pos[b] + 1) % m == 0, and nothing for that sequence
+ *                   otherwise.  pos0 and n_rows are ignored.  With m = 1 every
+ *                   token is an entry: the window-row store.
+ * Decode appends one token per step to the rings and compresses a block when
+ * it completes: incremental compression, bitwise equal to compressing the
+ * whole sequence at once (same kernels, same order of every sum).
  */
 typedef struct CsaCompressArgs {
   int32_t B;
@@ -181,6 +242,14 @@ typedef struct CsaCompressArgs {
   int64_t out0_seq_stride;
   int64_t out1_stride;
   int64_t out1_seq_stride;
+  /* ABI 3: state-cache rings and paged outputs */
+  int32_t in_ring;                  /* 0: row r = position pos0 + r; > 0: position p at row p % in_ring */
+  int32_t out_block_rows;           /* entries per block of out_block_table */
+  const int32_t* out_block_table;   /* NULL: contiguous outputs; else [B][out_bt_stride] block ids */
+  int64_t out_bt_stride;            /* int32 elements per sequence in out_block_table */
+  int32_t out_pool_blocks;          /* blocks in the output pools */
+  int32_t out_ring;                 /* > 0: entry i at output row i % out_ring (no block table) */
+  const int64_t* seq_pos;           /* NULL, or device int64 [B]: per-sequence decode mode */
 } CsaCompressArgs;
 
 /*
@@ -226,6 +295,11 @@ typedef struct CsaCompressArgs {
  * per sequence, so the workspace stays below about 3 GiB at any n_q (with
  * or without out_score).
  * Constraint: n_cap <= 4194304.
+ * Paged keys (ABI 3): with block_table, k0 and k1 are the pools' bases and key
+ * i of sequence b is row i % block_rows of block block_table[b * bt_stride +
+ * i / block_rows] (64-byte code rows and 4-byte scale words with MXFP4,
+ * d_I floats with F32); MXFP4 needs block_rows == 32 and pool_blocks <= 2^20.
+ * Scores and selections equal those of the contiguous layout bitwise.
  * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
  * records on `stream` around its scoring kernel (with several internal query
  * blocks, before the first block's and after the last block's).
@@ -252,6 +326,12 @@ typedef struct CsaIndexArgs {
   void* out_score;   /* fp32, or BF16 codes with CSA_INDEX_BF16_SCORES */
   void* ev_start;   /* optional hipEvent_t recorded just before the scoring kernel */
   void* ev_stop;    /* optional hipEvent_t recorded just after it (NULL = none) */
+  /* ABI 3: paged keys (see "paged layout"); NULL block_table = contiguous */
+  const int32_t* block_table;   /* [B][bt_stride] block ids */
+  int32_t bt_stride;
+  int32_t block_rows;           /* keys per block: 32 with MXFP4 */
+  int32_t pool_blocks;          /* blocks in the k0 / k1 pools */
+  int32_t _pad1;
 } CsaIndexArgs;
 
 /*
@@ -289,6 +369,12 @@ typedef struct CsaIndexArgs {
  * strides (kv_stride, win_stride) below 2^31 bytes (CSA_EUNSUPPORTED otherwise);
  * F32 needs d <= 512 and H <= 128.  1 <= n_win, win_len >= 0.
  * Workspace: csa_workspace_bytes(CSA_OP_ATTEND / CSA_OP_HCA_ATTEND, &args).
+ * Paged entries (ABI 3): with block_table, kv0 / kv1 are the pools' bases
+ * and entry i of sequence b is row i % block_rows of block block_table[b *
+ * bt_stride + i / block_rows] (kv_seq_stride unused); entries in blocks
+ * outside [0, pool_blocks) are skipped.  With CSA_ATTEND_WIN_RING the window
+ * buffer is a ring (see the flag).  Outputs equal those of the contiguous
+ * layout bitwise.
  * Timing hook: ev_start / ev_stop, when not NULL, are HIP events the call
  * records on `stream` around its attention kernel.
  */
@@ -326,6 +412,12 @@ typedef struct CsaAttendArgs {
   float* out_lse;
   void* ev_start;   /* optional hipEvent_t recorded just before the attention kernel */
   void* ev_stop;    /* optional hipEvent_t recorded just after it (NULL = none) */
+  /* ABI 3: paged entries (see "paged layout"); NULL block_table = contiguous */
+  const int32_t* block_table;   /* [B][bt_stride] block ids */
+  int32_t bt_stride;
+  int32_t block_rows;           /* entries per block: 32 for CSA, 1 for HCA */
+  int32_t pool_blocks;          /* blocks in the kv0 / kv1 pools */
+  int32_t _pad1;
 } CsaAttendArgs;
 
 /* ABI version of the loaded library (CSA_ABI_VERSION). */

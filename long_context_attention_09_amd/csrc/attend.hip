@@ -9,20 +9,20 @@
 // joins every head's softmax denominator.
 //
 // FP8_BF16 kernel (gfx950 matrix cores).  A workgroup owns one query, 64
-// heads and one contiguous split of the query's KV list.  KV rows stream
-// through LDS in tiles of 32 entries: every thread fetches its share of the
-// 576-byte rows (448 E4M3FN bytes + 64 BF16 values) with 16-byte loads into
-// registers three tiles ahead, then widens FP8 to BF16 (exact, hardware
-// converter) into a row-major LDS tile whose 16-byte chunks are swizzled per
-// row.  Per tile the eight wavefronts first form the scores
-//   S^T[32 entries x 64 heads] = K Q^T       (V_MFMA_F32_32X32X16_BF16)
-// split as 2 head halves x 4 dim quarters, with the normalised, rotated
-// query held in registers as the B operand; the dim-quarter partials are
-// summed through LDS by the wave that runs the online softmax (log2 domain,
-// lazy rescale) of 8 heads, which leaves P in LDS as BF16.  Then
-//   O^T[512 dims x 64 heads] += V^T P^T
-// is split by dims only (64 per wave), with V^T read once through
-// ds_read_b64_tr_b16 transposing reads.
+// heads and one split of the query's KV list (the list's 32-entry tiles dealt
+// round-robin to the splits).  Eight wavefronts, two per SIMD: wave q + 4 h
+// owns dim quarter q and head half h.  Each lane loads 16-byte pieces of one
+// entry row straight into registers two tiles ahead; the FP8 bytes are
+// widened to BF16 in registers for the score product
+//   S^T[32 entries x 32 heads] (partial over the quarter) = K Q^T
+// (V_MFMA_F32_32X32X16_BF16, normalised and rotated query as the B operand),
+// and the raw bytes go to the quarter's slice of an LDS tile.  The four
+// quarters' partial scores meet in LDS, where each wave runs the online
+// softmax (log2 domain, lazy rescale) of 8 heads and leaves P as BF16; then
+//   O^T[quarter's 128 dims x 32 heads] += V^T P^T
+// with V^T read back from the slice by transposing LDS reads.  Scores of tile
+// t, softmax of tile t-1 and the output product of tile t-2 share one step
+// and one barrier.
 //
 // A split that covers the whole list finalises in place (sink, normalisation,
 // inverse RoPE, BF16 store); otherwise (running max, sum, normalised output) partials
@@ -47,8 +47,9 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 struct ListInfo {
   int n_comp;     // compressed part of the list (top_k for CSA, n_vis for HCA)
   int n_vis;      // visible compressed entries
-  int win_lo;     // first window buffer row
+  int win_lo;     // window buffer row of the first window position in the list
   int n_w;        // window rows present
+  int win_wrap;   // rows of the ring (window row win_lo + w wraps there); large without a ring
   int64_t t;
 };
 
@@ -62,14 +63,36 @@ __device__ __forceinline__ ListInfo list_info(const AttendLaunch& a, int b, int 
   nv = nv < a.n_cap ? nv : a.n_cap;
   L.n_vis = (int)(nv < 0 ? 0 : nv);
   L.n_comp = a.idx ? a.top_k : L.n_vis;
-  const int64_t wp0 = a.win_pos0[b];
+  int64_t wp0;
+  if (a.win_pos0) {
+    wp0 = a.win_pos0[b];
+  } else {                       // a ring that ends at the query's own position
+    wp0 = t - a.win_len + 1;
+    wp0 = wp0 > 0 ? wp0 : 0;
+  }
   int64_t lo = t - a.n_win + 1;
   lo = lo > 0 ? lo : 0;
   lo = lo > wp0 ? lo : wp0;
   int64_t hi = t < wp0 + a.win_len - 1 ? t : wp0 + a.win_len - 1;
-  L.win_lo = (int)(lo - wp0);
+  const bool ring = (a.flags & CSA_ATTEND_WIN_RING) && a.win_len > 0;
+  L.win_lo = ring ? (int)(lo % a.win_len) : (int)(lo - wp0);
+  L.win_wrap = ring ? a.win_len : 0x7fffffff;
   L.n_w = hi >= lo ? (int)(hi - lo + 1) : 0;
   return L;
+}
+
+// Window buffer row of the list's window position w.
+__device__ __forceinline__ int window_row(const ListInfo& L, int w) {
+  const int row = L.win_lo + w;
+  return row >= L.win_wrap ? row - L.win_wrap : row;
+}
+
+// Row of entry e (0 <= e < n_vis) of sequence b in the kv arrays: e itself,
+// or with a block table its row in the pool; -1 when its block is unallocated.
+__device__ __forceinline__ int entry_row(const AttendLaunch& a, int b, int e) {
+  if (!a.bt) return e;
+  const int blk = a.bt[(int64_t)b * a.bt_stride + e / a.block_rows];
+  return blk >= 0 && blk < a.pool_blocks ? blk * a.block_rows + e % a.block_rows : -1;
 }
 
 // Splits of a query's list.  Normally the launch's split count (chosen to fill
@@ -93,6 +116,8 @@ __device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, co
       e = a.idx[((int64_t)b * a.n_q + r) * a.top_k + p];
       if (e < 0 || e >= L.n_vis) return false;
     }
+    e = entry_row(a, b, e);
+    if (e < 0) return false;
     const int64_t off = (int64_t)b * a.kv_seq_stride + (int64_t)e * a.kv_stride;
     *pn = (const uint8_t*)a.kv0 + off;
     *pr = (const uint8_t*)a.kv1 + off;
@@ -100,7 +125,7 @@ __device__ __forceinline__ bool list_row(const AttendLaunch& a, int b, int r, co
   }
   const int w = p - L.n_comp;
   if (w >= L.n_w) return false;
-  const int64_t off = (int64_t)b * a.win_seq_stride + (int64_t)(L.win_lo + w) * a.win_stride;
+  const int64_t off = (int64_t)b * a.win_seq_stride + (int64_t)window_row(L, w) * a.win_stride;
   *pn = (const uint8_t*)a.win0 + off;
   *pr = (const uint8_t*)a.win1 + off;
   return true;
@@ -191,23 +216,27 @@ struct RowSource {
   uint64_t kvb0, kvb1, wb0, wb1, dummy;   // entry / window bases of the sequence
   uint32_t kvs, wns;                      // row strides
   int p1, n_comp, n_vis, n_w;             // list end, list layout
-  bool gather;                            // entries through staged indices (CSA)
+  int wlo, wrap;                          // window row of the first window position; ring rows
+  bool gather;                            // entries through staged rows (CSA, or a block table)
 };
 struct RowPtrs {
   uint64_t pn, pr;                        // FP8 bytes, RoPE bytes of the row
   uint32_t live;                          // the tile's live-entry mask
 };
 
-// Row pointers of list position p (sel: its staged index when gathering).
+// Row pointers of list position p (sel: its staged row when gathering,
+// already checked against the visible entries; -1 = masked).
 template <bool kRope>
 __device__ __forceinline__ RowPtrs row_ptrs(const RowSource rs, int p, int sel) {
   const bool in = p < rs.p1;
   const bool comp = p < rs.n_comp;
   const int e = rs.gather ? sel : p;
   const int w = p - rs.n_comp;
-  const bool ok_c = in && comp && e >= 0 && e < rs.n_vis;
+  const bool ok_c = in && comp && e >= 0 && (rs.gather || e < rs.n_vis);
   const bool ok_w = in && !comp && w < rs.n_w;
-  const uint32_t row = ok_c ? (uint32_t)e : ok_w ? (uint32_t)w : 0u;
+  int wr = rs.wlo + w;
+  wr = wr >= rs.wrap ? wr - rs.wrap : wr;
+  const uint32_t row = ok_c ? (uint32_t)e : ok_w ? (uint32_t)wr : 0u;
   const uint32_t stride = ok_c ? rs.kvs : rs.wns;
   const uint64_t off = (uint64_t)row * stride;
   RowPtrs r;
@@ -275,9 +304,17 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
 #pragma unroll
   for (int u = 0; u < kStages; ++u) {
     const int pos = ATTEND_POS(u);
-    sel0[u] = a.idx ? idx_row[pos < a.top_k ? pos : 0] : ((const int*)a.q)[r32];
+    sel0[u] = a.idx ? idx_row[pos < a.top_k ? pos : 0] : pos;
   }
   if (!inv) L = list_info(a, b, r);
+  // Entries are gathered through staged rows for CSA and with a block table:
+  // entry index -> row of the kv arrays, -1 for an invisible or unallocated one.
+  const bool gather = a.idx != nullptr || a.bt != nullptr;
+  auto stage_row = [&](int e) { return e >= 0 && e < L.n_vis ? entry_row(a, b, e) : -1; };
+  if (gather) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) sel0[u] = stage_row(sel0[u]);
+  }
   const int list_len = L.n_comp + L.n_w;
   const int list_tiles = (list_len + kTile - 1) / kTile;
   const int n_tiles = list_tiles > split ? (list_tiles - split + n_sp - 1) / n_sp : 0;
@@ -289,15 +326,17 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   rsrc.dummy = (uint64_t)a.q;                // >= 1 KiB of readable bytes
   rsrc.kvb0 = (uint64_t)a.kv0 + (uint64_t)((int64_t)b * a.kv_seq_stride);
   rsrc.kvb1 = (uint64_t)a.kv1 + (uint64_t)((int64_t)b * a.kv_seq_stride);
-  rsrc.wb0 = (uint64_t)a.win0 + (uint64_t)((int64_t)b * a.win_seq_stride + (int64_t)L.win_lo * a.win_stride);
-  rsrc.wb1 = (uint64_t)a.win1 + (uint64_t)((int64_t)b * a.win_seq_stride + (int64_t)L.win_lo * a.win_stride);
+  rsrc.wb0 = (uint64_t)a.win0 + (uint64_t)((int64_t)b * a.win_seq_stride);
+  rsrc.wb1 = (uint64_t)a.win1 + (uint64_t)((int64_t)b * a.win_seq_stride);
+  rsrc.wlo = L.win_lo;
+  rsrc.wrap = L.win_wrap;
   rsrc.kvs = (uint32_t)a.kv_stride;
   rsrc.wns = (uint32_t)a.win_stride;
   rsrc.p1 = list_len;
   rsrc.n_comp = L.n_comp;
   rsrc.n_vis = L.n_vis;
   rsrc.n_w = L.n_w;
-  rsrc.gather = a.idx != nullptr;
+  rsrc.gather = gather;
   // index of tile t's entry for this lane (tiles from kStages on: staged in LDS)
 #define ATTEND_SEL(t) S.lidx[(t) * kTile + r32 < kIdxMax ? (t) * kTile + r32 : kIdxMax - 1]
   i32x4 kst[kStages][NL];
@@ -315,12 +354,11 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
     S.rope[tid] = cs;
     S.rope[32 + tid] = sn;
   }
-  if (a.idx) {
-    const int* src = a.idx + ((int64_t)b * a.n_q + r) * a.top_k;
+  if (gather) {
     const int n_loc = n_tiles * kTile < kIdxMax ? n_tiles * kTile : kIdxMax;
     for (int i = tid; i < n_loc; i += kThreads) {
       const int pos = ((i / kTile) * n_sp + split) * kTile + (i % kTile);
-      if (pos < L.n_comp) S.lidx[i] = src[pos];
+      if (pos < L.n_comp) S.lidx[i] = stage_row(idx_row ? idx_row[pos] : pos);
     }
   }
   // tile -1's slices (buffer 1) and tile -2's P (buffer 0) are zero, its factors 1

@@ -196,7 +196,7 @@ __device__ __forceinline__ void fold_candidates(const CompressLaunch& a, int b, 
         live[u] = c < c_end;
         c = live[u] ? c : 0;
         const bool a_side = c < m;
-        const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
+        const int64_t row = compress_in_row(a, a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0);
         const char* kp = (a_side ? base_ka : base_kb) + row * a.in_row_stride + (int64_t)coff * (int64_t)sizeof(T);
         const char* g = a_side ? base_ga : base_gb;
         g_ok[u] = in && g != nullptr;
@@ -252,7 +252,7 @@ __device__ __forceinline__ void fold_candidates(const CompressLaunch& a, int b, 
       live[u] = c < c_end;
       c = live[u] ? c : 0;
       const bool a_side = c < m;
-      const int64_t row = a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0;
+      const int64_t row = compress_in_row(a, a_side ? m * i + c - a.pos0 : m * (i - 1) + (c - m) - a.pos0);
       const char* kbase = a_side ? base_ka : base_kb;
       const char* gbase = a_side ? base_ga : base_gb;
       const float* bb = a_side ? a.bias_a : a.bias_b;
@@ -310,7 +310,8 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
   const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
   const int b = blockIdx.y;
   if (b >= a.B || entry_local >= a.n_entries) return;
-  const int64_t i = a.i_first + entry_local;           // absolute entry index
+  const int64_t i = compress_entry(a, b, entry_local);  // absolute entry index
+  if (i < 0) return;
   const int c0 = lane * CPT;
   const int d = a.d;
   const int m = a.m;
@@ -415,14 +416,17 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
     }
   }
 
+  const int64_t off0 = compress_out_off(a, b, i, a.out0_stride, a.out0_seq_stride);
+  const int64_t off1 = compress_out_off(a, b, i, a.out1_stride, a.out1_seq_stride);
+  if (off0 < 0) return;                                // unallocated block
   if (a.out_fmt == CSA_FMT_F32) {
-    float* o = (float*)((char*)a.out0 + (int64_t)b * a.out0_seq_stride + (i - a.out_row0) * a.out0_stride);
+    float* o = (float*)((char*)a.out0 + off0);
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
       if (c0 + k < d) o[c0 + k] = x[k];
   } else if (a.out_fmt == CSA_FMT_FP8_BF16) {
-    uint8_t* on = (uint8_t*)a.out0 + (int64_t)b * a.out0_seq_stride + (i - a.out_row0) * a.out0_stride;
-    uint16_t* orr = (uint16_t*)((char*)a.out1 + (int64_t)b * a.out1_seq_stride + (i - a.out_row0) * a.out1_stride);
+    uint8_t* on = (uint8_t*)a.out0 + off0;
+    uint16_t* orr = (uint16_t*)((char*)a.out1 + off1);
     if constexpr (CPT == 8) {
       // a lane's 8 channels are all FP8 or all BF16 when d - d_rope is a
       // multiple of 8: one 8-byte or 16-byte store where aligned
@@ -453,8 +457,8 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
     for (int k = 0; k < CPT; ++k) amax = fmaxf(amax, fabsf(x[k]));
     for (int o = 1; o < 32 / CPT; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     const int E = mx_block_exponent(amax);
-    uint8_t* oc = (uint8_t*)a.out0 + (int64_t)b * a.out0_seq_stride + (i - a.out_row0) * a.out0_stride;
-    uint8_t* os = (uint8_t*)a.out1 + (int64_t)b * a.out1_seq_stride + (i - a.out_row0) * a.out1_stride;
+    uint8_t* oc = (uint8_t*)a.out0 + off0;
+    uint8_t* os = (uint8_t*)a.out1 + off1;
     if (c0 < d) {
 #pragma unroll
       for (int k = 0; k < CPT; k += 2) {
@@ -481,7 +485,8 @@ __global__ void __launch_bounds__(256, 2) compress_part_kernel(CompressBatch bat
   const int e = blockIdx.x / a.n_parts, g = blockIdx.x % a.n_parts;
   const int b = blockIdx.y;
   if (b >= a.B || e >= a.n_entries) return;
-  const int64_t i = a.i_first + e;
+  const int64_t i = compress_entry(a, b, e);
+  if (i < 0) return;
   const int n_cand = (a.kv_b && i >= 1) ? 2 * a.m : a.m;
   const int c_lo = g * kPartCands;
   const int c_end = c_lo + kPartCands < n_cand ? c_lo + kPartCands : n_cand;

@@ -63,7 +63,29 @@ int check_compress(const CsaCompressArgs* a) {
     if (a->d % 32 || a->d_rope != 0) return CSA_EUNSUPPORTED;
     if (a->out1_stride <= 0 || a->out1_seq_stride < 0) return CSA_EINVAL;
   }
+  if (a->in_ring < 0 || (a->in_ring > 0 && !a->seq_pos && a->n_rows > a->in_ring)) return CSA_EINVAL;
+  if (a->out_block_table) {
+    if (!aligned(a->out_block_table, 4) || a->out_block_rows < 1 || a->out_bt_stride < 1 ||
+        a->out_pool_blocks < 1 || a->out_row0 != 0)
+      return CSA_EINVAL;
+  }
+  if (a->out_ring < 0 || (a->out_ring > 0 && (a->out_block_table || a->out_row0 != 0))) return CSA_EINVAL;
+  if (a->seq_pos) {
+    if (!aligned(a->seq_pos, 8) || a->in_ring < (a->overlap ? 2 * a->m : a->m)) return CSA_EINVAL;
+  }
   return CSA_OK;
+}
+
+// Entries [first, end) the job stores (the per-sequence decode mode: one slot,
+// resolved per sequence on the device).
+void job_entries(const CsaCompressArgs* a, int64_t* first, int64_t* end) {
+  if (a->seq_pos) {
+    *first = 0;
+    *end = 1;
+    return;
+  }
+  *first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
+  *end = (a->pos0 + a->n_rows) / a->m;
 }
 
 }  // namespace
@@ -92,6 +114,13 @@ int check_index(const CsaIndexArgs* a) {
     if (!aligned(a->q0, 4) || !aligned(a->k0, 4)) return CSA_EINVAL;
   } else {
     return CSA_EINVAL;
+  }
+  if (a->block_table) {
+    if (!aligned(a->block_table, 4) || a->block_rows < 1 || a->bt_stride < 1 || a->pool_blocks < 1)
+      return CSA_EINVAL;
+    if ((int64_t)a->bt_stride * a->block_rows < a->n_cap) return CSA_EINVAL;
+    if (a->fmt == CSA_FMT_MXFP4 && (a->block_rows != 32 || a->pool_blocks >= (1 << 20)))
+      return CSA_EUNSUPPORTED;
   }
   return CSA_OK;
 }
@@ -160,16 +189,26 @@ int check_attend(const CsaAttendArgs* a, bool dense) {
   if (a->d_rope < 0 || a->d_rope > a->d || (a->d_rope & 1)) return CSA_EINVAL;
   if (a->d_rope > 0 && !(a->rope_theta > 0.0)) return CSA_EINVAL;
   if (!(a->softmax_scale >= 0.0f)) return CSA_EINVAL;
-  if (!a->q_pos || !a->q || !a->sink || !a->out || !a->win_pos0) return CSA_EINVAL;
+  if (!a->q_pos || !a->q || !a->sink || !a->out) return CSA_EINVAL;
+  if (!a->win_pos0 && !(a->flags & CSA_ATTEND_WIN_RING)) return CSA_EINVAL;
   if (a->n_cap > 0 && !a->kv0) return CSA_EINVAL;
   if (a->win_len > 0 && !a->win0) return CSA_EINVAL;
   if (dense ? a->idx != nullptr : (a->idx == nullptr || a->top_k < 1)) return CSA_EINVAL;
-  if (!aligned(a->q_pos, 8) || !aligned(a->win_pos0, 8) || !aligned(a->sink, 4)) return CSA_EINVAL;
+  if (!aligned(a->q_pos, 8) || (a->win_pos0 && !aligned(a->win_pos0, 8)) || !aligned(a->sink, 4))
+    return CSA_EINVAL;
   if (a->idx && !aligned(a->idx, 4)) return CSA_EINVAL;
   if (a->n_entries && !aligned(a->n_entries, 4)) return CSA_EINVAL;
   if (a->out_lse && !aligned(a->out_lse, 4)) return CSA_EINVAL;
   if (a->kv_stride < 0 || a->kv_seq_stride < 0 || a->win_stride < 0 || a->win_seq_stride < 0)
     return CSA_EINVAL;
+  if (a->flags & ~(CSA_ATTEND_NORM_Q | CSA_ATTEND_NO_INV_ROPE | CSA_ATTEND_BATCH_INVARIANT | CSA_ATTEND_WIN_RING))
+    return CSA_EINVAL;
+  if (a->block_table) {
+    if (!aligned(a->block_table, 4) || a->block_rows < 1 || a->bt_stride < 1 || a->pool_blocks < 1)
+      return CSA_EINVAL;
+    if ((int64_t)a->bt_stride * a->block_rows < a->n_cap) return CSA_EINVAL;
+    if ((int64_t)a->pool_blocks * a->block_rows > INT32_MAX) return CSA_EUNSUPPORTED;
+  }
   if (a->fmt == CSA_FMT_FP8_BF16) {
     if (a->d != 512 || a->d_rope != 64 || a->H % 16) return CSA_EUNSUPPORTED;
     if (a->n_cap > 0 && !a->kv1) return CSA_EINVAL;
@@ -233,8 +272,9 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   int64_t s = (256 + units - 1) / units;          // one workgroup per compute unit
   int64_t s_max = (tiles + 2) / 3;                // at least three tiles per split
   if (s > s_max) s = s_max;
-  const int64_t per_max = csa::kAttendIdxMax / 32;    // a CSA split's indices fit the kernel's stage
-  if (!dense) {
+  const int64_t per_max = csa::kAttendIdxMax / 32;    // a split's gathered rows fit the kernel's stage
+  const bool staged = !dense || a->block_table != nullptr;
+  if (staged) {
     const int64_t s_min = (tiles + per_max - 1) / per_max;
     if (s < s_min) s = s_min;
   }
@@ -244,7 +284,7 @@ AttendPlan plan_attend(const CsaAttendArgs* a, bool dense) {
   // an even number of tiles waste no step, so an odd count grows by one
   // (fewer splits for the combine, same kernel time).
   per += per & 1;
-  if (!dense && per > per_max) per = per_max;
+  if (staged && per > per_max) per = per_max;
   s = (tiles + per - 1) / per;
   const int64_t len = per * 32;
   p.n_splits = (int)s;
@@ -276,7 +316,9 @@ int run_attend(const CsaAttendArgs* a, void* ws, size_t ws_bytes, void* stream, 
   L.n_splits = p.n_splits; L.list_len = p.list_len; L.split_len = p.split_len;
   L.q_pos = a->q_pos; L.q = a->q; L.kv0 = a->kv0;
   L.kv1 = a->kv1;
-  L.kv_stride = a->kv_stride; L.kv_seq_stride = a->kv_seq_stride;
+  L.kv_stride = a->kv_stride; L.kv_seq_stride = a->block_table ? 0 : a->kv_seq_stride;
+  L.bt = a->block_table; L.bt_stride = a->bt_stride; L.block_rows = a->block_rows;
+  L.pool_blocks = a->pool_blocks;
   L.n_entries = a->n_entries; L.idx = dense ? nullptr : a->idx;
   L.win0 = a->win0; L.win1 = a->win1; L.win_stride = a->win_stride; L.win_seq_stride = a->win_seq_stride;
   L.win_pos0 = a->win_pos0; L.sink = a->sink; L.out = a->out; L.out_lse = a->out_lse;
@@ -341,14 +383,14 @@ namespace {
 
 // Fill the launch descriptor of one validated job; false when it has no entry.
 bool compress_job(const CsaCompressArgs* a, csa::CompressLaunch* L) {
-  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
-  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  int64_t first, end;
+  job_entries(a, &first, &end);
   if (end <= first) return false;
   *L = csa::CompressLaunch{};
   L->B = a->B; L->d = a->d; L->d_rope = a->d_rope; L->m = a->m; L->in_dtype = a->in_dtype;
   L->out_fmt = a->out_fmt; L->do_norm = a->do_norm; L->n_entries = (int32_t)(end - first);
   L->rms_eps = a->rms_eps; L->log_theta = a->d_rope > 0 ? log(a->rope_theta) : 0.0;
-  L->pos0 = a->pos0; L->i_first = first; L->out_row0 = a->out_row0;
+  L->pos0 = a->seq_pos ? 0 : a->pos0; L->i_first = first; L->out_row0 = a->out_row0;
   L->kv_a = a->kv_a; L->gate_a = a->gate_a; L->kv_b = a->kv_b; L->gate_b = a->gate_b;
   L->in_row_stride = a->in_row_stride;
   L->in_seq_stride = a->in_seq_stride;
@@ -356,15 +398,21 @@ bool compress_job(const CsaCompressArgs* a, csa::CompressLaunch* L) {
   L->out0 = a->out0; L->out1 = a->out1;
   L->out0_stride = a->out0_stride; L->out0_seq_stride = a->out0_seq_stride;
   L->out1_stride = a->out1_stride; L->out1_seq_stride = a->out1_seq_stride;
+  L->in_ring = a->in_ring;
+  L->out_bt = a->out_block_table; L->out_bt_stride = a->out_bt_stride;
+  L->out_block_rows = a->out_block_rows; L->out_pool_blocks = a->out_pool_blocks;
+  L->out_ring = a->out_ring; L->seq_pos = a->seq_pos;
   return true;
 }
 
 int check_compress_entries(const CsaCompressArgs* a) {
-  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
-  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  if (a->seq_pos) return CSA_OK;     // checked per sequence on the device (block ids against the pool)
+  int64_t first, end;
+  job_entries(a, &first, &end);
   if (end <= first) return CSA_OK;
   if (first < a->out_row0) return CSA_EINVAL;
   if (end - first > INT32_MAX / 4) return CSA_EUNSUPPORTED;
+  if (a->out_block_table && (end - 1) / a->out_block_rows >= a->out_bt_stride) return CSA_EINVAL;
   return CSA_OK;
 }
 
@@ -382,8 +430,8 @@ int compress_parts(const CsaCompressArgs* a) {
 
 size_t compress_part_bytes(const CsaCompressArgs* a) {
   const int P = compress_parts(a);
-  const int64_t first = a->pos0 / a->m + ((a->overlap && a->pos0 > 0) ? 1 : 0);
-  const int64_t end = (a->pos0 + a->n_rows) / a->m;
+  int64_t first, end;
+  job_entries(a, &first, &end);
   if (P == 0 || end <= first) return 0;
   return align_up((size_t)a->B * (size_t)(end - first) * (size_t)P * 3 * (size_t)a->d * sizeof(float));
 }
@@ -485,6 +533,8 @@ int run_index(const CsaIndexArgs* a, const IndexPlan& p, char* ws, void* stream)
     L.chunk_sel = (int32_t*)(ws + p.off_csel);
     L.chunk_eqb = (int32_t*)(ws + p.off_ceqb);
     L.lin = (uint8_t*)(ws + p.off_lin);
+    L.bt = a->block_table; L.bt_stride = a->bt_stride; L.block_rows = a->block_rows;
+    L.pool_blocks = a->pool_blocks;
     L.ev_start = q0 == 0 ? (hipEvent_t)a->ev_start : nullptr;
     L.ev_stop = q0 + p.n_qb >= a->n_q ? (hipEvent_t)a->ev_stop : nullptr;
     if (csa::launch_index_topk(L, (hipStream_t)stream) != hipSuccess) return CSA_EHIP;

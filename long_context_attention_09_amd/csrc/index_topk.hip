@@ -216,10 +216,19 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   const int W = (int)blockIdx.x * 4 + wave;
   constexpr int kGroups = kTilesPerWave / 4;                 // groups per wave
   const int ngv = (nvis_max + 63) / 64;                      // groups with a visible key
-  const uint8_t* kc = (const uint8_t*)a.k0 + (int64_t)b * a.n_cap * 64;
-  const uint32_t* ks = (const uint32_t*)a.k1 + (int64_t)b * a.n_cap;
+  // Paged keys: k0 / k1 are the pools and the wave's 2 kGroups blocks (two
+  // per 64-key group) are looked up once, lane l holding slot l; contiguous
+  // keys start at the sequence's row 0.
+  const bool paged = a.bt != nullptr;
+  const uint8_t* kc = (const uint8_t*)a.k0 + (paged ? 0 : (int64_t)b * a.n_cap * 64);
+  const uint32_t* ks = (const uint32_t*)a.k1 + (paged ? 0 : (int64_t)b * a.n_cap);
 
   if (W < ngv) {
+    int blk_v = -1;
+    if (paged && lane < 2 * kGroups) {
+      const int lb = 2 * (W + (lane >> 1) * NW) + (lane & 1);
+      if (lb * 32 < nvis_max) blk_v = a.bt[(int64_t)b * a.bt_stride + lb];
+    }
     // query operands: head (16 hg + col), bytes 16g .. 16g+15 of its 64-byte row
     i32x4 qa[QT][4];
     int qs[QT][4];
@@ -246,10 +255,11 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // count of loads in flight exact across iterations, and the ring stays
     // full instead of draining once per round.  (Byte offsets fit 32 bits:
     // n_cap <= 4M keys.)
+    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)nvis_max;   // key rows in range
     const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)((uint32_t)nvis_max * 64u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)(n_rec * 64u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)((uint32_t)nvis_max * 4u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)(n_rec * 4u), kBufferWord3);
     __amdgpu_buffer_rsrc_t rsc[QT];
 #pragma unroll
     for (int qi = 0; qi < QT; ++qi) {
@@ -276,9 +286,19 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // tile t of the wave: tile t % 4 of its group t / 4
     auto fetch = [&](int t, int u) {
       const uint32_t j = (uint32_t)t >> 2, q = (uint32_t)t & 3u;
-      kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rc, off_c + j * gs_c + q * 1024u, 0, 0));
-      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + j * gs_s + q * 64u, 0, 0);
+      uint32_t oc = off_c + j * gs_c + q * 1024u, os = off_s + j * gs_s + q * 64u;
+      if (paged) {
+        // tile q of group j: rows 16 (q % 2) .. +15 of the group's block q / 2;
+        // an unallocated block (or a tile past the wave's) reads zeros
+        const int sl = 2 * (int)j + (int)(q >> 1);
+        const int blk = sl < 2 * kGroups ? __builtin_amdgcn_readlane(blk_v, sl) : -1;
+        const bool ok = blk >= 0 && blk < a.pool_blocks;
+        const uint32_t row = 16u * (q & 1u) + (uint32_t)col;
+        oc = ok ? (uint32_t)blk * 2048u + row * 64u + (uint32_t)g * 16u : 0xffffff00u;
+        os = ok ? (uint32_t)blk * 128u + row * 4u : 0xffffff00u;
+      }
+      kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0));
+      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
     };
     // issue the first round in ring order (the loop consumes it in that order)
 #pragma unroll
@@ -449,6 +469,12 @@ __global__ void __launch_bounds__(128) index_linear_kernel(IndexLaunch a) {
   }
 }
 
+// Tiles of wave W (of NW per sequence, TPW at most) that hold a visible key.
+__device__ __forceinline__ int vt_all(int ntv, int W, int NW, int TPW) {
+  const int v = (ntv - W + NW - 1) / NW;
+  return v < TPW ? v : TPW;
+}
+
 template <int NH32>
 __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   constexpr int QT = kMqQT, R = kMqRing, TPW = kMqTiles;
@@ -476,8 +502,10 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   const int NW = 4 * (int)gridDim.x;
   const int W = (int)blockIdx.x * 4 + wave;
   const int ntv = (nvis_max + 31) / 32;        // tiles with a visible key
-  const uint8_t* kc = (const uint8_t*)a.k0 + (int64_t)b * a.n_cap * 64;
-  const uint32_t* ks = (const uint32_t*)a.k1 + (int64_t)b * a.n_cap;
+  // paged keys: k0 / k1 are the pools, a 32-key tile is one block
+  const bool paged = a.bt != nullptr;
+  const uint8_t* kc = (const uint8_t*)a.k0 + (paged ? 0 : (int64_t)b * a.n_cap * 64);
+  const uint32_t* ks = (const uint32_t*)a.k1 + (paged ? 0 : (int64_t)b * a.n_cap);
   // both query rows of the block's scores through one resource: rows past
   // the live queries are outside it, so their stores are dropped
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
@@ -531,19 +559,36 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
       la[s] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       ls[s] = lc < kLinComps ? (int)lin[kLinScaleOff + lc * 4 + 2 * s + h] : 127;
     }
+    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)nvis_max;   // key rows in range
     const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)((uint32_t)nvis_max * 64u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)(n_rec * 64u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)((uint32_t)nvis_max * 4u), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)ks, 0, (int)(n_rec * 4u), kBufferWord3);
     const uint32_t off_c = (uint32_t)W * 2048u + (uint32_t)col * 64u + (uint32_t)h * 16u;
     const uint32_t off_s = (uint32_t)W * 128u + (uint32_t)col * 4u;
     const uint32_t st_c = (uint32_t)NW * 2048u, st_s = (uint32_t)NW * 128u;
+    // paged: the block of the wave's tile 64 r + l in register r of lane l
+    int blk_v[TPW / 64];
+#pragma unroll
+    for (int r = 0; r < TPW / 64; ++r) {
+      const int T = W + (64 * r + lane) * NW;
+      blk_v[r] = paged && 64 * r + lane < vt_all(ntv, W, NW, TPW) ? a.bt[(int64_t)b * a.bt_stride + T] : -1;
+    }
     i32x4 kb[R][2];
     uint32_t kw[R];
     auto fetch = [&](int j, int u) {
-      kb[u][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, off_c + (uint32_t)j * st_c, 0, 0));
-      kb[u][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, off_c + (uint32_t)j * st_c + 32u, 0, 0));
-      kw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_s + (uint32_t)j * st_s, 0, 0);
+      uint32_t oc = off_c + (uint32_t)j * st_c, os = off_s + (uint32_t)j * st_s;
+      if (paged) {
+        const int r = j >> 6;
+        const int v = r == 0 ? blk_v[0] : r == 1 ? blk_v[1] : r == 2 ? blk_v[2] : blk_v[3];
+        const int blk = j < TPW ? __builtin_amdgcn_readlane(v, j & 63) : -1;
+        const bool ok = blk >= 0 && blk < a.pool_blocks;
+        oc = ok ? (uint32_t)blk * 2048u + (uint32_t)col * 64u + (uint32_t)h * 16u : 0xffffff00u;
+        os = ok ? (uint32_t)blk * 128u + (uint32_t)col * 4u : 0xffffff00u;
+      }
+      kb[u][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0));
+      kb[u][1] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc + 32u, 0, 0));
+      kw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
     };
 #pragma unroll
     for (int u = 0; u < R; ++u) {
@@ -623,12 +668,18 @@ __global__ void __launch_bounds__(256) index_f32_kernel(IndexLaunch a) {
   if (key < a.n_cap) {
     float s = -INFINITY;
     if (key < nvis) {
-      const float* k = (const float*)a.k0 + ((int64_t)b * a.n_cap + key) * a.d_I;
+      int64_t row = (int64_t)b * a.n_cap + key;
+      if (a.bt) {                    // paged: row key % block_rows of its block (none: a zero key)
+        const int blk = a.bt[(int64_t)b * a.bt_stride + key / a.block_rows];
+        row = blk >= 0 && blk < a.pool_blocks ? (int64_t)blk * a.block_rows + key % a.block_rows : -1;
+      }
+      const float* k = (const float*)a.k0 + (row < 0 ? 0 : row) * a.d_I;
       s = 0.f;
       for (int h = 0; h < a.H_I; ++h) {
         const float* q = (const float*)a.q0 + (qrow + h) * a.d_I;
         float dot = 0.f;
-        for (int c = 0; c < a.d_I; ++c) dot = fmaf(q[c], k[c], dot);
+        if (row >= 0)
+          for (int c = 0; c < a.d_I; ++c) dot = fmaf(q[c], k[c], dot);
         s += a.w[qrow + h] * fmaxf(dot, 0.f);
       }
       atomicAdd(&lhist[order_key(stored_score(a, s)) >> kShift1], 1u);

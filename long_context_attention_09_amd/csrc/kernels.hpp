@@ -24,7 +24,38 @@ struct CompressLaunch {
   int64_t out0_stride, out0_seq_stride, out1_stride, out1_seq_stride;
   float* part;               // NULL, or [B][n_entries][n_parts][3][d] pooled candidate groups
   int32_t n_parts;           // candidate groups of kPartCands per entry (with part)
+  int32_t in_ring;           // > 0: inputs are rings, position p at row p % in_ring
+  const int32_t* out_bt;     // NULL, or [B][out_bt_stride] output block ids
+  int64_t out_bt_stride;
+  int32_t out_block_rows, out_pool_blocks;
+  int32_t out_ring;          // > 0: entry i at output row i % out_ring
+  const int64_t* seq_pos;    // NULL, or [B]: per-sequence decode mode (one entry per sequence at most)
 };
+
+// Entry of sequence b that this launch's entry slot e stands for; -1: none.
+// Per-sequence decode mode: the entry that token seq_pos[b] completes.
+__device__ __forceinline__ int64_t compress_entry(const CompressLaunch& a, int b, int e) {
+  if (!a.seq_pos) return a.i_first + e;
+  const int64_t p1 = a.seq_pos[b] + 1;
+  return (p1 >= a.m && p1 % a.m == 0) ? p1 / a.m - 1 : -1;
+}
+
+// Row of position-relative input row `row` (position pos0 + row).
+__device__ __forceinline__ int64_t compress_in_row(const CompressLaunch& a, int64_t row) {
+  return a.in_ring > 0 ? (row + a.pos0) % a.in_ring : row;
+}
+
+// Byte offset of entry i of sequence b in an output array (row stride
+// `stride`, sequence stride `seq`); -1 when its block is unallocated.
+__device__ __forceinline__ int64_t compress_out_off(const CompressLaunch& a, int b, int64_t i, int64_t stride,
+                                                    int64_t seq) {
+  if (a.out_ring > 0) return (int64_t)b * seq + (i % a.out_ring) * stride;
+  if (!a.out_bt) return (int64_t)b * seq + (i - a.out_row0) * stride;
+  if (i / a.out_block_rows >= a.out_bt_stride) return -1;
+  const int blk = a.out_bt[(int64_t)b * a.out_bt_stride + i / a.out_block_rows];
+  if (blk < 0 || blk >= a.out_pool_blocks) return -1;
+  return ((int64_t)blk * a.out_block_rows + i % a.out_block_rows) * stride;
+}
 
 // Candidates per workgroup when long blocks are pooled in groups.
 constexpr int kPartCands = 16;
@@ -68,6 +99,8 @@ struct IndexLaunch {
   int32_t list_mode;         // collect leaves the chunk's selected-index lists in its score region
   uint8_t* lin;              // [B * n_qb][kIndexLinBytes]: FP8 split of the weighted query sum (query blocks)
   hipEvent_t ev_start, ev_stop;  // recorded around the scoring kernel (may be null)
+  const int32_t* bt;         // NULL, or [B][bt_stride] key block ids (k0 / k1 are the pools)
+  int32_t bt_stride, block_rows, pool_blocks;
 };
 
 // Longest split of a CSA selection list the FP8 attention kernel stages in LDS.
@@ -97,6 +130,8 @@ struct AttendLaunch {
   _Float16* part_o;          // [units][n_splits][64][d] partial outputs (normalised)
   float* part_ml;            // [units][n_splits][64][2]  (running max, sum)
   hipEvent_t ev_start, ev_stop;  // recorded around the attention kernel (may be null)
+  const int32_t* bt;         // NULL, or [B][bt_stride] entry block ids (kv0 / kv1 are the pools)
+  int32_t bt_stride, block_rows, pool_blocks;
 };
 
 constexpr int kMaxJobs = 4;
