@@ -338,6 +338,65 @@ def flash_leg(ev, st, steps):
     return out
 
 
+def paged_leg(ev, st, steps, shapes, inps, contiguous_ms):
+    """The decode step over the heterogeneous paged cache: entries in shuffled
+    128-token blocks through block tables, window and compressor tails in
+    per-request rings, compression in the per-sequence decode mode.  Timed at
+    t = L (the step stores the window row only) and at t = L + m - 1 (that
+    token completes a block: the entry is compressed as well, the pessimistic
+    form the headline value uses), with COPIES pool copies rotated like the
+    contiguous caches."""
+    import numpy as np
+    import torch
+    from long_context_attention_09_amd import paged
+    out = {}
+    for shape, inp in zip(shapes, inps):
+        kind = "csa" if shape.csa else "hca"
+        print(f"[bench] paged {kind}: building pools", file=sys.stderr, flush=True)
+        per_req = -(-shape.L // paged.TOKENS_PER_BLOCK) + 1
+        n_blocks = shape.B * per_req
+        alloc = paged.BlockAllocator(n_blocks, order=np.random.default_rng(shape.seed).permutation(n_blocks))
+        cache = paged.PagedCache(shape.B, shape.L + paged.TOKENS_PER_BLOCK, alloc, "cuda")
+        for b in range(shape.B):
+            cache.reserve(b, shape.L + paged.TOKENS_PER_BLOCK)
+        mn = inp["main"]
+        bias = {"main": (mn["ba"], mn.get("bb"))}
+        if shape.csa:
+            bias["idx"] = (inp["idx"]["ba"], inp["idx"]["bb"])
+        done = shape.m - 1                               # t = L + m - 1 completes entry L / m
+        steps_at = {0: [], done: []}
+        layers = []
+        for c in range(COPIES):
+            sfx = "" if c == 0 else f"_{c}"
+            layer = paged.PagedLayer(cache, shape, bias, "cuda")
+            layer.import_contiguous(inp["cache" + sfx], inp.get("keys_codes" + sfx), inp.get("keys_scales" + sfx),
+                                    inp["win"], inp["win_pos0"].tolist())
+            for n, t in layer.main_ring.items():       # raw rows of the newest tokens (synthetic)
+                t.copy_(mn[n][:, :layer.ring_rows])
+            if shape.csa:
+                for n, t in layer.idx_ring.items():
+                    t.copy_(inp["idx"][n][:, :layer.ring_rows])
+            layer.win_raw.copy_(inp["win_raw"])
+            layers.append(layer)
+            for dt in (0, done):
+                seq_pos = inp["q_pos"].view(-1) + dt
+                steps_at[dt].append(paged.PagedDecodeStep(layer, seq_pos, inp["q"], inp["sink"], inp.get("q_idx_codes"),
+                                                          inp.get("q_idx_scales"), inp.get("w")))
+        torch.cuda.synchronize()
+        t_w = time_steps(ev, st, steps, 2, lambda k: steps_at[0][k % COPIES].run(stream=st))
+        t_b = time_steps(ev, st, steps, 2, lambda k: steps_at[done][k % COPIES].run(stream=st))
+        out[kind] = {"ms_window_only": round(t_w, 4), "ms_block_completes": round(t_b, 4),
+                     "vs_contiguous": round(contiguous_ms[kind] / t_b, 4),
+                     "blocks": n_blocks, "entries_per_block": paged.TOKENS_PER_BLOCK // shape.m}
+        del steps_at, layers, cache
+        torch.cuda.empty_cache()
+    out["tokens_per_s"] = round(1.0 / (out["csa"]["ms_block_completes"] / shapes[0].B
+                                       + out["hca"]["ms_block_completes"] / shapes[1].B) * 1e3, 1)
+    out["note"] = ("blocks of 128 raw tokens (32 CSA entries / indexer keys, 1 HCA entry) in shuffled physical "
+                   "order; vs_contiguous = contiguous step time / paged step time, both compressing an entry")
+    return out
+
+
 def prefill_leg(ev, st, steps, warmup, oracle_rows):
     """One 8192-token chunk after 2^20 cached tokens through a CSA and an HCA
     layer, timed with HIP events per operation on the bench stream."""
@@ -555,6 +614,9 @@ def main():
         "csa_ms_per_step": round(t_csa_i, 4), "hca_ms_per_step": round(t_hca_i, 4),
         "tokens_per_s": round(v_inv, 1), "vs_default": round(v_inv / value, 4)}
     del csa_i, hca_i
+    # the same decode over the heterogeneous paged cache (block tables + state rings)
+    line["config"]["paged_kv"] = paged_leg(ev, st, args.steps, (csa_shape, hca_shape), (csa_inp, hca_inp),
+                                           {"csa": t_csa, "hca": t_hca})
     # copy bandwidth measured on this GPU: the roofline against it as well
     bw = copy_bandwidth()
     roofline["measured_copy_GBps"] = round(bw, 1)

@@ -878,8 +878,8 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
 // in the output.  It then emits its selected indices in index order.
 //
 // The candidates are read in one round trip with everything else: the first
-// kSlots = 4096 / n_act slots of every chunk's region are loaded before the
-// counts are known (16 per thread) and masked by the counts afterwards;
+// 4096 / n_chunks slots of every chunk's region are loaded before the counts
+// are known (16 per thread) and masked by the counts afterwards;
 // only a chunk holding more candidates than that needs a second pass over
 // its region.
 constexpr int kOptSlots = 4096;                 // candidate slots loaded up front per workgroup
@@ -889,10 +889,13 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   const int chunk = blockIdx.x;
   const int64_t c0 = (int64_t)chunk * kChunk;
   const int n_chunks_cap = a.n_chunks;          // chunks of the capacity (>= active chunks)
-  // slots per chunk of the up-front load (a power of two, 4 .. 4096)
-  int slots = kOptSlots;
-  while (slots > 4 && slots * n_chunks_cap > kOptSlots) slots >>= 1;
-  const int slot_shift = __builtin_ctz(slots);
+  // slots per chunk of the up-front load: an equal share of the kOptSlots
+  // (4 .. 4096; n_chunks_cap <= kMaxChunks).  Not rounded to a power of two:
+  // a capacity one block past 2^k chunks would otherwise halve every chunk's
+  // share and send full chunks down the slow overflow path.
+  const int slots = kOptSlots / n_chunks_cap;
+  // virtual slot v = slot + chunk * slots (an exact integer quotient: slots is uniform)
+  auto slot_chunk = [&](int v) { return (int)((uint32_t)v / (uint32_t)slots); };
   // ---- one round trip: this thread's 16 scores, the state, every chunk's
   // counts and the leading candidate slots
   const float* sc = score_row(a, q / a.n_qb, q % a.n_qb);
@@ -926,8 +929,9 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
   uint32_t okey[kOptPT];
 #pragma unroll
   for (int j = 0; j < kOptPT; ++j) {
-    const int v = (int)threadIdx.x + 256 * j;   // virtual slot: chunk v >> shift, slot v & (slots-1)
-    const int64_t e = (int64_t)(v >> slot_shift) * kChunk + (v & (slots - 1));
+    const int v = (int)threadIdx.x + 256 * j;   // virtual slot: chunk v / slots, slot v % slots
+    const int vc = slot_chunk(v);
+    const int64_t e = (int64_t)vc * kChunk + (v - vc * slots);
     okey[j] = e < a.n_cap ? ck[e] : 0u;          // (a chunk's candidates never pass the capacity)
   }
   // leave the first-digit histogram zeroed for the next call (collect, its
@@ -976,15 +980,15 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
 #pragma unroll
   for (int j = 0; j < kOptPT; ++j) {
     const int v = (int)threadIdx.x + 256 * j;
-    const int c = v >> slot_shift;
-    valid |= (uint32_t)(c < n_act && (v & (slots - 1)) < lcnt[c < kMaxChunks ? c : 0]) << j;
+    const int c = slot_chunk(v);
+    valid |= (uint32_t)(c < n_act && (v - c * slots) < lcnt[c < kMaxChunks ? c : 0]) << j;
   }
   // every candidate goes through `visit(key, chunk)`: the up-front ones from
   // registers, the rest of an over-full chunk from its region
   auto for_each = [&](auto&& visit) {
 #pragma unroll
     for (int j = 0; j < kOptPT; ++j)
-      if (valid >> j & 1u) visit(okey[j], ((int)threadIdx.x + 256 * j) >> slot_shift);
+      if (valid >> j & 1u) visit(okey[j], slot_chunk((int)threadIdx.x + 256 * j));
     if (overflow) {
       for (int c = 0; c < n_act; ++c) {
         const int n = lcnt[c];

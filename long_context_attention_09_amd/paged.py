@@ -154,6 +154,24 @@ class PagedLayer:
                 t[ar, slot] = idx_rows[n]
         self.win_raw[:, 0] = win_row
 
+    def import_contiguous(self, entries, key_codes=None, key_scales=None, window=None, win_pos0=None):
+        """Copy caches in the contiguous layout into this layer: entries
+        [B, n, 576] (and indexer keys [B, n, 64] / [B, n, 4]) into the pools
+        through the block table (blocks must be reserved), window rows
+        [B, W, 576] holding positions win_pos0[b] .. + W - 1 into the ring."""
+        B, n = entries.shape[:2]
+        for b in range(B):
+            rows = torch.as_tensor(self.cache.entry_rows(b, n, self.per_block), device=entries.device)
+            self.pool.view(-1, ENTRY_BYTES)[rows] = entries[b]
+            if key_codes is not None:
+                self.key_codes.view(-1, key_codes.shape[-1])[rows] = key_codes[b]
+                self.key_scales.view(-1, key_scales.shape[-1])[rows] = key_scales[b]
+        if window is not None:
+            W = window.shape[1]
+            for b in range(B):
+                pos = int(win_pos0[b]) + torch.arange(W, device=window.device)
+                self.win_ring[b, pos % self.s.n_win] = window[b]
+
     # ------------------------------------------------------------ the step's calls
 
     def compress_jobs(self, seq_pos: torch.Tensor):

@@ -229,3 +229,56 @@ def test_paged_incremental_decode(S, T, delays, checks):
     cache.release(0)
     assert alloc.n_free == free0 + blocks_per_req
     assert (cache.block_table[0] == -1).all()
+
+
+@pytest.mark.parametrize("name", ["pro-csa-decode-1m", "flash-hca-decode-1m"])
+def test_paged_full_size_matches_contiguous(name):
+    """At the benchmark shapes (8 x 2^20 tokens CSA, 32 x 2^20 HCA) the paged
+    decode step over shuffled blocks gives the contiguous step's selection,
+    scores, output and LSE bitwise (the step at t = L stores the window row
+    only: token L completes no block)."""
+    K = _K()
+    from long_context_attention_09_amd import paged
+    from long_context_attention_09_amd.layer import LayerStep
+    S = {s.name: s for s in (synth.PRO_CSA_DECODE, synth.FLASH_HCA_DECODE)}[name]
+    _say(f"paged full size {S.name} B={S.B} L={S.L}")
+    inp = synth.quant_decode_inputs(S, device="cuda")
+    ref = LayerStep(S, inp)
+    n_cap = S.L // S.m
+    sc_ref = None
+    if S.csa:
+        sc_ref = torch.empty(S.B, 1, n_cap, device="cuda")
+        K.index_topk(inp["q_idx_codes"], inp["w"], inp["keys_codes"], inp["q_pos"], m=S.m, top_k=S.top_k,
+                     out_idx=torch.empty_like(ref.idx), q1=inp["q_idx_scales"], k1=inp["keys_scales"],
+                     fmt=K.FMT_MXFP4, out_score=sc_ref)
+    ref.run(entries=False)
+    torch.cuda.synchronize()
+    per_req = -(-S.L // paged.TOKENS_PER_BLOCK) + 1
+    n_blocks = S.B * per_req
+    alloc = paged.BlockAllocator(n_blocks, order=np.random.default_rng(S.seed).permutation(n_blocks))
+    cache = paged.PagedCache(S.B, S.L + paged.TOKENS_PER_BLOCK, alloc, "cuda")
+    for b in range(S.B):
+        cache.reserve(b, S.L + 1)
+    mn = inp["main"]
+    bias = {"main": (mn["ba"], mn.get("bb"))}
+    if S.csa:
+        bias["idx"] = (inp["idx"]["ba"], inp["idx"]["bb"])
+    layer = paged.PagedLayer(cache, S, bias, "cuda")
+    layer.import_contiguous(inp["cache"], inp.get("keys_codes"), inp.get("keys_scales"), inp["win"],
+                            inp["win_pos0"].tolist())
+    layer.win_raw.copy_(inp["win_raw"])
+    seq_pos = inp["q_pos"].view(-1).clone()
+    step = paged.PagedDecodeStep(layer, seq_pos, inp["q"], inp["sink"], inp.get("q_idx_codes"),
+                                 inp.get("q_idx_scales"), inp.get("w"))
+    step.run()
+    torch.cuda.synchronize()
+    if S.csa:
+        sc = torch.empty(S.B, 1, cache.max_blocks * layer.per_block, device="cuda")
+        K.index_topk(inp["q_idx_codes"], inp["w"], layer.key_codes, step.q_pos, m=S.m, top_k=S.top_k,
+                     out_idx=torch.empty_like(step.idx), q1=inp["q_idx_scales"], k1=layer.key_scales,
+                     fmt=K.FMT_MXFP4, block_table=cache.block_table, out_score=sc)
+        torch.cuda.synchronize()
+        assert torch.equal(sc[:, :, :n_cap].view(torch.int32), sc_ref.view(torch.int32))
+        assert torch.equal(step.idx, ref.idx)
+    assert torch.equal(step.out.view(torch.int16), ref.out.view(torch.int16))
+    assert torch.equal(step.lse.view(torch.int32), ref.lse.view(torch.int32))
