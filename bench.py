@@ -56,12 +56,12 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "cb8dcc4f50a3f60620c8821f9799d365777e8127fffd38b48f6114930b5c21a9",
-        "fetch_kib": 83362.8, "write_kib": 16512.0},
+        "sha256": "63ebc3fb71249ffcd58e973e4441081a86198f21b119d92eec8b8873f5e25fa9",
+        "fetch_kib": 83404.1, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "c3ed423c0ab27ac553428022494903b77456bf9d186f6457b46290f78a1bb369",
-        "fetch_kib": 69825.7, "write_kib": 8517.0},
+        "sha256": "92a4626965e139ac2dee18da7c82c1d44cf090723b85d7a62d15bc95ee13b4d4",
+        "fetch_kib": 69865.6, "write_kib": 8517.1},
 }
 
 
@@ -489,6 +489,8 @@ def main():
                     help="query rows per layer the oracle is timed on (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the 1 GiB elementwise copy used to scale HBM counters")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline decode steps (no side measurements): for profilers")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -585,6 +587,9 @@ def main():
         },
         "roofline": roofline,
     }
+    if args.headline_only:
+        print(json.dumps(line), flush=True)
+        return
     # the same decode step with the newest entries' compression amortised over
     # the m (CSA) and m' (HCA) tokens a block takes to complete: steps that
     # only store the window row, plus 1/m of the entry compression
