@@ -178,18 +178,22 @@ def test_paged_incremental_decode(S, T, delays, checks):
         layer.write_token(seq_pos, {n: d["main"][n][ar, seq_pos] for n in layer.main_ring},
                           {n: d["idx"][n][ar, seq_pos] for n in layer.idx_ring} if S.csa else None,
                           d["win_raw"][ar, seq_pos])
-        step.compress()
         if k not in checks:
+            step.compress()
             continue
-        # the step's own index + attend at these positions
+        # the whole step at these positions: the completed entries compressed on
+        # a second stream while the window row, index and attention run
+        step.run()
         sc = None
         if S.csa:
             n_cap = cache.max_blocks * layer.per_block
             sc = torch.empty(S.B, 1, n_cap, device="cuda")
+            idx2 = torch.empty_like(step.idx)
             K.index_topk(d["q_idx_codes"], d["w"], layer.key_codes, step.q_pos, m=S.m, top_k=S.top_k,
-                         out_idx=step.idx, q1=d["q_idx_scales"], k1=layer.key_scales, fmt=K.FMT_MXFP4,
+                         out_idx=idx2, q1=d["q_idx_scales"], k1=layer.key_scales, fmt=K.FMT_MXFP4,
                          flags=flags_i, block_table=cache.block_table, out_score=sc)
-        step.attend()
+            torch.cuda.synchronize()
+            assert torch.equal(idx2, step.idx)
         torch.cuda.synchronize()
         for b in range(S.B):
             t = pos[b]

@@ -463,6 +463,53 @@ def test_topk_ties_and_empty():
         assert np.array_equal(got, OC.topk(rs, k)), f"b={b}"
 
 
+@pytest.mark.parametrize("with_scores", [False, True], ids=["list", "threshold-emit"])
+def test_topk_ties_query_blocks(with_scores):
+    """The same exact-tie rule on the query-block paths (70 queries per
+    sequence: the 32-head MXFP4 scorer with the split linear term, then the
+    list pass without caller-kept scores, threshold + emit with them): keys
+    drawn from 4 code patterns give 4 distinct scores per query, so most of
+    the k-th bucket is ties that must go to the lower index; queries that see
+    every entry, none, or fewer than k."""
+    K = _K()
+    B, n_q, n_cap, H_I = 2, 70, 5000, 32
+    rng = np.random.default_rng(1)
+    pat = rng.integers(0, 256, size=(4, 64), dtype=np.uint8)
+    which = rng.integers(0, 4, size=(B, n_cap))
+    kc = pat[which]
+    ks = np.full((B, n_cap, 4), 127, np.uint8)
+    qc = rng.integers(0, 256, size=(B, n_q, H_I, 64), dtype=np.uint8)
+    qs = np.full((B, n_q, H_I, 4), 127, np.uint8)
+    w = rng.normal(size=(B, n_q, H_I)).astype(np.float32)          # signed weights
+    pos = rng.integers(0, 4 * n_cap + 8, size=(B, n_q)).astype(np.int64)
+    pos[:, 0] = 4 * n_cap + 3                                      # sees every entry
+    pos[:, 1] = 2                                                  # sees none
+    pos[:, 2] = 4 * 600 + 1                                        # fewer than k
+    k = 1000
+    idx = torch.empty(B, n_q, k, dtype=torch.int32, device="cuda")
+    score = torch.empty(B, n_q, n_cap, device="cuda") if with_scores else None
+    _say(f"top-k ties, query blocks, scores kept: {with_scores}")
+    K.index_topk(torch.from_numpy(qc).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(kc).cuda(),
+                 torch.from_numpy(pos).cuda(), m=4, top_k=k, out_idx=idx, q1=torch.from_numpy(qs).cuda(),
+                 k1=torch.from_numpy(ks).cuda(), out_score=score, fmt=K.FMT_MXFP4)
+    torch.cuda.synchronize()
+    got_all = idx.cpu().numpy()
+    keys_all = [F.decode_mxfp4(kc[b], ks[b]) for b in range(B)]
+    n_ties = 0
+    for b in range(B):
+        for r in range(n_q):
+            n_vis = OC.visible_entries(int(pos[b, r]), 4, n_cap)
+            qI = F.decode_mxfp4(qc[b, r], qs[b, r])
+            rs = OC.index_scores(qI, w[b, r], keys_all[b][:n_vis], n_vis)
+            want = OC.topk(rs, k)
+            assert np.array_equal(got_all[b, r], want), f"b={b} r={r} n_vis={n_vis}"
+            if n_vis > k:
+                s_k = np.sort(rs)[::-1][k - 1]
+                n_ties += int((rs == s_k).sum())
+    assert n_ties > 1000                    # the k-th score is shared by many keys
+    _say(f"  keys tied with the k-th score, all queries: {n_ties}")
+
+
 def test_invalid_arguments_are_rejected():
     K = _K()
     from long_context_attention_09_amd._lib import CsaError
