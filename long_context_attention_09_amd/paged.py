@@ -199,20 +199,48 @@ class PagedLayer:
                                     out_ring=s.n_win, seq_pos=seq_pos))
         return jobs
 
+    def chunk_jobs(self, main_streams, idx_streams, pos0):
+        """csa_compress jobs of a prefill chunk: every entry (and indexer key)
+        that rows pos0 .. of the given linear streams ([B, rows, D]; with
+        overlap the first m rows are the previous block's tail) complete, into
+        the pools through the block table (the blocks must be reserved)."""
+        s = self.s
+        bt = self.cache.block_table
+        nope, rope = K.split_main(self.pool)
+        mn = main_streams
+        ba, bb = self.bias["main"]
+        jobs = [K.compress_args(mn["ca"], gate_a=mn["za"], bias_a=ba, kv_b=mn.get("cb"), gate_b=mn.get("zb"),
+                                bias_b=bb, m=s.m, pos0=pos0, out0=nope, out1=rope, d_rope=s.d_r,
+                                rope_theta=s.theta, do_norm=True, out_fmt=K.FMT_FP8_BF16, block_table=bt)]
+        if s.csa:
+            ix = idx_streams
+            ia, ib = self.bias["idx"]
+            jobs.append(K.compress_args(ix["ca"], gate_a=ix["za"], bias_a=ia, kv_b=ix["cb"], gate_b=ix["zb"],
+                                        bias_b=ib, m=s.m, pos0=pos0, out0=self.key_codes, out1=self.key_scales,
+                                        d_rope=0, do_norm=False, out_fmt=K.FMT_MXFP4, block_table=bt))
+        return jobs
+
     def index_args(self, q_pos, q_codes, q_scales, w, out_idx, out_score=None, flags=0):
         s = self.s
         return K.index_args(q_codes, w, self.key_codes, q_pos, m=s.m, top_k=s.top_k, out_idx=out_idx,
                             q1=q_scales, k1=self.key_scales, fmt=K.FMT_MXFP4, flags=flags,
                             block_table=self.cache.block_table, out_score=out_score)
 
-    def attend_args(self, q, q_pos, sink, out, idx=None, out_lse=None, flags=K.ATTEND_NORM_Q):
+    def attend_args(self, q, q_pos, sink, out, idx=None, out_lse=None, flags=K.ATTEND_NORM_Q, window=None,
+                    win_pos0=None):
+        """Attention over the paged entries and the window ring, or (prefill:
+        the chunk's queries see more window rows than the ring holds) over a
+        linear window buffer [B, W, 576] whose row 0 holds position win_pos0[b]."""
         s = self.s
         nope, rope = K.split_main(self.pool)
-        wn, wr = K.split_main(self.win_ring)
-        return K.attend_args(q, q_pos, nope, wn, None, sink, out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
+        if window is None:
+            wn, wr = K.split_main(self.win_ring)
+            flags |= K.ATTEND_WIN_RING
+        else:
+            wn, wr = K.split_main(window)
+        return K.attend_args(q, q_pos, nope, wn, win_pos0, sink, out, m=s.m, n_win=s.n_win, kv1=rope, win1=wr,
                              idx=idx, out_lse=out_lse, d_rope=s.d_r, rope_theta=s.theta,
-                             fmt=K.FMT_FP8_BF16, flags=flags | K.ATTEND_WIN_RING,
-                             block_table=self.cache.block_table)
+                             fmt=K.FMT_FP8_BF16, flags=flags, block_table=self.cache.block_table)
 
 
 class PagedDecodeStep:

@@ -14,6 +14,8 @@ and the newest request's results must match the fp64 oracle.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import numpy as np
 import pytest
 import torch
@@ -286,3 +288,61 @@ def test_paged_full_size_matches_contiguous(name):
         assert torch.equal(step.idx, ref.idx)
     assert torch.equal(step.out.view(torch.int16), ref.out.view(torch.int16))
     assert torch.equal(step.lse.view(torch.int32), ref.lse.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["pro-csa-prefill-8k-after-1m", "pro-hca-prefill-8k-after-1m"])
+def test_paged_prefill_matches_contiguous(name):
+    """A prefill chunk (300 queries after 4096 cached tokens) through the paged
+    layout: the chunk's entries and keys compressed into shuffled blocks, the
+    query-block indexer and the attention reading through the block table (the
+    chunk's window in a linear buffer), bitwise equal to the contiguous chunk.
+    Both sides run in the batch-invariant mode, whose splits depend on each
+    query's list alone (the paged capacity is a whole number of blocks)."""
+    K = _K()
+    from long_context_attention_09_amd import paged
+    from long_context_attention_09_amd.layer import LayerStep
+    S = {s.name: s for s in (synth.PRO_CSA_PREFILL, synth.PRO_HCA_PREFILL)}[name].replace(L=4096, n_q=300)
+    _say(f"paged prefill {S.name} L={S.L} n_q={S.n_q}")
+    d = _dev(synth.quant_prefill_inputs(S))
+    ref = LayerStep(S, d, prefill=True, batch_invariant=True)
+    ref.run()
+    torch.cuda.synchronize()
+    T = S.L + S.n_q
+    per_req = -(-T // paged.TOKENS_PER_BLOCK) + 1
+    n_blocks = S.B * per_req + 3
+    alloc = paged.BlockAllocator(n_blocks, order=np.random.default_rng(S.seed).permutation(n_blocks))
+    cache = paged.PagedCache(S.B, T + paged.TOKENS_PER_BLOCK, alloc, "cuda")
+    for b in range(S.B):
+        cache.reserve(b, T)
+    bias = {"main": (d["main"]["ba"], d["main"].get("bb"))}
+    if S.csa:
+        bias["idx"] = (d["idx"]["ba"], d["idx"]["bb"])
+    layer = paged.PagedLayer(cache, S, bias, "cuda")
+    layer.import_contiguous(d["cache_old"], d.get("keys_codes_old"), d.get("keys_scales_old"))
+    tail = S.m if S.overlap else 0
+    jobs = layer.chunk_jobs(d["main"], d.get("idx"), S.L - tail)
+    win = torch.zeros(S.B, S.n_win - 1 + S.n_q, 576, dtype=torch.uint8, device="cuda")
+    win[:, :S.n_win - 1] = d["win_old"]
+    wn, wr = K.split_main(win)
+    jobs.append(K.compress_args(d["win_raw"], m=1, pos0=S.L, out0=wn, out1=wr, d_rope=S.d_r, rope_theta=S.theta,
+                                do_norm=True, out_fmt=K.FMT_FP8_BF16, out_row0=S.L - S.n_win + 1))
+    K.compress_batch(jobs)
+    idx = None
+    if S.csa:
+        idx = torch.empty(S.B, S.n_q, S.top_k, dtype=torch.int32, device="cuda")
+        K.index_topk(d["q_idx_codes"], d["w"], layer.key_codes, d["q_pos"], m=S.m, top_k=S.top_k, out_idx=idx,
+                     q1=d["q_idx_scales"], k1=layer.key_scales, fmt=K.FMT_MXFP4, flags=K.INDEX_BATCH_INVARIANT,
+                     block_table=cache.block_table)
+    out = torch.empty_like(ref.out)
+    a = layer.attend_args(d["q"], d["q_pos"], d["sink"], out, idx=idx,
+                          flags=K.ATTEND_NORM_Q | K.ATTEND_BATCH_INVARIANT, window=win, win_pos0=d["win_pos0"])
+    ws, n = K._workspace(K.OP_ATTEND if S.csa else K.OP_HCA_ATTEND, a, None)
+    fn = K.load().csa_attend if S.csa else K.load().hca_attend
+    K._check(fn(C.byref(a), K._ptr(ws), n, K._stream()), "attend")
+    torch.cuda.synchronize()
+    n_e = T // S.m
+    rows = torch.as_tensor(cache.entry_rows(0, n_e, layer.per_block), device="cuda")
+    assert torch.equal(layer.pool.view(-1, 576)[rows], ref.caches[0][0, :n_e]), "chunk entries"
+    if S.csa:
+        assert torch.equal(idx, ref.idx), "selection"
+    assert torch.equal(out.view(torch.int16), ref.out.view(torch.int16)), "attention"
