@@ -491,6 +491,8 @@ def main():
                     help="run only the 1 GiB elementwise copy used to scale HBM counters")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline decode steps (no side measurements): for profilers")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunk and print its measurement: for profilers")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -509,6 +511,11 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     K.load()
+    if args.prefill_only:
+        ev = HipEvents()
+        st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        print(json.dumps({"prefill": prefill_leg(ev, st, max(args.prefill_steps, 1), 1, 0)}), flush=True)
+        return
     dev = "cuda"
     csa_shape, hca_shape = synth.PRO_CSA_DECODE, synth.FLASH_HCA_DECODE
     print("[bench] generating inputs", file=sys.stderr, flush=True)
