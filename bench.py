@@ -11,7 +11,7 @@ blocks, window store, index + top-k for CSA, attention).  Per-token cost of
 the pair is t_csa / 8 + t_hca / 32, so the reported value is
 1 / (t_csa / 8 + t_hca / 32) decode tokens per second per layer pair.
 
-Caches are kept in three copies that consecutive steps rotate through, so the
+Caches are kept in four copies that consecutive steps rotate through, so the
 256 MB Infinity Cache cannot serve a step from the previous step's reads (each
 layer of a real model has caches of its own).  All inputs are resident in HBM
 before the timed region.
@@ -40,7 +40,7 @@ METRIC = "decode tokens/s per layer at 1M ctx (CSA+HCA) and % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MXFP4_PEAK_TFLOPS = 10100.0     # dense MFMA, published
 BF16_PEAK_TFLOPS = 2500.0       # dense MFMA, published
-COPIES = 3
+COPIES = 4
 EVENT_DISABLE_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence
 CSRC = os.path.join(ROOT, "long_context_attention_09_amd", "csrc")
 

@@ -74,3 +74,33 @@ def test_noalloc_decode_batch_and_limit():
         K.index_topk_noalloc(big["q0"], big["w"], big["k0"], big["q_pos"], m=SHAPE.m, top_k=1024, out_idx=out,
                              q1=big["q1"], k1=big["k1"], fmt=K.FMT_MXFP4)
     assert e.value.status == K.CSA_ESCRATCH
+
+
+def test_noalloc_paged_keys():
+    """Paged indexer keys (blocks of 32 keys in shuffled order, read through a
+    block table) through both entry points: the same selection as the
+    contiguous keys."""
+    import numpy as np
+    K = _K()
+    B, n_q, L, top_k = 2, 3, 1 << 16, 512
+    print(f"[gpu] noalloc paged keys B={B} n_q={n_q} L={L}", flush=True)
+    inp = _inputs(B, n_q, L, "paged")
+    n_cap = inp["k0"].shape[1]
+    per = -(-n_cap // 32)
+    P = B * per + 5
+    order = torch.as_tensor(np.random.default_rng(3).permutation(P)[:B * per].astype(np.int32),
+                            device="cuda").view(B, per)
+    kc = torch.zeros(P, 32, 64, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(P, 32, 4, dtype=torch.uint8, device="cuda")
+    for b in range(B):
+        rows = (order[b].long().view(-1, 1) * 32 + torch.arange(32, device="cuda")).view(-1)[:n_cap]
+        kc.view(-1, 64)[rows] = inp["k0"][b]
+        ks.view(-1, 4)[rows] = inp["k1"][b]
+    ref, _ = _both(K, inp, top_k)
+    kw = dict(m=SHAPE.m, top_k=top_k, q1=inp["q1"], k1=ks, fmt=K.FMT_MXFP4, block_table=order.contiguous())
+    a = torch.full_like(ref, -3)
+    c = torch.full_like(ref, -5)
+    K.index_topk(inp["q0"], inp["w"], kc, inp["q_pos"], out_idx=a, **kw)
+    K.index_topk_noalloc(inp["q0"], inp["w"], kc, inp["q_pos"], out_idx=c, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, ref) and torch.equal(c, ref)
