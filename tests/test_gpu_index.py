@@ -94,3 +94,43 @@ def test_index_signed_weights_spread_exponents(n_q, B, L):
             worst = max(worst, float(err.max() / abs(s_k)))
             check_topk(idx_s[b, r], ref, s.top_k)
     print(f"[gpu]   worst score error / |s_k| = {worst:.3e}", flush=True)
+
+
+def test_index_maximum_capacity():
+    """The largest capacity the selector takes (n_cap = 4194304 keys, 1024
+    chunks of 4096): the selection is the exact top-k of the GPU's own stored
+    scores (ties to the lower index, checked over all 4M scores), those
+    scores match the oracle on the selected keys and on 4096 random others
+    (the bound of the adversarial test), and keys past the visible range
+    score -inf."""
+    K = _K()
+    s = synth.PRO_CSA_DECODE.replace(name="index-max", B=1)
+    n_cap, top_k = 1 << 22, 1024
+    print(f"[gpu] index at maximum capacity n_cap={n_cap}", flush=True)
+    kc, ks = synth.mxfp4_codes(s, "keys", n_cap, s.d_I)
+    qc, qs = synth.mxfp4_codes(s, "q", s.H_I, s.d_I)
+    w = synth.head_weights(s, (1, 1, s.H_I))
+    n_vis = n_cap - 1000                       # the last 1000 keys are not visible yet
+    q_pos = torch.tensor([[4 * n_vis + 2]], dtype=torch.int64)
+    idx = torch.empty(1, 1, top_k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(1, 1, n_cap, device="cuda")
+    K.index_topk(qc.view(1, 1, s.H_I, -1).cuda(), w.cuda(), kc.view(1, n_cap, -1).cuda(), q_pos.cuda(), m=4,
+                 top_k=top_k, out_idx=idx, q1=qs.view(1, 1, s.H_I, -1).cuda(), k1=ks.view(1, n_cap, -1).cuda(),
+                 out_score=sc, fmt=K.FMT_MXFP4)
+    torch.cuda.synchronize()
+    got = idx[0, 0].cpu().numpy()
+    g = sc[0, 0].cpu().numpy()
+    assert np.all(np.isneginf(g[n_vis:])) and np.all(np.isfinite(g[:n_vis]))
+    # exact top-k of the stored scores: k largest by (score desc, index asc), ascending output
+    order = np.lexsort((np.arange(n_vis), -g[:n_vis].astype(np.float64)))
+    assert np.array_equal(got, np.sort(order[:top_k]))
+    # sampled scores against the oracle
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([got, rng.integers(0, n_vis, 4096)]))
+    keys = F.decode_mxfp4(kc.numpy()[sample], ks.numpy()[sample])
+    qI = F.decode_mxfp4(qc.numpy(), qs.numpy())
+    wv = w[0, 0].numpy().astype(np.float64)
+    ref = OC.index_scores(qI, wv, keys, len(sample))
+    mag = (np.abs(keys) @ np.abs(qI).T) @ np.abs(wv)
+    err = np.abs(g[sample] - ref)
+    assert np.all(err <= 2.0 ** -17 * mag), float((err / np.maximum(mag, 1e-300)).max())
