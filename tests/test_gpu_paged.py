@@ -346,3 +346,65 @@ def test_paged_prefill_matches_contiguous(name):
     if S.csa:
         assert torch.equal(idx, ref.idx), "selection"
     assert torch.equal(out.view(torch.int16), ref.out.view(torch.int16)), "attention"
+
+
+def _attend_oracle(S, q, t, entries_u8, sel, win_u8, win_pos0, sink, dense):
+    entries = P.decode_entry_bytes(entries_u8, S.d_nope)
+    window = P.decode_entry_bytes(win_u8, S.d_nope)
+    args = (q, t, entries) + (() if dense else (sel,)) + (window, win_pos0, S.n_win, sink, S.theta, S.d_r, S.m)
+    return (OC.hca_attend if dense else OC.csa_attend)(*args)[0]
+
+
+def test_attend_long_lists_split_by_the_stage():
+    """Lists longer than the 2048 rows a split stages: a CSA selection of 6000
+    indices (with -1 and out-of-range ones mixed in) and paged HCA lists at
+    B = 256 (one split per query would hold 68 tiles, over the 64-tile stage,
+    so the paged plan splits them): both against the oracle."""
+    K = _K()
+    from long_context_attention_09_amd import paged
+    # CSA, top-k 6000 over 16384 entries
+    S = synth.PRO_CSA_DECODE.replace(name="long-csa", B=2, L=1 << 16, top_k=6000, H=64)
+    _say(f"long CSA selection top_k={S.top_k}")
+    d = synth.quant_decode_inputs(S, device="cuda")
+    n_e = S.L // S.m
+    g = torch.Generator(device="cuda").manual_seed(11)
+    idx = torch.stack([torch.randperm(n_e, generator=g, device="cuda")[:S.top_k].sort().values
+                       for _ in range(S.B)]).to(torch.int32).view(S.B, 1, S.top_k)
+    idx[0, 0, 5:40] = -1
+    idx[1, 0, -30:] = n_e + 7                     # outside the visible range: skipped
+    out = torch.empty_like(d["q"])
+    nope, rope = K.split_main(d["cache"])
+    wn, wr = K.split_main(d["win"])
+    K.attend(d["q"], d["q_pos"], nope, wn, d["win_pos0"], d["sink"], out, m=S.m, n_win=S.n_win, kv1=rope,
+             win1=wr, idx=idx)
+    torch.cuda.synchronize()
+    for b in range(S.B):
+        o = _attend_oracle(S, bf16_to_np(d["q"][b, 0]), S.L, d["cache"][b].cpu().numpy(),
+                           idx[b, 0].cpu().numpy(), d["win"][b].cpu().numpy(), S.L - S.n_win + 1,
+                           d["sink"].double().cpu().numpy(), dense=False)
+        err = np.abs(bf16_to_np(out[b, 0]) - o).max()
+        assert err <= TOL_QUANT, (b, err)
+    # paged HCA at B = 256
+    S = synth.FLASH_HCA_DECODE.replace(name="long-hca", B=256, L=1 << 18)
+    _say(f"paged HCA B={S.B} L={S.L}")
+    d = synth.quant_decode_inputs(S, device="cuda")
+    per_req = -(-S.L // paged.TOKENS_PER_BLOCK) + 1
+    n_blocks = S.B * per_req
+    alloc = paged.BlockAllocator(n_blocks, order=np.random.default_rng(5).permutation(n_blocks))
+    cache = paged.PagedCache(S.B, S.L + paged.TOKENS_PER_BLOCK, alloc, "cuda")
+    for b in range(S.B):
+        cache.reserve(b, S.L + 1)
+    layer = paged.PagedLayer(cache, S, {"main": (d["main"]["ba"], None)}, "cuda")
+    layer.import_contiguous(d["cache"])
+    out = torch.empty_like(d["q"])
+    a = layer.attend_args(d["q"], d["q_pos"], d["sink"], out, window=d["win"], win_pos0=d["win_pos0"])
+    ws, n = K._workspace(K.OP_HCA_ATTEND, a, None)
+    assert n >= S.B * 2 * 64 * 512 * 2           # more than one split per query
+    K._check(K.load().hca_attend(C.byref(a), K._ptr(ws), n, K._stream()), "hca_attend")
+    torch.cuda.synchronize()
+    for b in (0, 131, 255):
+        o = _attend_oracle(S, bf16_to_np(d["q"][b, 0]), S.L, d["cache"][b].cpu().numpy(), None,
+                           d["win"][b].cpu().numpy(), S.L - S.n_win + 1, d["sink"].double().cpu().numpy(),
+                           dense=True)
+        err = np.abs(bf16_to_np(out[b, 0]) - o).max()
+        assert err <= TOL_QUANT, (b, err)
