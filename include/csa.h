@@ -24,7 +24,7 @@
  *     failure nothing is launched and a negative status is returned.
  *   - Status: CSA_OK (0); CSA_EINVAL (-1) null pointer, misaligned pointer or
  *     inconsistent shape; CSA_EUNSUPPORTED (-2) a shape or format combination
- *     this build has no kernel for; CSA_EHIP (-3) a launch error reported by
+ *     this library has no kernel for; CSA_EHIP (-3) a launch error reported by
  *     the HIP runtime; CSA_EWORKSPACE (-4) workspace missing or too small;
  *     CSA_ESCRATCH (-5) a problem too large for csa_index_topk_noalloc.
  *   - Deterministic: for a fixed input and shape the results are bitwise

@@ -74,8 +74,8 @@ def check_mxfp4_codes(gpu_codes, gpu_scales, exact, rel=REL_CODE):
 
 
 def check_topk(gpu_idx, oracle_scores, k, tie_rel=None):
-    """North-star rule for a top-k set against the oracle's fp64 scores (tie
-    window tie_rel, default the benchmark spec's 1e-3 of the k-th score)."""
+    """The top-k rule for a GPU selection against the oracle's fp64 scores: tie
+    window tie_rel, by default 1e-3 of the k-th score."""
     tie = TIE_REL if tie_rel is None else tie_rel
     gpu_idx = np.asarray(gpu_idx)
     n = oracle_scores.shape[0]
