@@ -52,10 +52,10 @@
 
 namespace csa {
 
-constexpr int kTilesPerWave = 16;                    // 16 keys per tile: 256 keys per wave
+constexpr int kTilesPerWave = 32;                    // 16 keys per tile: 512 keys per wave
 constexpr int kRing = 8;                             // tiles of keys in flight per wave
-constexpr int kWaveKeys = kTilesPerWave * 16;        // 256
-constexpr int kKeysPerWG = 4 * kWaveKeys;            // 1024
+constexpr int kWaveKeys = kTilesPerWave * 16;        // 512
+constexpr int kKeysPerWG = 4 * kWaveKeys;            // 2048
 constexpr int kChunk = 4096;                         // scores per workgroup in collect / write
 constexpr int kBins1 = 4096;                         // 12-bit first digit
 constexpr int kShift1 = 20;
@@ -183,7 +183,8 @@ __device__ __forceinline__ void my_buckets(const uint32_t* cnt, uint32_t (&v)[PE
 // ------------------------------------------------------------------ MXFP4 indexer
 
 template <int QT, int NHG>
-__global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 1)))
+index_mxfp4_kernel(IndexLaunch a) {
   __shared__ uint32_t lhist[QT][kBins1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -194,18 +195,6 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   constexpr int nhg = NHG;       // head groups of 16 (H_I / 16)
 
   for (int i = threadIdx.x; i < QT * kBins1; i += 256) (&lhist[0][0])[i] = 0;
-
-  int nvis[QT];
-  int nvis_max = 0;
-#pragma unroll
-  for (int qi = 0; qi < QT; ++qi) {
-    // the counts are uniform over the workgroup: keep them in scalar registers
-    nvis[qi] = __builtin_amdgcn_readfirstlane((r0 + qi < a.n_qb) ? query_n_vis(a, b, r0 + qi) : 0);
-    nvis_max = nvis[qi] > nvis_max ? nvis[qi] : nvis_max;
-  }
-  // (the maximum may be formed with a vector instruction: make it a scalar
-  // again, or every buffer access below turns into a per-lane loop)
-  nvis_max = __builtin_amdgcn_readfirstlane(nvis_max);
   __syncthreads();
 
   // Key groups of 64 (four 16-key tiles) are dealt to the waves of the
@@ -215,7 +204,6 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   const int NW = 4 * (int)gridDim.x;                         // waves per sequence
   const int W = (int)blockIdx.x * 4 + wave;
   constexpr int kGroups = kTilesPerWave / 4;                 // groups per wave
-  const int ngv = (nvis_max + 63) / 64;                      // groups with a visible key
   // Paged keys: k0 / k1 are the pools and the wave's 2 kGroups blocks (two
   // per 64-key group) are looked up once, lane l holding slot l; contiguous
   // keys start at the sequence's row 0.
@@ -223,11 +211,15 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
   const uint8_t* kc = (const uint8_t*)a.k0 + (paged ? 0 : (int64_t)b * a.n_cap * 64);
   const uint32_t* ks = (const uint32_t*)a.k1 + (paged ? 0 : (int64_t)b * a.n_cap);
 
-  if (W < ngv) {
+  // Waves with a key of the capacity request their first ring of keys before
+  // the visible counts arrive (the counts only set the loop's trip count and
+  // which scores are kept); a wave with no key of the capacity has nothing to
+  // write.
+  if (W < (a.n_cap + 63) / 64) {
     int blk_v = -1;
     if (paged && lane < 2 * kGroups) {
       const int lb = 2 * (W + (lane >> 1) * NW) + (lane & 1);
-      if (lb * 32 < nvis_max) blk_v = a.bt[(int64_t)b * a.bt_stride + lb];
+      if (lb * 32 < a.n_cap) blk_v = a.bt[(int64_t)b * a.bt_stride + lb];
     }
     // query operands: head (16 hg + col), bytes 16g .. 16g+15 of its 64-byte row
     i32x4 qa[QT][4];
@@ -255,7 +247,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // count of loads in flight exact across iterations, and the ring stays
     // full instead of draining once per round.  (Byte offsets fit 32 bits:
     // n_cap <= 4M keys.)
-    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)nvis_max;   // key rows in range
+    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)a.n_cap;   // key rows in range
     const __amdgpu_buffer_rsrc_t rc =
         __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)(n_rec * 64u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs =
@@ -275,18 +267,23 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
     // (the byte of its k-group g is the operand's block scale).  Scores move
     // four tiles (64 keys) at a time, as one 256-byte store per wave: lane
     // (g, col) keeps the score of tile g of the group.
-    const uint32_t off_s = (uint32_t)W * 256u + (uint32_t)col * 4u;
+    // Scale words: lane l loads the word of key l of a 64-key group with the
+    // group's first tile (one 4-byte load per lane and group, against one per
+    // lane and tile when every lane fetched its own key's word: four lanes
+    // share each word), and the words of the four tiles' keys reach the lanes
+    // that use them by lane permutes.
     const uint32_t off_o = (uint32_t)W * 256u + (uint32_t)lane * 4u;
-    // ring of kRing tiles in flight (16 B of codes and a scale word per lane
-    // and tile); tile t + kRing is requested as soon as tile t is scored
-    // (tiles past the wave's keys read as zeros without touching memory)
+    // ring of kRing tiles in flight (16 B of codes per lane and tile, a scale
+    // word per lane and group); tile t + kRing is requested as soon as tile t
+    // is scored (tiles past the wave's keys read as zeros without touching
+    // memory)
     static_assert(kRing % 4 == 0, "tiles move in groups of four");
     i32x4 kbuf[kRing];
-    uint32_t kscw[kRing];
-    // tile t of the wave: tile t % 4 of its group t / 4
+    uint32_t kscg[kRing / 4];
+    // tile t of the wave (t % 4 == u % 4): tile t % 4 of its group t / 4
     auto fetch = [&](int t, int u) {
-      const uint32_t j = (uint32_t)t >> 2, q = (uint32_t)t & 3u;
-      uint32_t oc = off_c + j * gs_c + q * 1024u, os = off_s + j * gs_s + q * 64u;
+      const uint32_t j = (uint32_t)t >> 2, q = (uint32_t)u & 3u;
+      uint32_t oc = off_c + j * gs_c + q * 1024u, os = off_o + j * gs_s;
       if (paged) {
         // tile q of group j: rows 16 (q % 2) .. +15 of the group's block q / 2;
         // an unallocated block (or a tile past the wave's) reads zeros
@@ -295,10 +292,17 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         const bool ok = blk >= 0 && blk < a.pool_blocks;
         const uint32_t row = 16u * (q & 1u) + (uint32_t)col;
         oc = ok ? (uint32_t)blk * 2048u + row * 64u + (uint32_t)g * 16u : 0xffffff00u;
-        os = ok ? (uint32_t)blk * 128u + row * 4u : 0xffffff00u;
+        if (q == 0) {
+          // key l of the group: row l % 32 of the group's block l / 32
+          const int s0 = 2 * (int)j;
+          const int b0 = s0 < 2 * kGroups ? __builtin_amdgcn_readlane(blk_v, s0) : -1;
+          const int b1 = s0 + 1 < 2 * kGroups ? __builtin_amdgcn_readlane(blk_v, s0 + 1) : -1;
+          const int bl = lane < 32 ? b0 : b1;
+          os = bl >= 0 && bl < a.pool_blocks ? (uint32_t)bl * 128u + (uint32_t)(lane & 31) * 4u : 0xffffff00u;
+        }
       }
       kbuf[u] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, 0));
-      kscw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+      if (q == 0) kscg[u >> 2] = __builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
     };
     // issue the first round in ring order (the loop consumes it in that order)
 #pragma unroll
@@ -306,17 +310,35 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
       fetch(u, u);
       __builtin_amdgcn_sched_barrier(0);
     }
+    int nvis[QT];
+    int nvis_max = 0;
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      // the counts are uniform over the workgroup: keep them in scalar registers
+      nvis[qi] = __builtin_amdgcn_readfirstlane((r0 + qi < a.n_qb) ? query_n_vis(a, b, r0 + qi) : 0);
+      nvis_max = nvis[qi] > nvis_max ? nvis[qi] : nvis_max;
+    }
+    // (the maximum may be formed with a vector instruction: make it a scalar
+    // again, or the loop bound below turns into a per-lane one)
+    nvis_max = __builtin_amdgcn_readfirstlane(nvis_max);
+    const int ngv = (nvis_max + 63) / 64;                    // groups with a visible key
     // rounds over the wave's groups that hold a visible key
-    int vgroups = (ngv - W + NW - 1) / NW;
+    int vgroups = W < ngv ? (ngv - W + NW - 1) / NW : 0;
     vgroups = vgroups < kGroups ? vgroups : kGroups;
     const int n_rounds = (vgroups * 4 + kRing - 1) / kRing;
     for (int t0 = 0; t0 < n_rounds * kRing; t0 += kRing) {
       float part[QT][4];      // lane partials of the group's four tiles
+      uint32_t ksw[4];        // scale words of the keys of the group's four tiles (this lane's column)
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;
+        if (u % 4 == 0) {
+          // the group's words, before the slot takes the next group's
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) ksw[qq] = (uint32_t)__shfl((int)kscg[u >> 2], 16 * qq + col, 64);
+        }
         const i32x8 kb = {kbuf[u][0], kbuf[u][1], kbuf[u][2], kbuf[u][3], 0, 0, 0, 0};
-        const int ksc = (int)((kscw[u] >> (8 * g)) & 0xffu);
+        const int ksc = (int)((ksw[u % 4] >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int qi = 0; qi < QT; ++qi) {
           // w . ReLU over the lane's 4 heads of every head group, in two
@@ -373,16 +395,6 @@ __global__ void __launch_bounds__(256) index_mxfp4_kernel(IndexLaunch a) {
         else
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rsc[qi], off_o + j * gs_s, 0, 0);
       }
-  } else {
-    // no query sees any key of this wave
-    for (int qi = 0; qi < QT; ++qi) {
-      if (r0 + qi >= a.n_qb) break;
-      float* row = score_row(a, b, r0 + qi);
-      for (int j = 0; j < kGroups; ++j) {
-        const int64_t k = (int64_t)(W + j * NW) * 64 + lane;
-        if (k < a.n_cap) store_score(a, row, k, -INFINITY);
-      }
-    }
   }
   __syncthreads();
 #pragma unroll
@@ -559,7 +571,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
       la[s] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       ls[s] = lc < kLinComps ? (int)lin[kLinScaleOff + lc * 4 + 2 * s + h] : 127;
     }
-    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)nvis_max;   // key rows in range
+    const uint32_t n_rec = paged ? (uint32_t)a.pool_blocks * 32u : (uint32_t)a.n_cap;   // key rows in range
     const __amdgpu_buffer_rsrc_t rc =
         __builtin_amdgcn_make_buffer_rsrc((void*)kc, 0, (int)(n_rec * 64u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs =
