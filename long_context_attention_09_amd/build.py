@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["csa_api.hip", "noalloc.hip", "compress.hip", "index_topk.hip", "attend.hip"]
+SOURCES = ["csa_api.hip", "noalloc.hip", "compress.hip", "index_topk.hip", "attend.hip", "attend_mh.hip"]
 
 # Per-source extra flags: the indexer's MFMA accumulators stay in ordinary
 # VGPRs, so its ReLU / head-weight epilogue works on them in place (no AGPR

@@ -143,5 +143,9 @@ struct CompressBatch {
 hipError_t launch_compress(const CompressBatch& b, hipStream_t s);
 hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
+// The 128-heads-per-workgroup attention for calls with several queries
+// (attend_mh.hip): whether it serves `a`, and its launch (no combine).
+bool attend_mh_applies(const AttendLaunch& a);
+hipError_t launch_attend_mh(const AttendLaunch& a, hipStream_t s);
 
 }  // namespace csa
