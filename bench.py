@@ -56,12 +56,12 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "63ebc3fb71249ffcd58e973e4441081a86198f21b119d92eec8b8873f5e25fa9",
-        "fetch_kib": 83404.1, "write_kib": 16512.0},
+        "sha256": "801298c957691d396d315b2633563ca3dbe71e1308f1973a087434f9682530f1",
+        "fetch_kib": 83404.4, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "92a4626965e139ac2dee18da7c82c1d44cf090723b85d7a62d15bc95ee13b4d4",
-        "fetch_kib": 69865.6, "write_kib": 8517.1},
+        "sha256": "2c78f8a799768dc6f092d85f162dac8b34bd4cee2d2299354df48f638c89464b",
+        "fetch_kib": 69845.1, "write_kib": 8356.8},
 }
 
 
