@@ -240,6 +240,29 @@ def test_prefill_chunk_reduced(shape):
     _prefill_check(shape, inp, step, rows)
 
 
+# A call with only a few queries of a 128-head model splits each query's list
+# over several workgroups of the prefill attention kernel, whose partial
+# outputs the combine pass merges (a chunk of many queries runs one split per
+# query): every row is checked.
+PREFILL_FEW = [
+    synth.PRO_CSA_PREFILL.replace(L=16384, n_q=3),
+    synth.PRO_HCA_PREFILL.replace(L=16384, n_q=3),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_FEW, ids=lambda s: f"{s.name}-L{s.L}-q{s.n_q}")
+def test_prefill_few_queries_split(shape):
+    _K()
+    from long_context_attention_09_amd.layer import LayerStep
+    _say(f"prefill (split lists) {shape.name} L={shape.L} n_q={shape.n_q}")
+    inp = synth.quant_prefill_inputs(shape)
+    step = LayerStep(shape, to_dev(inp), prefill=True)
+    assert step.ws_attend[1] > 0, "the attention should split each list (a workspace for the partials)"
+    step.run()
+    torch.cuda.synchronize()
+    _prefill_check(shape, inp, step, list(range(shape.n_q)))
+
+
 PREFILL_FULL = [synth.PRO_CSA_PREFILL, synth.PRO_HCA_PREFILL]
 
 
