@@ -263,6 +263,28 @@ def test_prefill_few_queries_split(shape):
     _prefill_check(shape, inp, step, list(range(shape.n_q)))
 
 
+# 256 heads: two 128-head workgroups per query in the prefill attention, with
+# split lists (3 queries) and without (a 64-query chunk).
+PREFILL_256 = [
+    (synth.PRO_HCA_PREFILL.replace(L=16384, n_q=3, H=256), True),
+    (synth.PRO_CSA_PREFILL.replace(L=4096, n_q=64, H=256), False),
+]
+
+
+@pytest.mark.parametrize("shape,split", PREFILL_256, ids=lambda v: f"{v.name}-q{v.n_q}-H{v.H}" if hasattr(v, "name") else str(v))
+def test_prefill_256_heads(shape, split):
+    _K()
+    from long_context_attention_09_amd.layer import LayerStep
+    _say(f"prefill {shape.name} L={shape.L} n_q={shape.n_q} H={shape.H}")
+    inp = synth.quant_prefill_inputs(shape)
+    step = LayerStep(shape, to_dev(inp), prefill=True)
+    assert (step.ws_attend[1] > 0) == split
+    step.run()
+    torch.cuda.synchronize()
+    rows = list(range(shape.n_q)) if shape.n_q <= 8 else [0, 1, 2, 31, 32, shape.n_q - 2, shape.n_q - 1]
+    _prefill_check(shape, inp, step, rows)
+
+
 PREFILL_FULL = [synth.PRO_CSA_PREFILL, synth.PRO_HCA_PREFILL]
 
 
