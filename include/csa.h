@@ -89,7 +89,9 @@ enum {
    * fixed length (CSA_INVARIANT_SPLIT_ROWS rows), whatever B and n_q are, so
    * a query's output and LSE are bitwise the same alone, inside any batch and
    * as one row of a prefill chunk.  Without it the split count follows B and
-   * n_q (to fill the GPU), which changes the order of the fp32 sums. */
+   * n_q (to fill the GPU), and calls with several queries and a multiple of
+   * 128 heads run a kernel that serves 128 heads per workgroup; both change
+   * the order of the fp32 sums. */
   CSA_ATTEND_BATCH_INVARIANT = 4,
   /* The window buffer is a per-request ring (the state cache of the paged
    * layout below): position p sits at row p % win_len, and the ring holds
