@@ -57,11 +57,11 @@ TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
         "sha256": "801298c957691d396d315b2633563ca3dbe71e1308f1973a087434f9682530f1",
-        "fetch_kib": 83404.4, "write_kib": 16512.0},
+        "fetch_kib": 83403.3, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "2c78f8a799768dc6f092d85f162dac8b34bd4cee2d2299354df48f638c89464b",
-        "fetch_kib": 69845.1, "write_kib": 8356.8},
+        "sha256": "2811ac7cc005f05d98e3428c6b08e42e060cc1d695175dd0970751915405875d",
+        "fetch_kib": 69843.6, "write_kib": 8356.8},
 }
 
 

@@ -423,7 +423,11 @@ index_mxfp4_kernel(IndexLaunch a) {
 //    result elements 0-5 are the six components of the query of its lane half.
 // Every lane of the result holds 16 heads of one key; the two lane halves are
 // summed by one 32-lane swap that also leaves query 0 in lanes 0-31 and
-// query 1 in lanes 32-63.
+// query 1 in lanes 32-63.  The products are software-pipelined one head group
+// ahead (the matrix cores work on group g + 1 while the vector unit weighs
+// group g, and on the next tile's first group during a tile's epilogue); the
+// score dtype and paging are template arguments, so a round of tiles is one
+// basic block the scheduler can interleave.
 //
 // Operand layouts of the 32x32x64 form (per lane l, K-step s of 64 dims):
 //   MXFP4 (keys, query heads): row/column l % 32, dims 64 s + 32 (l / 32) .. +31
@@ -487,10 +491,11 @@ __device__ __forceinline__ int vt_all(int ntv, int W, int NW, int TPW) {
   return v < TPW ? v : TPW;
 }
 
-template <int NH32>
+template <int NH32, bool BF16, bool PAGED>
 __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   constexpr int QT = kMqQT, R = kMqRing, TPW = kMqTiles;
-  __shared__ uint32_t lhist[QT][kBins1];
+  // one spare bin per query takes the adds of invisible keys, so the add needs no branch
+  __shared__ uint32_t lhist[QT][kBins1 + 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;        // operand dim half / result row half; after the swap: the query
@@ -499,7 +504,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   const int r0 = blockIdx.y * QT;
   const int live_q = a.n_qb - r0 < QT ? a.n_qb - r0 : QT;
 
-  for (int i = threadIdx.x; i < QT * kBins1; i += 256) (&lhist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < QT * (kBins1 + 4); i += 256) (&lhist[0][0])[i] = 0;
   int nvis[QT];
   int nvis_max = 0;
 #pragma unroll
@@ -515,24 +520,24 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
   const int W = (int)blockIdx.x * 4 + wave;
   const int ntv = (nvis_max + 31) / 32;        // tiles with a visible key
   // paged keys: k0 / k1 are the pools, a 32-key tile is one block
-  const bool paged = a.bt != nullptr;
+  constexpr bool paged = PAGED;
   const uint8_t* kc = (const uint8_t*)a.k0 + (paged ? 0 : (int64_t)b * a.n_cap * 64);
   const uint32_t* ks = (const uint32_t*)a.k1 + (paged ? 0 : (int64_t)b * a.n_cap);
   // both query rows of the block's scores through one resource: rows past
   // the live queries are outside it, so their stores are dropped
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)score_row(a, b, r0), 0,
-      (int)((uint32_t)live_q * (uint32_t)a.n_cap * (bf16_scores(a) ? 2u : 4u)), kBufferWord3);
+      (int)((uint32_t)live_q * (uint32_t)a.n_cap * (BF16 ? 2u : 4u)), kBufferWord3);
   const int my_nvis = h ? nvis[1] : nvis[0];
   // byte offset of this lane's score for key `key`; keys past the row map
   // outside the resource (their stores are dropped instead of landing in the
   // next query's row)
-  const uint32_t es = bf16_scores(a) ? 2u : 4u;
+  constexpr uint32_t es = BF16 ? 2u : 4u;
   auto score_off = [&](int key) {
     return key < a.n_cap ? ((uint32_t)h * (uint32_t)a.n_cap + (uint32_t)key) * es : 0xfffffff0u;
   };
   auto store_sc = [&](float v, uint32_t off) {
-    if (es == 2u) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rsc, off, 0, 0);
+    if constexpr (BF16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rsc, off, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsc, off, 0, 0);
   };
 
@@ -590,7 +595,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
     uint32_t kw[R];
     auto fetch = [&](int j, int u) {
       uint32_t oc = off_c + (uint32_t)j * st_c, os = off_s + (uint32_t)j * st_s;
-      if (paged) {
+      if constexpr (PAGED) {
         const int r = j >> 6;
         const int v = r == 0 ? blk_v[0] : r == 1 ? blk_v[1] : r == 2 ? blk_v[2] : blk_v[3];
         const int blk = j < TPW ? __builtin_amdgcn_readlane(v, j & 63) : -1;
@@ -610,33 +615,56 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
     int vt = (ntv - W + NW - 1) / NW;
     vt = vt < TPW ? vt : TPW;
     const int n_rounds = (vt + R - 1) / R;
+    // key operands of ring slot u
+    auto kop = [&](int u, int s) {
+      return (i32x8){kb[u][s][0], kb[u][s][1], kb[u][s][2], kb[u][s][3], 0, 0, 0, 0};
+    };
+    auto ksc = [&](int u, int s) { return (int)((kw[u] >> (8 * (2 * s + h))) & 0xffu); };
+    // the head group g = qi * NH32 + hg against the keys of ring slot u
+    auto head_pair = [&](int g, int u) {
+      const int qi = g / NH32, hg = g % NH32;
+      const i32x8 a0 = {qa[qi][hg][0][0], qa[qi][hg][0][1], qa[qi][hg][0][2], qa[qi][hg][0][3], 0, 0, 0, 0};
+      const i32x8 a1 = {qa[qi][hg][1][0], qa[qi][hg][1][1], qa[qi][hg][1][2], qa[qi][hg][1][3], 0, 0, 0, 0};
+      f32x16 acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, kop(u, 0), acc, 4, 4, 0, qs[qi][hg][0], 0, ksc(u, 0));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, kop(u, 1), acc, 4, 4, 0, qs[qi][hg][1], 0, ksc(u, 1));
+      return acc;
+    };
+    constexpr int G = QT * NH32;
+    // the linear product of the keys of ring slot u
+    auto lin_pair = [&](int u) {
+      f32x16 acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[0], kop(u, 0), acc, 0, 4, 0, ls[0], 0, ksc(u, 0));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[1], kop(u, 1), acc, 0, 4, 0, ls[1], 0, ksc(u, 1));
+      return acc;
+    };
+    // software pipeline: the first head group and the linear product of a
+    // tile are multiplied while the previous tile's epilogue runs, every
+    // later head group while the previous group's weights are applied
+    f32x16 acc_cur = head_pair(0, 0);
     for (int j0 = 0; j0 < n_rounds * R; j0 += R) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int j = j0 + u;
-        const i32x8 b0 = {kb[u][0][0], kb[u][0][1], kb[u][0][2], kb[u][0][3], 0, 0, 0, 0};
-        const i32x8 b1 = {kb[u][1][0], kb[u][1][1], kb[u][1][2], kb[u][1][3], 0, 0, 0, 0};
-        const int ks0 = (int)((kw[u] >> (8 * h)) & 0xffu);
-        const int ks1 = (int)((kw[u] >> (8 * (2 + h))) & 0xffu);
-        f32x16 accl = {};
-        accl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[0], b0, accl, 0, 4, 0, ls[0], 0, ks0);
-        accl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[1], b1, accl, 0, 4, 0, ls[1], 0, ks1);
+        const int un = (u + 1) % R;
+        const f32x16 accl = lin_pair(u);
+        float pp[QT][2] = {};
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          f32x16 nxt;
+          if (g + 1 < G) {
+            nxt = head_pair(g + 1, u);
+          } else {
+            nxt = head_pair(0, un);
+          }
+          const int qi = g / NH32, hg = g % NH32;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pp[qi][e & 1] = fmaf(w2[qi][hg][e], fabsf(acc_cur[e]), pp[qi][e & 1]);
+          acc_cur = nxt;
+        }
         float part[QT];
 #pragma unroll
-        for (int qi = 0; qi < QT; ++qi) {
-          float p = 0.f;
-#pragma unroll
-          for (int hg = 0; hg < NH32; ++hg) {
-            const i32x8 a0 = {qa[qi][hg][0][0], qa[qi][hg][0][1], qa[qi][hg][0][2], qa[qi][hg][0][3], 0, 0, 0, 0};
-            const i32x8 a1 = {qa[qi][hg][1][0], qa[qi][hg][1][1], qa[qi][hg][1][2], qa[qi][hg][1][3], 0, 0, 0, 0};
-            f32x16 acc = {};
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, acc, 4, 4, 0, qs[qi][hg][0], 0, ks0);
-            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, acc, 4, 4, 0, qs[qi][hg][1], 0, ks1);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) p = fmaf(w2[qi][hg][e], fabsf(acc[e]), p);
-          }
-          part[qi] = p;
-        }
+        for (int qi = 0; qi < QT; ++qi) part[qi] = pp[qi][0] + pp[qi][1];
         // lanes 0-31: query 0, lanes 32-63: query 1, summed over both row halves
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
         // the linear term of this lane half's query, smallest components first
@@ -646,7 +674,8 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
         const bool vis = key < my_nvis;
         const float sc = vis ? tot : -INFINITY;
         store_sc(sc, score_off(key));
-        if (vis) atomicAdd(&lhist[h][order_key(stored_score(a, sc)) >> kShift1], 1u);
+        const float kept = BF16 ? bf16_to_f32(f32_to_bf16(sc)) : sc;
+        atomicAdd(&lhist[h][vis ? (int)(order_key(kept) >> kShift1) : kBins1], 1u);
         fetch(j + R, u);
       }
     }
@@ -1342,10 +1371,16 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
     index_linear_kernel<<<dim3(a.n_qb, a.B), 128, 0, s>>>(a);
     const int per_wg = 4 * kMqTiles * 32;
     dim3 grid((a.n_cap + per_wg - 1) / per_wg, (a.n_qb + kMqQT - 1) / kMqQT, a.B);
-    if (a.H_I == 64)
-      hipExtLaunchKernelGGL(index_mxfp4_mq_kernel<2>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(index_mxfp4_mq_kernel<1>, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+    // score dtype and paging are template arguments, so the tile loop has no branch
+    const bool bf = (a.flags & CSA_INDEX_BF16_SCORES) != 0, pg = a.bt != nullptr;
+    auto go = [&](auto nh) {
+      constexpr int NH = decltype(nh)::value;
+      auto* k = bf ? (pg ? index_mxfp4_mq_kernel<NH, true, true> : index_mxfp4_mq_kernel<NH, true, false>)
+                   : (pg ? index_mxfp4_mq_kernel<NH, false, true> : index_mxfp4_mq_kernel<NH, false, false>);
+      hipExtLaunchKernelGGL(k, grid, dim3(256), 0, s, a.ev_start, a.ev_stop, 0, a);
+    };
+    if (a.H_I == 64) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 1>{});
   } else if (a.fmt == CSA_FMT_MXFP4) {
     const int kchunks = (a.n_cap + kKeysPerWG - 1) / kKeysPerWG;
     const int nhg = a.H_I / 16;
