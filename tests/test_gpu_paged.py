@@ -355,6 +355,66 @@ def _attend_oracle(S, q, t, entries_u8, sel, win_u8, win_pos0, sink, dense):
     return (OC.hca_attend if dense else OC.csa_attend)(*args)[0]
 
 
+@pytest.mark.parametrize("H_I", [32, 64])
+def test_paged_query_blocks_match_contiguous(H_I):
+    """The query-block indexer (several queries per call) reading its keys
+    through shuffled 32-key blocks gives, bitwise, the scores and selection of
+    the contiguous layout, with fp32 scores and with BF16 scores, for 32 and 64
+    indexer heads; the BF16 scores are the fp32 ones rounded, and every
+    selection is the exact top-k of the scores it was made from (ties to the
+    lower index)."""
+    K = _K()
+    B, n_q, max_blocks, top_k = 2, 9, 96, 256
+    n_cap = max_blocks * 32
+    S = CSA.replace(name=f"paged-qblocks-{H_I}", H_I=H_I)
+    _say(f"paged query blocks H_I={H_I} B={B} n_q={n_q} n_cap={n_cap}")
+    kc, ks = synth.mxfp4_codes(S, "k", B * n_cap, 128)
+    kc, ks = kc.view(B, n_cap, 64), ks.view(B, n_cap, 4)
+    qc, qs = synth.mxfp4_codes(S, "q", B * n_q * H_I, 128)
+    qc, qs = qc.view(B, n_q, H_I, 64), qs.view(B, n_q, H_I, 4)
+    w = synth.head_weights(S, (B, n_q, H_I))
+    # block j of sequence b sits at a shuffled pool slot; some slots stay unused
+    n_pool = B * max_blocks + 7
+    slots = np.random.default_rng(5).permutation(n_pool)[:B * max_blocks].astype(np.int32)
+    bt = torch.from_numpy(slots).view(B, max_blocks)
+    pool_c = torch.zeros(n_pool, 32, 64, dtype=torch.uint8)
+    pool_s = torch.full((n_pool, 32, 4), 127, dtype=torch.uint8)
+    pool_c[bt.reshape(-1).long()] = kc.reshape(B * max_blocks, 32, 64)
+    pool_s[bt.reshape(-1).long()] = ks.reshape(B * max_blocks, 32, 4)
+    # visible entries from n_cap - 1 down to about 2,700, different per sequence
+    q_pos = torch.stack([4 * n_cap - 1 - 5 * b - 41 * torch.arange(n_q) for b in range(B)]).contiguous()
+
+    def run(paged, flags):
+        g = _dev
+        k0, k1 = (g(pool_c), g(pool_s)) if paged else (g(kc), g(ks))
+        extra = {"block_table": g(bt)} if paged else {}
+        idx = torch.empty(B, n_q, top_k, dtype=torch.int32, device="cuda")
+        dt = torch.bfloat16 if flags else torch.float32
+        sc = torch.empty(B, n_q, n_cap, dtype=dt, device="cuda")
+        K.index_topk(g(qc), g(w), k0, g(q_pos), m=4, top_k=top_k, out_idx=idx, q1=g(qs), k1=k1, out_score=sc,
+                     fmt=K.FMT_MXFP4, flags=flags, **extra)
+        idx2 = torch.empty_like(idx)                 # the same call without caller-kept scores
+        K.index_topk(g(qc), g(w), k0, g(q_pos), m=4, top_k=top_k, out_idx=idx2, q1=g(qs), k1=k1,
+                     fmt=K.FMT_MXFP4, flags=flags, **extra)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2)
+        return idx.cpu().numpy(), sc.float().cpu().numpy().astype(np.float64)
+
+    got = {(paged, bf): run(paged, K.INDEX_BF16_SCORES if bf else 0) for paged in (False, True) for bf in (False, True)}
+    for bf in (False, True):
+        assert np.array_equal(got[(True, bf)][0], got[(False, bf)][0]), f"selection, bf16={bf}"
+        assert np.array_equal(got[(True, bf)][1], got[(False, bf)][1]), f"scores, bf16={bf}"
+    sc32, sc16 = got[(False, False)][1], got[(False, True)][1]
+    for b in range(B):
+        for r in range(n_q):
+            n_vis = OC.visible_entries(int(q_pos[b, r]), 4, n_cap)
+            r32 = torch.from_numpy(sc32[b, r, :n_vis].astype(np.float32)).to(torch.bfloat16).double().numpy()
+            assert np.array_equal(sc16[b, r, :n_vis], r32), (b, r)
+            for bf, sc in ((False, sc32), (True, sc16)):
+                want = OC.topk(sc[b, r, :n_vis], top_k)
+                assert np.array_equal(got[(False, bf)][0][b, r], want), (b, r, bf)
+
+
 def test_attend_long_lists_split_by_the_stage():
     """Lists longer than the 2048 rows a split stages: a CSA selection of 6000
     indices (with -1 and out-of-range ones mixed in) and paged HCA lists at
