@@ -13,15 +13,19 @@
 // 32-entry tile serves all 128 heads of the workgroup (the 64-head decode
 // kernel serves half of them per copy).  Four wavefronts, one per SIMD; wave
 // w owns heads 32 w .. +31 across all 512 dims, so
-//   S^T[32 entries x 32 heads] = K Q^T          (32 V_MFMA_F32_32X32X16_BF16)
+//   S^T[32 entries x 32 heads] = K Q^T
+// (the 448 FP8 dims: 14 V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the entry bytes
+// as they are against a two-component E4M3 split of the query; the 64 RoPE
+// dims: 4 V_MFMA_F32_32X32X16_BF16)
 // is complete inside the wave: the online softmax works on registers (lane l
 // holds head l % 32 and 16 of the tile's entries, lane l ^ 32 the other 16),
 // two 32-lane swaps per 16 entries turn P^T from the result layout into the
 // B-operand layout of
 //   O^T[512 dims x 32 heads] += V^T P^T          (32 MFMAs, 256 accumulators)
 // and a lane's accumulators all belong to its own head, so a rescale is one
-// factor per lane.  K comes from the LDS tile as 8-byte reads widened FP8 ->
-// BF16 (16-byte reads for the BF16 RoPE dims), V^T by transposing LDS reads.
+// factor per lane.  K comes from the LDS tile as 16-byte reads used as they
+// are (the RoPE dims as BF16), V^T by transposing LDS reads widened FP8 ->
+// BF16 in registers.
 //
 // The tile is stored as [36 sixteen-byte chunks][32 entries]: each 1 KiB
 // direct-to-LDS load of a wave brings chunks 2i and 2i+1 of all 32 entries,
@@ -63,6 +67,22 @@ __device__ __forceinline__ void lds_dma16(uint64_t gaddr, uint32_t lds_off) {
                        : "memory", "m0");
 }
 
+// Scaled 32x32x64 product of FP8 entry bytes (scale 2^0) and an FP8 query
+// component whose E8M0 scale is byte SEL of scw.
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_q8(const i32x8& k, const i32x8& q, const f32x16& c, uint32_t scw) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k, q, c, 0, 0, 0, 127, SEL, (int)scw);
+}
+__device__ __forceinline__ f32x16 mfma_q8_byte(int sel, const i32x8& k, const i32x8& q, const f32x16& c,
+                                               uint32_t scw) {
+  switch (sel) {
+    case 0: return mfma_q8<0>(k, q, c, scw);
+    case 1: return mfma_q8<1>(k, q, c, scw);
+    case 2: return mfma_q8<2>(k, q, c, scw);
+    default: return mfma_q8<3>(k, q, c, scw);
+  }
+}
+
 }  // namespace
 
 __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a) {
@@ -83,11 +103,20 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
   // ---- prologue: the query, the sink, the list layout and (gathering) the
   // split's staged entry rows
   const float sink_raw = a.sink[head];
-  i32x4 qraw[32];                                      // dims 16 s + 8 g .. +7, BF16
+  // BF16 query: the FP8-stored dims in the layout of the scaled 32x32x64
+  // operand (K-step s: dims 64 s + 16 g .. +15 and 64 s + 32 + 16 g .. +15),
+  // the RoPE dims in the layout of the BF16 32x32x16 operand (dims
+  // kDN + 16 u + 8 g .. +7)
+  i32x4 qfr[kDN / 64][4];
+  i32x4 qrr[kDR / 16];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * a.n_q + r) * a.H + head) * kD;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) qraw[s] = *(gbl_i32x4*)(qrow + 16 * s + 8 * g);
+    for (int s = 0; s < kDN / 64; ++s)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) qfr[s][p] = *(gbl_i32x4*)(qrow + 64 * s + 32 * (p >> 1) + 16 * g + 8 * (p & 1));
+#pragma unroll
+    for (int u = 0; u < kDR / 16; ++u) qrr[u] = *(gbl_i32x4*)(qrow + kDN + 16 * u + 8 * g);
   }
   const ListInfo L = list_info(a, b, r);
   const bool gather = a.idx != nullptr || a.bt != nullptr;
@@ -155,43 +184,114 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
   uint32_t live1 = issue_tile(1, 1);
 
   // The query operand: RMSNorm over the 512 dims (lane l ^ 32 holds the
-  // other half), the softmax scale in log2 units, RoPE on dims 448 .. 511,
-  // BF16 (nearest even).
-  bf16x8 qv[32];
+  // other half), the softmax scale in log2 units, then
+  //  * the FP8-stored dims as two E4M3 components per 32-dim block, each with
+  //    its own E8M0 scale that puts the block's largest magnitude in
+  //    [128, 256): q = 2^e1 c1 + 2^e2 c2 + r with |r| below 2^-8 of the block
+  //    maximum (the precision of BF16), so the score product reads the FP8
+  //    entry bytes as they are (scaled 32x32x64 products, no widening);
+  //  * RoPE on dims 448 .. 511, BF16 (nearest even).
+  // Lane half g supplies the scales of blocks 2 s + g (the operand's rule);
+  // component c of K-step s has its scale in byte (7 c + s) % 4 of word
+  // (7 c + s) / 4.
+  i32x8 qf[2][kDN / 64];
+  uint32_t qsc[4] = {0u, 0u, 0u, 0u};
+  bf16x8 qv[kDR / 16];
   {
     float ss = 0.f;
-#pragma unroll
-    for (int s = 0; s < 32; ++s)
+    auto acc_ss = [&](const i32x4& w4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = (uint32_t)qraw[s][j];
+        const uint32_t w = (uint32_t)w4[j];
         const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
         ss += lo * lo + hi * hi;
       }
+    };
+#pragma unroll
+    for (int s = 0; s < kDN / 64; ++s)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc_ss(qfr[s][p]);
+#pragma unroll
+    for (int u = 0; u < kDR / 16; ++u) acc_ss(qrr[u]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
     const float tot = g == 0 ? ss + __uint_as_float(sw[1]) : __uint_as_float(sw[0]) + ss;
     const float rs = ((a.flags & CSA_ATTEND_NORM_Q) ? 1.0f / sqrtf(tot / (float)kD + 1e-6f) : 1.0f) * a.scale_log2;
-#pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = (uint32_t)qraw[s][j];
-        x[2 * j] = __uint_as_float(w << 16) * rs;
-        x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
+    // E8M0 exponent that puts a block maximum m in [128, 256) (-127: an all-zero block)
+    auto block_exp = [](float m) {
+      int e = -127;
+      if (m > 0.0f) {
+        int ex;
+        frexpf(m, &ex);
+        e = ex - 8;
       }
-      if (s >= kDN / 16) {
+      return e < -127 ? -127 : (e > 127 ? 127 : e);
+    };
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int u = (16 * s + 8 * g + j - kDN) >> 1;
-          const float cs = rope_cs[u], sn = rope_cs[32 + u];
-          const float xe = x[j], xo = x[j + 1];
-          x[j] = xe * cs - xo * sn;
-          x[j + 1] = xe * sn + xo * cs;
+    for (int s = 0; s < kDN / 64; ++s) {
+      uint32_t wc[2][8];                       // packed codes of both components
+      int e_lane[2] = {0, 0};                  // this lane's scales (block 2 s + g)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {         // block 2 s + hb: dims 64 s + 32 hb .. +31
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = (uint32_t)qfr[s][2 * hb + (j >> 2)][j & 3];
+          x[2 * j] = __uint_as_float(w << 16) * rs;
+          x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float m = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[j]));
+          const auto mw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(m, __uint_as_float(g == 0 ? mw[1] : mw[0]));   // the block's maximum (both lane halves)
+          const int e = block_exp(m);
+          const float down = ldexpf(1.0f, -e), up = ldexpf(1.0f, e);
+#pragma unroll
+          for (int j = 0; j < 16; j += 4) {
+            // E4M3 codes by the hardware converter (nearest even; the scaled
+            // values lie below 256, inside the format's range)
+            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(x[j] * down, x[j + 1] * down, 0, false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(x[j + 2] * down, x[j + 3] * down, wv, true);
+            // what the next component carries
+            x[j] -= __builtin_amdgcn_cvt_f32_fp8(wv, 0) * up;
+            x[j + 1] -= __builtin_amdgcn_cvt_f32_fp8(wv, 1) * up;
+            x[j + 2] -= __builtin_amdgcn_cvt_f32_fp8(wv, 2) * up;
+            x[j + 3] -= __builtin_amdgcn_cvt_f32_fp8(wv, 3) * up;
+            wc[c][4 * hb + j / 4] = (uint32_t)wv;
+          }
+          if (hb == 0) e_lane[c] = e;
+          else if (g == 1) e_lane[c] = e;
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qv[s][j] = (__bf16)x[j];
+      for (int c = 0; c < 2; ++c) {
+        qf[c][s] = (i32x8){(int)wc[c][0], (int)wc[c][1], (int)wc[c][2], (int)wc[c][3],
+                           (int)wc[c][4], (int)wc[c][5], (int)wc[c][6], (int)wc[c][7]};
+        const int idx = 7 * c + s;
+        qsc[idx / 4] |= (uint32_t)(e_lane[c] + 127) << (8 * (idx % 4));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDR / 16; ++u) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (uint32_t)qrr[u][j];
+        x[2 * j] = __uint_as_float(w << 16) * rs;
+        x[2 * j + 1] = __uint_as_float(w & 0xffff0000u) * rs;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int v = (16 * u + 8 * g + j) >> 1;
+        const float cs = rope_cs[v], sn = rope_cs[32 + v];
+        const float xe = x[j], xo = x[j + 1];
+        x[j] = xe * cs - xo * sn;
+        x[j + 1] = xe * sn + xo * cs;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[u][j] = (__bf16)x[j];
     }
   }
 
@@ -228,16 +328,21 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
 
     // scores: lane holds head r32, entries 8 j + 4 g + i (i < 4) in sc[4 j + i]
     f32x16 sc = {};
+    // FP8 dims: the entry bytes as the A operand of the scaled 32x32x64
+    // product (scale 2^0) against both query components
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      bf16x8 kop;
-      if (s < kDN / 16) {
-        const i32x2 w = *(const i32x2*)(tb + s * 512 + 16 * r32 + 8 * g);
-        kop = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
-      } else {
-        kop = *(const bf16x8*)(tb + (kDN / 16 + 2 * (s - kDN / 16) + g) * 512 + 16 * r32);
-      }
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[s], sc, 0, 0, 0);
+    for (int s = 0; s < kDN / 64; ++s) {
+      const i32x4 lo = *(const i32x4*)(tb + (4 * s + g) * 512 + 16 * r32);
+      const i32x4 hi = *(const i32x4*)(tb + (4 * s + 2 + g) * 512 + 16 * r32);
+      const i32x8 kop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      sc = mfma_q8_byte(s % 4, kop, qf[0][s], sc, qsc[s / 4]);
+      sc = mfma_q8_byte((7 + s) % 4, kop, qf[1][s], sc, qsc[(7 + s) / 4]);
+    }
+    // RoPE dims: BF16 products
+#pragma unroll
+    for (int u = 0; u < kDR / 16; ++u) {
+      const bf16x8 kop = *(const bf16x8*)(tb + (kDN / 16 + 2 * u + g) * 512 + 16 * r32);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qv[u], sc, 0, 0, 0);
     }
 
     // online softmax of the head over the tile
