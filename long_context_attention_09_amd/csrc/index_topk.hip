@@ -851,36 +851,50 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
       a.chunk_cand[(int64_t)q * a.n_chunks + blockIdx.x] = n_here;
     }
   } else {
-    // Lists of indices in index order: the chunk's scores are loaded
-    // coalesced (thread t: entries c0 + 256 j + t) and passed through LDS so
-    // that thread t then holds the 16 consecutive entries c0 + 16 t + j; the
-    // scans in thread order then give index order.  (LDS rows padded by one
-    // word per 16 so both passes are free of bank conflicts.)
+    // Lists of indices in index order: thread t holds the 16 consecutive
+    // entries c0 + 16 t + j, so the scans in thread order give index order.
     float* const sc = score_row(a, q / a.n_qb, q % a.n_qb);
     constexpr int PT = kChunk / 256;
-    __shared__ float tr[kChunk + kChunk / 16];
+    static_assert(PT == 16, "thread t takes entries c0 + 16 t .. +15");
+    // thread t loads its 16 consecutive entries (four 16-byte loads of fp32
+    // scores, two of BF16 codes) when they lie inside the visible range and
+    // the row is 16-byte aligned (a caller's row length may be odd), entry
+    // by entry otherwise
+    const int64_t e0 = c0 + 16 * (int64_t)threadIdx.x;
+    const bool row_aligned = (((uintptr_t)sc) & 15) == 0;
     float sv[PT];
+    if (e0 + PT <= n_vis && row_aligned) {
+      if (bf16_scores(a)) {
+        const uint16_t* r16 = (const uint16_t*)sc + e0;
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int64_t i = c0 + j * 256 + threadIdx.x;
-      sv[j] = i < n_vis ? load_score(a, sc, i) : 0.f;
+        for (int v = 0; v < 2; ++v) {
+          const i32x4 w = *(const i32x4*)(r16 + 8 * v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[8 * v + 2 * i] = __uint_as_float((uint32_t)w[i] << 16);
+            sv[8 * v + 2 * i + 1] = __uint_as_float((uint32_t)w[i] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const f32x4 w = *(const f32x4*)(sc + e0 + 4 * v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[4 * v + i] = w[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PT; ++j) sv[j] = e0 + j < n_vis ? load_score(a, sc, e0 + j) : 0.f;
     }
     // the bucket of the k-th key, found once per query by topk_bucket_kernel
     const TopkState st = a.state[q];
-#pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      const int e = j * 256 + (int)threadIdx.x;
-      tr[e + (e >> 4)] = sv[j];
-    }
-    __syncthreads();
-    const int64_t e0 = c0 + 16 * (int64_t)threadIdx.x;
     uint32_t keys[PT];
     uint32_t want = 0, above = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int e = 16 * (int)threadIdx.x + j;
       const bool in = e0 + j < st.n_vis;
-      keys[j] = in ? order_key(tr[e + (e >> 4)]) : 0u;
+      keys[j] = in ? order_key(sv[j]) : 0u;
       const uint32_t d1 = keys[j] >> kShift1;
       above |= (uint32_t)(in && d1 > st.b1) << j;
       want |= (uint32_t)(in && d1 == st.b1) << j;
