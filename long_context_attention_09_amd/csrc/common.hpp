@@ -78,9 +78,10 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 
 // ------------------------------------------------------------------ MXFP4
 
+// E2M1 code n (sign in bit 3): twice the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6 are the nibbles of 0xC8643210, so the decode needs no table in memory
 __device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
-  const float mags[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
-  const float v = mags[n & 7u];
+  const float v = 0.5f * (float)((0xC8643210u >> (4u * (n & 7u))) & 15u);
   return (n & 8u) ? -v : v;
 }
 

@@ -459,6 +459,7 @@ __global__ void __launch_bounds__(128) index_linear_kernel(IndexLaunch a) {
   const uint8_t* qc = (const uint8_t*)a.q0;
   const uint8_t* qsc = (const uint8_t*)a.q1;
   float u = 0.f;
+#pragma unroll 8
   for (int hh = 0; hh < a.H_I; ++hh) {
     const uint32_t byte = qc[(qrow + hh) * 64 + (k >> 1)];
     const float v = e2m1_to_f32((byte >> (4 * (k & 1))) & 15u) *
