@@ -94,7 +94,8 @@ __device__ __forceinline__ void unpack_words(const uint32_t (&w)[KW], bool in, f
 
 // WIDE: one 512-thread workgroup per entry, its eight wavefronts fold
 // interleaved candidates and merge their running (max, sum, weighted sum)
-// through LDS (the 128-token HCA blocks); otherwise one wavefront per entry.
+// through LDS (the 128-token HCA blocks); otherwise one wavefront per entry
+// (in a wide launch too, for the jobs of short blocks, eight to a workgroup).
 // blockIdx.z selects one of up to kMaxJobs independent jobs of one launch.
 // Merge another running (max, sum, weighted sum) state into this one, channel
 // by channel, without branches: where both maxima are -inf the scale factors
@@ -307,7 +308,11 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
   constexpr int kWaves = WIDE ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int entry_local = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
+  // a job of short blocks (m < 16) takes one entry per wave, also when a
+  // long-block job of the same batch makes the launch wide (the raw window
+  // rows of a prefill chunk beside its long blocks); uniform per workgroup
+  const bool per_wave = !WIDE || a.m < 16;
+  const int entry_local = per_wave ? (int)blockIdx.x * kWaves + wave : (int)blockIdx.x;
   const int b = blockIdx.y;
   if (b >= a.B || entry_local >= a.n_entries) return;
   const int64_t i = compress_entry(a, b, entry_local);  // absolute entry index
@@ -326,7 +331,7 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
     // candidates pooled in n_parts groups by compress_part_kernel: wave w
     // merges the groups' (max, sum, weighted sum) states w, w + kWaves, ...
     const float* pp = a.part + ((int64_t)b * a.n_entries + entry_local) * a.n_parts * 3 * d;
-    const int g_first = WIDE ? wave : 0, g_step = WIDE ? kWaves : 1;
+    const int g_first = per_wave ? 0 : wave, g_step = per_wave ? 1 : kWaves;
     for (int g = g_first; g < a.n_parts; g += g_step) {
       const float* q = pp + (int64_t)g * 3 * d;
       float pm[CPT], ps[CPT], pa[CPT];
@@ -335,9 +340,10 @@ __global__ void __launch_bounds__(WIDE ? 512 : 256, WIDE ? 1 : 2) compress_kerne
     }
   } else {
     constexpr int kBatch = CPT >= 16 ? 4 : 8;   // candidates whose loads are in flight together
-    fold_candidates<T, CPT, VEC, kBatch>(a, b, i, lane, WIDE ? wave : 0, WIDE ? kWaves : 1, n_cand, mx, sm, acc);
+    fold_candidates<T, CPT, VEC, kBatch>(a, b, i, lane, per_wave ? 0 : wave, per_wave ? 1 : kWaves, n_cand, mx, sm,
+                                         acc);
   }
-  if constexpr (WIDE) {
+  if (WIDE && !per_wave) {
     // tree merge, 8 -> 4 -> 2 -> 1 waves; each level has its own LDS slots
     // (4 + 2 + 1), so one barrier per level
     __shared__ __attribute__((aligned(16))) float red[(kWaves - 1) * 3 * 64 * CPT];
@@ -527,16 +533,24 @@ __global__ void __launch_bounds__(256, 2) compress_part_kernel(CompressBatch bat
 }
 
 template <typename T, int CPT, bool VEC>
-static void launch_cpt(const CompressBatch& bt, int B, int n_entries, bool wide, hipStream_t s) {
+static void launch_cpt(const CompressBatch& bt, int B, bool wide, hipStream_t s) {
   int n_part_wg = 0;
   for (int j = 0; j < bt.n_jobs; ++j)
     if (bt.job[j].part && bt.job[j].n_entries * bt.job[j].n_parts > n_part_wg)
       n_part_wg = bt.job[j].n_entries * bt.job[j].n_parts;
   if (n_part_wg > 0) compress_part_kernel<T, CPT, VEC><<<dim3(n_part_wg, B, bt.n_jobs), 256, 0, s>>>(bt);
+  // workgroups per job: wide launches take a long-block entry per workgroup
+  // and eight short-block entries (one per wave); narrow ones four entries
+  int gx = 1;
+  for (int j = 0; j < bt.n_jobs; ++j) {
+    const CompressLaunch& a = bt.job[j];
+    const int n = wide ? (a.m >= 16 ? a.n_entries : (a.n_entries + 7) / 8) : (a.n_entries + 3) / 4;
+    gx = n > gx ? n : gx;
+  }
   if (wide) {
-    compress_kernel<T, CPT, true, VEC><<<dim3(n_entries, B, bt.n_jobs), 512, 0, s>>>(bt);
+    compress_kernel<T, CPT, true, VEC><<<dim3(gx, B, bt.n_jobs), 512, 0, s>>>(bt);
   } else {
-    compress_kernel<T, CPT, false, VEC><<<dim3((n_entries + 3) / 4, B, bt.n_jobs), 256, 0, s>>>(bt);
+    compress_kernel<T, CPT, false, VEC><<<dim3(gx, B, bt.n_jobs), 256, 0, s>>>(bt);
   }
 }
 
@@ -552,16 +566,16 @@ static bool vec_ok(const CompressLaunch& a) {
 }
 
 template <typename T, int CPT>
-static void launch_cpt(const CompressBatch& bt, int B, int n_entries, bool wide, hipStream_t s) {
+static void launch_cpt(const CompressBatch& bt, int B, bool wide, hipStream_t s) {
   bool vec = true;
   for (int j = 0; j < bt.n_jobs; ++j) vec = vec && vec_ok<T, CPT>(bt.job[j]);
-  if (vec) launch_cpt<T, CPT, true>(bt, B, n_entries, wide, s);
-  else launch_cpt<T, CPT, false>(bt, B, n_entries, wide, s);
+  if (vec) launch_cpt<T, CPT, true>(bt, B, wide, s);
+  else launch_cpt<T, CPT, false>(bt, B, wide, s);
 }
 
 template <typename T>
 static hipError_t launch_t(const CompressBatch& bt, hipStream_t s) {
-  int cpt = 1, B = 1, n_entries = 1;
+  int cpt = 1, B = 1;
   bool wide = false;
   for (int j = 0; j < bt.n_jobs; ++j) {
     const CompressLaunch& a = bt.job[j];
@@ -569,14 +583,13 @@ static hipError_t launch_t(const CompressBatch& bt, hipStream_t s) {
     if (a.out_fmt == CSA_FMT_MXFP4 && c < 2) c = 2;  // a lane packs whole bytes
     cpt = c > cpt ? c : cpt;
     B = a.B > B ? a.B : B;
-    n_entries = a.n_entries > n_entries ? a.n_entries : n_entries;
     wide = wide || a.m >= 16;
   }
-  if (cpt <= 1) launch_cpt<T, 1>(bt, B, n_entries, wide, s);
-  else if (cpt <= 2) launch_cpt<T, 2>(bt, B, n_entries, wide, s);
-  else if (cpt <= 4) launch_cpt<T, 4>(bt, B, n_entries, wide, s);
-  else if (cpt <= 8) launch_cpt<T, 8>(bt, B, n_entries, wide, s);
-  else launch_cpt<T, 16>(bt, B, n_entries, wide, s);
+  if (cpt <= 1) launch_cpt<T, 1>(bt, B, wide, s);
+  else if (cpt <= 2) launch_cpt<T, 2>(bt, B, wide, s);
+  else if (cpt <= 4) launch_cpt<T, 4>(bt, B, wide, s);
+  else if (cpt <= 8) launch_cpt<T, 8>(bt, B, wide, s);
+  else launch_cpt<T, 16>(bt, B, wide, s);
   return hipGetLastError();
 }
 
