@@ -374,11 +374,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
             vop = fp8x8_to_bf16((uint32_t)vt8[d8][ks][0], (uint32_t)vt8[d8][ks][1]);
           } else {
             const int d2 = dt - NDT8 < 0 ? 0 : dt - NDT8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              vop[i] = u16_as_bf16((uint16_t)vt16[d2][ks][0][i]);
-              vop[4 + i] = u16_as_bf16((uint16_t)vt16[d2][ks][1][i]);
-            }
+            vop = bf16x8_of(vt16[d2][ks][0], vt16[d2][ks][1]);
           }
           acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pf[ks], acc_o[dt], 0, 0, 0);
         }
@@ -401,13 +397,14 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);   // argument <= 0, or -inf
         float psum = 0.f;
-        bf16x4 pk;
+        float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(v[i] - m_use);
-          psum += p;
-          pk[i] = (__bf16)p;                   // nearest even
+          pv[i] = fast_exp2(v[i] - m_use);
+          psum += pv[i];
         }
+        // nearest even, two per conversion
+        const bf16x4 pk = __builtin_bit_cast(bf16x4, (u32x2){pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])});
         l_part = l_part * alpha + psum;
         m_run = m_new;
         *(bf16x4*)(sm + kOffP + (buf ^ 1) * kPBytes + hs * kPRow + 8 * q8) = pk;

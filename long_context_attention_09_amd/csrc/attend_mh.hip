@@ -377,8 +377,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
         const float p0 = fast_exp2(v[4 * j + 2 * h] - m_use);
         const float p1 = fast_exp2(v[4 * j + 2 * h + 1] - m_use);
         psum += p0 + p1;
-        pw[j][h] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p0) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p1) << 16);
+        pw[j][h] = pack_bf16x2(p0, p1);                 // nearest even
       }
     l_part = l_part * alpha + psum;
     m_run = m_new;
@@ -426,17 +425,17 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
               (lds_i32x2*)(tb + (2 * dt + (G & 1)) * 512 + 16 * row + 8 * (j16 & 1)));
           vop = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
         } else {
+          i16x4 h[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             // lane j supplies entry 16 ks + 8 (G / 2) + 4 u + j / 4 at the 4 RoPE
             // dims 32 d2 + 16 (G % 2) + 4 (j % 4); receives dim j's 4 entries
             const int row = 16 * ks + 8 * (G >> 1) + 4 * u + (j16 >> 2);
             const int byte = 64 * (dt - kDN / 32) + 32 * (G & 1) + 8 * (j16 & 3);   // in the RoPE bytes
-            const i16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            h[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4*)(tb + (kDN / 16 + (byte >> 4)) * 512 + 16 * row + (byte & 15)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vop[4 * u + i] = u16_as_bf16((uint16_t)h[i]);
           }
+          vop = bf16x8_of(h[0], h[1]);
         }
         if (dt < 15) {
           acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[ks], acc_o[dt], 0, 0, 0);

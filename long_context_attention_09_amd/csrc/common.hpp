@@ -18,6 +18,9 @@ typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -41,6 +44,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ __bf16 u16_as_bf16(uint16_t u) { return __builtin_bit_cast(__bf16, u); }
+
+// Two floats as BF16 (nearest even) in one packed conversion: lo in bits
+// 0-15, hi in bits 16-31.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Two 4 x 16-bit transposing LDS reads as one BF16 x 8 operand (a first).
+__device__ __forceinline__ bf16x8 bf16x8_of(const i16x4& a, const i16x4& b) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // ------------------------------------------------------------------ FP8 E4M3FN
 
