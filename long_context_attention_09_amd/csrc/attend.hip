@@ -179,7 +179,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
   uint32_t kmask[kStages];
 #pragma unroll
   for (int u = 0; u < kStages; ++u) {
-    const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, ATTEND_POS(u), sel0[u]);
+    const RowPtrs rp = row_ptrs_tile<kRopeWave>(rsrc, ATTEND_POS(u) - r32, r32, sel0[u]);
     kmask[u] = rp.live;
 #pragma unroll
     for (int c = 0; c < NL; ++c) kst[u][c] = load_chunk<kRopeWave>(c, rp, wdim, g);
@@ -322,7 +322,7 @@ __device__ __forceinline__ void attend_wave(const AttendLaunch a, const AttendSh
       }
       // partial scores of tile t; each chunk's registers take tile t+2's chunk
       // once its k-steps are issued
-      const RowPtrs rp = row_ptrs<kRopeWave>(rsrc, ATTEND_POS(t + kStages), sel);
+      const RowPtrs rp = row_ptrs_tile<kRopeWave>(rsrc, ATTEND_POS(t + kStages) - r32, r32, sel);
       km = rp.live;
       f32x16 sc = {};
 #pragma unroll

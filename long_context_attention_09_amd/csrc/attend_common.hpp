@@ -172,4 +172,22 @@ __device__ __forceinline__ RowPtrs row_ptrs(const RowSource rs, int p, int sel) 
   return r;
 }
 
+// Row pointers of the tile whose lane 0 has list position p0 (uniform over
+// the wave); lane r32 takes position p0 + r32.  A tile wholly inside the
+// visible entries of a list that is not gathered takes one multiply-add per
+// pointer; any other tile (gathered rows, the window, the list's end) the
+// general form above.  The same pointers either way.
+template <bool kRope>
+__device__ __forceinline__ RowPtrs row_ptrs_tile(const RowSource rs, int p0, int r32, int sel) {
+  if (!rs.gather && p0 + kTile <= rs.n_comp && p0 + kTile <= rs.n_vis && p0 + kTile <= rs.p1) {
+    const uint64_t off = (uint64_t)(uint32_t)(p0 + r32) * rs.kvs;
+    RowPtrs r;
+    r.pn = rs.kvb0 + off;
+    r.pr = kRope ? rs.kvb1 + off : 0;
+    r.live = 0xffffffffu;
+    return r;
+  }
+  return row_ptrs<kRope>(rs, p0 + r32, sel);
+}
+
 }  // namespace csa

@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attend_mh_kernel(AttendLaunch a
   auto issue_tile = [&](int t, int bi) -> uint32_t {
     const int li = t * kTile + r32;
     const int sel = gather ? lidx[li < kMhIdxMax ? li : kMhIdxMax - 1] : 0;
-    const RowPtrs rp = row_ptrs<true>(rsrc, MH_POS(t), sel);
+    const RowPtrs rp = row_ptrs_tile<true>(rsrc, MH_POS(t) - r32, r32, sel);
     const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)sm + (uint32_t)(bi * kMhTileBytes);
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
