@@ -171,7 +171,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // fp32 score -> uint32 whose unsigned order is the float order.
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t x = __float_as_uint(f);
-  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+  return x ^ ((uint32_t)((int32_t)x >> 31) | 0x80000000u);   // ~x when negative, x | 2^31 otherwise
 }
 
 }  // namespace csa

@@ -620,23 +620,25 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
     auto kop = [&](int u, int s) {
       return (i32x8){kb[u][s][0], kb[u][s][1], kb[u][s][2], kb[u][s][3], 0, 0, 0, 0};
     };
-    auto ksc = [&](int u, int s) { return (int)((kw[u] >> (8 * (2 * s + h))) & 0xffu); };
+    // the keys' scale words shifted so that the matrix instruction's byte
+    // select picks block 2 s + h as byte 2 s
+    auto ksw = [&](int u) { return (int)(kw[u] >> (8 * h)); };
     // the head group g = qi * NH32 + hg against the keys of ring slot u
     auto head_pair = [&](int g, int u) {
       const int qi = g / NH32, hg = g % NH32;
       const i32x8 a0 = {qa[qi][hg][0][0], qa[qi][hg][0][1], qa[qi][hg][0][2], qa[qi][hg][0][3], 0, 0, 0, 0};
       const i32x8 a1 = {qa[qi][hg][1][0], qa[qi][hg][1][1], qa[qi][hg][1][2], qa[qi][hg][1][3], 0, 0, 0, 0};
       f32x16 acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, kop(u, 0), acc, 4, 4, 0, qs[qi][hg][0], 0, ksc(u, 0));
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, kop(u, 1), acc, 4, 4, 0, qs[qi][hg][1], 0, ksc(u, 1));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, kop(u, 0), acc, 4, 4, 0, qs[qi][hg][0], 0, ksw(u));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, kop(u, 1), acc, 4, 4, 0, qs[qi][hg][1], 2, ksw(u));
       return acc;
     };
     constexpr int G = QT * NH32;
     // the linear product of the keys of ring slot u
     auto lin_pair = [&](int u) {
       f32x16 acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[0], kop(u, 0), acc, 0, 4, 0, ls[0], 0, ksc(u, 0));
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[1], kop(u, 1), acc, 0, 4, 0, ls[1], 0, ksc(u, 1));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[0], kop(u, 0), acc, 0, 4, 0, ls[0], 0, ksw(u));
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(la[1], kop(u, 1), acc, 0, 4, 0, ls[1], 2, ksw(u));
       return acc;
     };
     // software pipeline: the first head group and the linear product of a
@@ -649,7 +651,7 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
         const int j = j0 + u;
         const int un = (u + 1) % R;
         const f32x16 accl = lin_pair(u);
-        float pp[QT][2] = {};
+        float pp[QT] = {};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           f32x16 nxt;
@@ -660,12 +662,12 @@ __global__ void __launch_bounds__(256) index_mxfp4_mq_kernel(IndexLaunch a) {
           }
           const int qi = g / NH32, hg = g % NH32;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) pp[qi][e & 1] = fmaf(w2[qi][hg][e], fabsf(acc_cur[e]), pp[qi][e & 1]);
+          for (int e = 0; e < 16; ++e) pp[qi] = fmaf(w2[qi][hg][e], fabsf(acc_cur[e]), pp[qi]);
           acc_cur = nxt;
         }
         float part[QT];
 #pragma unroll
-        for (int qi = 0; qi < QT; ++qi) part[qi] = pp[qi][0] + pp[qi][1];
+        for (int qi = 0; qi < QT; ++qi) part[qi] = pp[qi];
         // lanes 0-31: query 0, lanes 32-63: query 1, summed over both row halves
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
         // the linear term of this lane half's query, smallest components first
