@@ -56,12 +56,12 @@ WRITE_FACTOR = 1.0    # true bytes written / (WRITE_SIZE KiB * 1024) on the copy
 TRAFFIC = {
     "attend_fp8_kernel(hca)": {
         "source": "attend.hip",
-        "sha256": "801298c957691d396d315b2633563ca3dbe71e1308f1973a087434f9682530f1",
-        "fetch_kib": 83403.3, "write_kib": 16512.0},
+        "sha256": "f0cc14f98ffa7f86e21d0069cfff0b89cebd7c3d37000985ba398b2794dd716b",
+        "fetch_kib": 83406.6, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "2811ac7cc005f05d98e3428c6b08e42e060cc1d695175dd0970751915405875d",
-        "fetch_kib": 69843.6, "write_kib": 8356.8},
+        "sha256": "ee9f35f78e4cfa24d60e2270cd193a5ad6a7f9a6c411efc4ea5d0feece1925ca",
+        "fetch_kib": 69843.2, "write_kib": 8356.8},
 }
 
 
