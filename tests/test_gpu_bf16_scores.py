@@ -43,7 +43,8 @@ def _bf16_round(x):
     return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("n_q,B,L", [(1, 2, 1 << 18), (33, 1, 1 << 16), (70, 1, 1 << 16)], ids=str)
+@pytest.mark.parametrize("n_q,B,L", [(1, 2, 1 << 18), (33, 1, 1 << 16), (70, 1, 1 << 16), (70, 1, (1 << 16) + 12)],
+                         ids=str)
 def test_bf16_scores(n_q, B, L):
     K = _K()
     print(f"[gpu] bf16 scores n_q={n_q} B={B} L={L}", flush=True)

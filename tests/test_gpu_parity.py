@@ -508,16 +508,18 @@ def test_topk_ties_and_empty():
         assert np.array_equal(got, OC.topk(rs, k)), f"b={b}"
 
 
+@pytest.mark.parametrize("n_cap", [5000, 4999], ids=["rows-aligned", "rows-odd"])
 @pytest.mark.parametrize("with_scores", [False, True], ids=["list", "threshold-emit"])
-def test_topk_ties_query_blocks(with_scores):
+def test_topk_ties_query_blocks(with_scores, n_cap):
     """The same exact-tie rule on the query-block paths (70 queries per
     sequence: the 32-head MXFP4 scorer with the split linear term, then the
     list pass without caller-kept scores, threshold + emit with them): keys
     drawn from 4 code patterns give 4 distinct scores per query, so most of
     the k-th bucket is ties that must go to the lower index; queries that see
-    every entry, none, or fewer than k."""
+    every entry, none, or fewer than k.  An odd capacity leaves most score
+    rows off 16-byte alignment, where the list pass reads entry by entry."""
     K = _K()
-    B, n_q, n_cap, H_I = 2, 70, 5000, 32
+    B, n_q, H_I = 2, 70, 32
     rng = np.random.default_rng(1)
     pat = rng.integers(0, 256, size=(4, 64), dtype=np.uint8)
     which = rng.integers(0, 4, size=(B, n_cap))
