@@ -397,6 +397,46 @@ def paged_leg(ev, st, steps, shapes, inps, contiguous_ms):
     return out
 
 
+def selection_recall(ref, got):
+    """Per row, the fraction of ref's selected indices (ascending, -1 padded)
+    that got also selects; rows of [..., k] int32 tensors on the device."""
+    import torch
+    k = ref.shape[-1]
+    r = ref.reshape(-1, k).long()
+    g = got.reshape(-1, k).long()
+    both = torch.cat([r, g], dim=1).sort(dim=1).values
+    common = ((both[:, 1:] == both[:, :-1]) & (both[:, 1:] >= 0)).sum(dim=1)
+    n_ref = (r >= 0).sum(dim=1).clamp(min=1)
+    return (common.float() / n_ref.float())
+
+
+def prefill_bf16_leg(ev, st, steps, csa, shape, inp):
+    """The prefill chunk's CSA index op with fp32 and with BF16 scores, timed
+    alternately in one loop (HIP events on the bench stream, same clocks and
+    caches for both), and the recall of the fp32 selection."""
+    import torch
+    from long_context_attention_09_amd.layer import LayerStep
+    b16 = LayerStep(shape, inp, prefill=True, bf16_scores=True)
+    b16.compress_all(stream=st)
+    record = ev.h.hipEventRecord
+    marks = {n: [(ev.create(), ev.create()) for _ in range(steps + 1)] for n in ("fp32", "bf16")}
+    for k in range(steps + 1):
+        for n, step in (("fp32", csa), ("bf16", b16)):
+            e0, e1 = marks[n][k]
+            record(C.c_void_p(e0), st)
+            step.index(stream=st)
+            record(C.c_void_p(e1), st)
+    torch.cuda.synchronize()
+    t = {n: sum(ev.elapsed_ms(e0, e1) for e0, e1 in m[1:]) / steps for n, m in marks.items()}
+    rec = selection_recall(csa.idx, b16.idx)
+    res = {"fp32_index_op_ms": round(t["fp32"], 3), "bf16_index_op_ms": round(t["bf16"], 3),
+           "speedup": round(t["fp32"] / t["bf16"], 3),
+           "recall_of_fp32_selection": {"min": round(float(rec.min()), 5), "mean": round(float(rec.mean()), 5)}}
+    del b16
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_leg(ev, st, steps, warmup, oracle_rows):
     """One 8192-token chunk after 2^20 cached tokens through a CSA and an HCA
     layer, timed with HIP events per operation on the bench stream."""
@@ -470,10 +510,17 @@ def prefill_leg(ev, st, steps, warmup, oracle_rows):
                  "csa_attend(fp8+bf16)": mfma(f_csa["attend"], t["csa_attend"], BF16_PEAK_TFLOPS),
                  "hca_attend(fp8+bf16)": mfma(f_hca["attend"], t["hca_attend"], BF16_PEAK_TFLOPS)},
     }
+    # BF16 index scores at prefill, where the top-k passes stream every
+    # query's scores: the CSA index op against the fp32 one, and the recall
+    # of the fp32 selection over every query of the chunk
+    print("[bench] prefill: bf16 index scores", file=sys.stderr, flush=True)
+    del hca
+    torch.cuda.empty_cache()
+    out["bf16_index_scores"] = prefill_bf16_leg(ev, st, steps, csa, csa_shape, csa_inp)
     if oracle_rows > 0:
         print("[bench] prefill: oracle sample", file=sys.stderr, flush=True)
         out["oracle"] = prefill_oracle((csa_shape, hca_shape), (csa_inp, hca_inp), oracle_rows)
-    del csa, hca, csa_inp, hca_inp
+    del csa, csa_inp, hca_inp
     torch.cuda.empty_cache()
     return out
 

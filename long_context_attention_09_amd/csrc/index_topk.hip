@@ -908,16 +908,25 @@ __global__ void __launch_bounds__(256) topk_collect_kernel(IndexLaunch a) {
     int aslot = block_excl_scan(__popc(above), red[1], &n_above);
     uint32_t* ck = a.cand_key + (int64_t)q * a.n_cap + c0;
     // the chunk's own score region (read in full above) takes the indices
-    // above the bucket, then the candidates' indices
+    // above the bucket, then the candidates' indices: 32-bit indices over
+    // fp32 scores, 16-bit offsets in the chunk over BF16 scores (a chunk's
+    // 4096 two-byte slots hold any of its lists)
+    const bool b16 = bf16_scores(a);
     uint32_t* const lst = (uint32_t*)sc + c0;
+    uint16_t* const lst16 = (uint16_t*)sc + c0;
+    auto put = [&](int at, int e_off) {
+      if (b16) lst16[at] = (uint16_t)e_off;
+      else lst[at] = (uint32_t)(c0 + e_off);
+    };
+    const int o0 = 16 * (int)threadIdx.x;        // e0 - c0
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
       if (want >> j & 1u) {
         ck[slot] = keys[j];
-        lst[n_above + slot] = (uint32_t)(e0 + j);
+        put(n_above + slot, o0 + j);
         ++slot;
       }
-      if (above >> j & 1u) lst[aslot++] = (uint32_t)(e0 + j);
+      if (above >> j & 1u) put(aslot++, o0 + j);
     }
     if (threadIdx.x == 0) {
       a.chunk_above[(int64_t)q * a.n_chunks + blockIdx.x] = n_above;
@@ -1279,6 +1288,14 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
   // candidates above T and the first k of those equal to T (fs), all in index
   // order; chunks are ascending index ranges, so flat order is index order.
   const uint32_t* const lst = (const uint32_t*)(score_row(a, q / a.n_qb, q % a.n_qb));
+  const uint16_t* const lst16 = (const uint16_t*)lst;
+  const bool b16 = bf16_scores(a);
+  // entry `at` of chunk c's list: an index (fp32 scores) or an offset in the
+  // chunk (BF16 scores)
+  auto list_at = [&](int c, int at) -> uint32_t {
+    const int64_t o = (int64_t)c * kChunk + at;
+    return b16 ? (uint32_t)c * (uint32_t)kChunk + lst16[o] : lst[o];
+  };
   auto chunk_in = [&](const int* pf, int i) {   // last c with pf[c] <= i
     int lo = 0, hi = n_act;
     while (hi - lo > 1) {
@@ -1298,13 +1315,13 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
     const int er = eq_seen + block_excl_scan(eq ? 1 : 0, red[2], &eq_tot);
     const bool take = gt || (eq && er < (int)k);
     const int p = n_s + block_excl_scan(take ? 1 : 0, red[3], &take_tot);
-    if (take && p < kFusedTopK) fs[p] = lst[(int64_t)c * kChunk + (apre[c + 1] - apre[c]) + (i - pre[c])];
+    if (take && p < kFusedTopK) fs[p] = list_at(c, (apre[c + 1] - apre[c]) + (i - pre[c]));
     n_s += take_tot;
     eq_seen += eq_tot;
   }
   for (int i = threadIdx.x; i < n_ab && i < kFusedTopK; i += 256) {
     const int c = chunk_in(apre, i);
-    fa[i] = lst[(int64_t)c * kChunk + (i - apre[c])];
+    fa[i] = list_at(c, i - apre[c]);
   }
   __syncthreads();
   auto below = [](const uint32_t* v, int n, uint32_t x) {
@@ -1425,11 +1442,10 @@ hipError_t launch_index_topk(const IndexLaunch& a, hipStream_t s) {
   dim3 g2(a.n_chunks, nq);
   IndexLaunch t = a;
   // with many queries and the scores in the workspace, collect leaves the
-  // selected-index lists in place of the scores and the threshold pass
-  // writes the output from them (no emit launch)
-  // (BF16 scores: a chunk's 2-byte score slots cannot hold its index lists)
-  t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK &&
-                !(a.flags & CSA_INDEX_BF16_SCORES);
+  // selected-index lists in place of the scores (16-bit offsets in the chunk
+  // over BF16 scores) and the threshold pass writes the output from them (no
+  // emit launch)
+  t.list_mode = nq >= kSplitSelectQueries && !a.out_score && a.top_k <= kFusedTopK;
   if (t.list_mode) {
     topk_bucket_kernel<<<nq, 256, 0, s>>>(t);
     topk_collect_kernel<true><<<g2, 256, 0, s>>>(t);

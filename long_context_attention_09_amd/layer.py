@@ -34,11 +34,14 @@ class LayerStep:
     seeded generator lays them out (decode: quant_decode_inputs, prefill:
     quant_prefill_inputs)."""
 
-    def __init__(self, shape, inp, prefill: bool = False, copies: int = 1, batch_invariant: bool = False):
+    def __init__(self, shape, inp, prefill: bool = False, copies: int = 1, batch_invariant: bool = False,
+                 bf16_scores: bool = False):
         self.s = shape
-        # batch-invariant mode: fixed attention splits and the exact indexer form
+        # batch-invariant mode: fixed attention splits and the exact indexer form;
+        # bf16_scores: index scores rounded to BF16 before they are stored and selected on
         self.attend_flags = K.ATTEND_NORM_Q | (K.ATTEND_BATCH_INVARIANT if batch_invariant else 0)
-        self.index_flags = K.INDEX_BATCH_INVARIANT if batch_invariant else 0
+        self.index_flags = ((K.INDEX_BATCH_INVARIANT if batch_invariant else 0) |
+                            (K.INDEX_BF16_SCORES if bf16_scores else 0))
         self.inp = inp
         self.prefill = prefill
         s = shape

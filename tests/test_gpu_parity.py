@@ -557,6 +557,56 @@ def test_topk_ties_query_blocks(with_scores, n_cap):
     _say(f"  keys tied with the k-th score, all queries: {n_ties}")
 
 
+
+@pytest.mark.parametrize("n_cap", [5000, 4999], ids=["rows-aligned", "rows-odd"])
+def test_topk_ties_query_blocks_bf16(n_cap):
+    """Exact ties with BF16 index scores on the query-block paths: the list
+    pass (16-bit offsets in the chunk written over the chunk's BF16 scores)
+    gives the selection of threshold + emit (scores kept by the caller), and
+    that selection is the exact top-k of the stored BF16 scores (highest
+    first, lower index on ties, ascending), for queries that see every entry,
+    none, or fewer than k."""
+    K = _K()
+    B, n_q, H_I = 2, 70, 32
+    rng = np.random.default_rng(2)
+    pat = rng.integers(0, 256, size=(4, 64), dtype=np.uint8)
+    kc = pat[rng.integers(0, 4, size=(B, n_cap))]
+    ks = np.full((B, n_cap, 4), 127, np.uint8)
+    qc = rng.integers(0, 256, size=(B, n_q, H_I, 64), dtype=np.uint8)
+    qs = np.full((B, n_q, H_I, 4), 127, np.uint8)
+    w = rng.normal(size=(B, n_q, H_I)).astype(np.float32)
+    pos = rng.integers(0, 4 * n_cap + 8, size=(B, n_q)).astype(np.int64)
+    pos[:, 0] = 4 * n_cap + 3
+    pos[:, 1] = 2
+    pos[:, 2] = 4 * 600 + 1
+    k = 1000
+    dev = {n: torch.from_numpy(x).cuda() for n, x in (("qc", qc), ("w", w), ("kc", kc), ("pos", pos),
+                                                      ("qs", qs), ("ks", ks))}
+    _say("top-k ties, query blocks, BF16 scores: list pass and threshold + emit")
+    idx_l = torch.empty(B, n_q, k, dtype=torch.int32, device="cuda")
+    idx_e = torch.empty_like(idx_l)
+    score = torch.empty(B, n_q, n_cap, dtype=torch.bfloat16, device="cuda")
+    for idx, sc in ((idx_l, None), (idx_e, score)):
+        K.index_topk(dev["qc"], dev["w"], dev["kc"], dev["pos"], m=4, top_k=k, out_idx=idx, q1=dev["qs"],
+                     k1=dev["ks"], out_score=sc, fmt=K.FMT_MXFP4, flags=K.INDEX_BF16_SCORES)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_l, idx_e)
+    got_all = idx_l.cpu().numpy()
+    st_all = score.float().cpu().numpy().astype(np.float64)
+    n_ties = 0
+    for b in range(B):
+        for r in range(n_q):
+            n_vis = OC.visible_entries(int(pos[b, r]), 4, n_cap)
+            st = st_all[b, r, :n_vis]
+            want = np.full(k, -1, np.int64)
+            sel = np.sort(np.lexsort((np.arange(n_vis), -st))[:k])
+            want[:len(sel)] = sel
+            assert np.array_equal(got_all[b, r], want), f"b={b} r={r} n_vis={n_vis}"
+            if n_vis > k:
+                n_ties += int((st == np.sort(st)[::-1][k - 1]).sum())
+    assert n_ties > 1000
+    _say(f"  keys tied with the k-th stored score, all queries: {n_ties}")
+
 def test_invalid_arguments_are_rejected():
     K = _K()
     from long_context_attention_09_amd._lib import CsaError
