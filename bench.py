@@ -60,8 +60,8 @@ TRAFFIC = {
         "fetch_kib": 83406.6, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "ee9f35f78e4cfa24d60e2270cd193a5ad6a7f9a6c411efc4ea5d0feece1925ca",
-        "fetch_kib": 69843.2, "write_kib": 8356.8},
+        "sha256": "aefae5d122c8b22f1f800cfc7ec22748174e3b64ba3dbadc20607d212c32c8af",
+        "fetch_kib": 69843.3, "write_kib": 8356.8},
 }
 
 
