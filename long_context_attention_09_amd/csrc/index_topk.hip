@@ -1079,6 +1079,14 @@ __global__ void __launch_bounds__(256) topk_select_kernel(IndexLaunch a) {
     prefix |= s_digit[pass] << shift;
     mask |= 1023u << shift;
     k = s_kin[pass];
+    // BF16 scores: the bits of an order key below bit 16 are all zero (a
+    // score >= 0, top key bit set) or all one (a negative score, whose key is
+    // the complement of its bits), so bits 19..10 already fix the k-th key
+    // (the last pass would put every candidate into one bin)
+    if (bf16_scores(a)) {
+      if ((prefix >> 31) == 0) prefix |= 1023u;
+      break;
+    }
   }
   const uint32_t T = prefix;          // the k-th largest key; k = how many keys == T to take
   for_each([&](uint32_t key, int c) {
@@ -1242,6 +1250,14 @@ __global__ void __launch_bounds__(256) topk_threshold_kernel(IndexLaunch a) {
     prefix |= s_digit[pass] << shift;
     mask |= 1023u << shift;
     k = s_kin[pass];
+    // BF16 scores: the bits of an order key below bit 16 are all zero (a
+    // score >= 0, top key bit set) or all one (a negative score, whose key is
+    // the complement of its bits), so bits 19..10 already fix the k-th key
+    // (the last pass would put every candidate into one bin)
+    if (bf16_scores(a)) {
+      if ((prefix >> 31) == 0) prefix |= 1023u;
+      break;
+    }
   }
   const uint32_t T = prefix;
   for_each([T](uint32_t key, int c) {
