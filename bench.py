@@ -60,8 +60,8 @@ TRAFFIC = {
         "fetch_kib": 83406.6, "write_kib": 16512.0},
     "index_mxfp4_kernel": {
         "source": "index_topk.hip",
-        "sha256": "aefae5d122c8b22f1f800cfc7ec22748174e3b64ba3dbadc20607d212c32c8af",
-        "fetch_kib": 69843.3, "write_kib": 8356.8},
+        "sha256": "74a377de10592a718226ca83c67691ed054afc4f302426dfdff911c3aaa33eff",
+        "fetch_kib": 69843.4, "write_kib": 8356.8},
 }
 
 
