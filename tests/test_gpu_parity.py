@@ -558,16 +558,19 @@ def test_topk_ties_query_blocks(with_scores, n_cap):
 
 
 
+@pytest.mark.parametrize("n_q", [70, 3], ids=["query-blocks", "select"])
 @pytest.mark.parametrize("n_cap", [5000, 4999], ids=["rows-aligned", "rows-odd"])
-def test_topk_ties_query_blocks_bf16(n_cap):
-    """Exact ties with BF16 index scores on the query-block paths: the list
-    pass (16-bit offsets in the chunk written over the chunk's BF16 scores)
-    gives the selection of threshold + emit (scores kept by the caller), and
-    that selection is the exact top-k of the stored BF16 scores (highest
-    first, lower index on ties, ascending), for queries that see every entry,
-    none, or fewer than k."""
+def test_topk_ties_query_blocks_bf16(n_cap, n_q):
+    """Exact ties with BF16 index scores and head weights of both signs (so
+    negative scores, whose order keys end in ones, are selected too).  With
+    70 queries (query-block paths) the list pass (16-bit offsets in the chunk
+    written over the chunk's BF16 scores) gives the selection of threshold +
+    emit (scores kept by the caller); with 3 queries both calls run collect +
+    select.  Either way the selection is the exact top-k of the stored BF16
+    scores (highest first, lower index on ties, ascending), for queries that
+    see every entry, none, or fewer than k."""
     K = _K()
-    B, n_q, H_I = 2, 70, 32
+    B, H_I = 2, 32
     rng = np.random.default_rng(2)
     pat = rng.integers(0, 256, size=(4, 64), dtype=np.uint8)
     kc = pat[rng.integers(0, 4, size=(B, n_cap))]
@@ -575,6 +578,7 @@ def test_topk_ties_query_blocks_bf16(n_cap):
     qc = rng.integers(0, 256, size=(B, n_q, H_I, 64), dtype=np.uint8)
     qs = np.full((B, n_q, H_I, 4), 127, np.uint8)
     w = rng.normal(size=(B, n_q, H_I)).astype(np.float32)
+    w[1] = -np.abs(w[1])                    # sequence 1: every score <= 0
     pos = rng.integers(0, 4 * n_cap + 8, size=(B, n_q)).astype(np.int64)
     pos[:, 0] = 4 * n_cap + 3
     pos[:, 1] = 2
@@ -582,7 +586,7 @@ def test_topk_ties_query_blocks_bf16(n_cap):
     k = 1000
     dev = {n: torch.from_numpy(x).cuda() for n, x in (("qc", qc), ("w", w), ("kc", kc), ("pos", pos),
                                                       ("qs", qs), ("ks", ks))}
-    _say("top-k ties, query blocks, BF16 scores: list pass and threshold + emit")
+    _say(f"top-k ties, BF16 scores, {n_q} queries, n_cap {n_cap}")
     idx_l = torch.empty(B, n_q, k, dtype=torch.int32, device="cuda")
     idx_e = torch.empty_like(idx_l)
     score = torch.empty(B, n_q, n_cap, dtype=torch.bfloat16, device="cuda")
@@ -593,7 +597,7 @@ def test_topk_ties_query_blocks_bf16(n_cap):
     assert torch.equal(idx_l, idx_e)
     got_all = idx_l.cpu().numpy()
     st_all = score.float().cpu().numpy().astype(np.float64)
-    n_ties = 0
+    n_ties = n_neg = 0
     for b in range(B):
         for r in range(n_q):
             n_vis = OC.visible_entries(int(pos[b, r]), 4, n_cap)
@@ -603,8 +607,11 @@ def test_topk_ties_query_blocks_bf16(n_cap):
             want[:len(sel)] = sel
             assert np.array_equal(got_all[b, r], want), f"b={b} r={r} n_vis={n_vis}"
             if n_vis > k:
-                n_ties += int((st == np.sort(st)[::-1][k - 1]).sum())
+                s_k = np.sort(st)[::-1][k - 1]
+                n_ties += int((st == s_k).sum())
+                n_neg += int(s_k < 0)
     assert n_ties > 1000
+    assert n_neg > 0                        # negative k-th scores were selected on
     _say(f"  keys tied with the k-th stored score, all queries: {n_ties}")
 
 def test_invalid_arguments_are_rejected():
